@@ -1,0 +1,104 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail at least one pin.
+
+Each mutation replaces one oracle step with a plausible wrong version; the
+pins of test_oracle_pins are then run and at least one must fail.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import hxq_oracle as H
+import test_oracle_pins as P
+
+PINS = [
+    lambda: P.test_u8_matches_bruteforce(7, 12, 3),
+    lambda: P.test_pk12_matches_bruteforce(6, 16, 3),
+    P.test_bf16_activations_bruteforce,
+    P.test_constant_index_closed_form,
+    P.test_constant_index_pk12_closed_form,
+    P.test_empty_sidecar_difference,
+    P.test_one_hot_reconstructs_columns,
+    P.test_cross_format_special_case,
+    P.test_pk12_golden_bytes,
+    P.test_bf16_round_matches_library_cast,
+]
+
+
+def _transposed_forward(W, X, bias=None):
+    Y = (X[:, : W.shape[0]] @ W[:, : X.shape[0]]) if W.shape[0] != W.shape[1] else X @ W
+    if bias is not None:
+        Y = Y + np.asarray(bias, np.float32).astype(np.float64)[None, :]
+    return Y
+
+
+def _no_bias_forward(W, X, bias=None):
+    return X @ W.T
+
+
+def _swapped_sidecar(W, rows, cols, deltas):
+    out = np.array(W, dtype=np.float64, copy=True)
+    r = np.asarray(cols, np.int64) % W.shape[0]
+    c = np.asarray(rows, np.int64) % W.shape[1]
+    if r.size:
+        np.add.at(out, (r, c), np.asarray(deltas, np.float32).astype(np.float64))
+    return out
+
+
+def _sidecar_overwrites_duplicates(W, rows, cols, deltas):
+    out = np.array(W, dtype=np.float64, copy=True)
+    r = np.asarray(rows, np.int64)
+    if r.size:
+        out[r, np.asarray(cols, np.int64)] += np.asarray(deltas, np.float32).astype(np.float64)
+    return out
+
+
+def _unpack_nibble_swapped(packed, N, K):
+    T = (K + 3) // 4
+    p = np.asarray(packed, np.uint8).reshape(N, T, 3).astype(np.int64)
+    a = p[:, :, 0] | ((p[:, :, 1] >> 4) << 8)
+    b = (p[:, :, 1] & 0xF) | (p[:, :, 2] << 4)
+    idx = np.empty((N, 2 * T), np.int64)
+    idx[:, 0::2] = a
+    idx[:, 1::2] = b
+    return idx[:, : K // 2]
+
+
+def _dequant_pk12_components_swapped(codebook2, idx2, K):
+    c = np.asarray(codebook2, np.float32).astype(np.float64)[:, ::-1]
+    return c[idx2].reshape(idx2.shape[0], K)
+
+
+def _bf16_truncate(v):
+    u = np.ascontiguousarray(v, np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(np.float32)
+
+
+def _bf16_bits_low_half(bits):
+    return np.asarray(bits, np.uint16).astype(np.float32).astype(np.float64)
+
+
+MUTATIONS = {
+    "transposed_weight": ("linear_forward", _transposed_forward),
+    "dropped_bias": ("linear_forward", _no_bias_forward),
+    "sidecar_row_col_swapped": ("apply_sidecar", _swapped_sidecar),
+    "sidecar_duplicates_not_summed": ("apply_sidecar", _sidecar_overwrites_duplicates),
+    "pk12_nibbles_swapped": ("unpack_pk12", _unpack_nibble_swapped),
+    "pk12_pair_components_swapped": ("dequant_pk12", _dequant_pk12_components_swapped),
+    "bf16_truncation": ("bf16_round_f32", _bf16_truncate),
+    "bf16_upcast_wrong": ("bf16_bits_to_f64", _bf16_bits_low_half),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    fn_name, bad = MUTATIONS[name]
+    monkeypatch.setattr(H, fn_name, bad)
+    monkeypatch.setattr(oracle, fn_name, bad)
+    failures = 0
+    for pin in PINS:
+        try:
+            pin()
+        except Exception:  # an AssertionError or a shape error both count as caught
+            failures += 1
+    assert failures > 0, "planted mistake %s passed every pin" % name
