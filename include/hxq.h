@@ -1,0 +1,149 @@
+/*
+ * libhxq: the HelixLinear forward pass computed from the compressed weights.
+ *
+ * A HelixLinear layer (model cards "Zamba2-1.2B-HXQ", "Mamba2-1.3B-HXQ",
+ * "Qwen2.5-3B-Instruct-HXQ", section "What is HelixCode?") replaces an
+ * nn.Linear weight W [N out, K in] by a float32 codebook, an index per weight
+ * and sparse sidecar corrections, and computes codebook[indices] @ x without
+ * forming W.  The HXQ whitepaper (J. P. Fellows, Echo Labs, 2026) gives the
+ * two index formats ("Method"; "2D vector quantization"):
+ *   u8   - 256-entry float32 codebook, one uint8 index per weight;
+ *   pk12 - 4096-entry codebook of float32 pairs over adjacent weights, two
+ *          12-bit indices packed into 3 bytes;
+ * and the sidecar: sparse (row, col, delta) triplets that correct the weights
+ * with the largest reconstruction error ("Method", sidecar outlier
+ * correction).  Every entry point computes, for m < M and n < N,
+ *
+ *     y[m][n] = sum_k (C[idx[n][k]] + S[n][k]) * x[m][k] + bias[n]
+ *
+ * where S[n][k] is the sum of the deltas of the triplets at (n, k).
+ *
+ * Conventions shared by all entry points
+ *   - Every pointer is device memory owned by the caller.  The library
+ *     allocates nothing, keeps no per-call state and never reads device memory
+ *     on the host.  Work is queued on `stream` (0 = the null stream) and the
+ *     call returns without waiting for it.
+ *   - Row-major layouts: indices [N][K] (u8) or [N][3*ceil(K/4)] (pk12),
+ *     x [M][K], y [M][N].  y must not overlap any input.
+ *   - x_dtype: HXQ_F32 (float) or HXQ_BF16 (bf16 bit patterns, uint16).
+ *     y is always float32.
+ *   - Sidecar: sc_rows / sc_cols int32, sc_deltas float32, nnz entries,
+ *     sorted by (row, col) in non-decreasing order; repeated coordinates add.
+ *     Entries out of range or out of order are undefined behaviour (they are
+ *     never checked on the device).  With nnz == 0 the three pointers may be
+ *     NULL.
+ *   - bias may be NULL (no bias).
+ *   - M == 0 or N == 0: nothing is launched, HXQ_OK.  K == 0: y = bias (or 0).
+ *   - Arithmetic: fp32 activations are multiplied in fp32 with fp32
+ *     accumulation; bf16 activations with M <= 16 are upcast exactly and take
+ *     the same fp32 path; bf16 activations with M > 16 (u8 format) run on bf16
+ *     matrix cores with fp32 accumulation, the codebook value (plus any
+ *     sidecar delta at that position, added in fp32) rounded once to bf16.
+ *   - Errors are returned as a negative hxq_status before anything is
+ *     launched; HXQ_ERR_HIP reports a failed launch.
+ */
+#ifndef HXQ_H
+#define HXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t; /* the same tag HIP uses */
+
+enum hxq_status {
+  HXQ_OK = 0,
+  HXQ_ERR_NULL = -1,        /* a required pointer is NULL while its extent is > 0 */
+  HXQ_ERR_SHAPE = -2,       /* negative M, N, K or nnz; odd K for pk12; M, N, K >= 2^31 */
+  HXQ_ERR_DTYPE = -3,       /* x_dtype is not HXQ_F32 or HXQ_BF16 */
+  HXQ_ERR_ALIGN = -4,       /* x not aligned to its element size, or y / codebook / bias /
+                               sidecar arrays not 4-byte aligned */
+  HXQ_ERR_UNSUPPORTED = -5, /* a combination this version does not implement */
+  HXQ_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+};
+
+enum hxq_dtype { HXQ_F32 = 0, HXQ_BF16 = 1 };
+
+/* Forward pass, 1D VQ (u8).
+ *   codebook  [256] float32 (model cards, "What is HelixCode?").
+ *   indices   [N][K] uint8, row-major, one index per weight.
+ *   sc_*      sidecar triplets as described above.
+ *   x         [M][K] float32 or bf16; bias [N] float32 or NULL; y [M][N] float32,
+ *             overwritten. */
+int hxq_linear_fwd_u8(const float* codebook, const uint8_t* indices,
+                      const int32_t* sc_rows, const int32_t* sc_cols,
+                      const float* sc_deltas, int64_t nnz,
+                      const void* x, int x_dtype, const float* bias, float* y,
+                      int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/* Forward pass, 2D VQ with 12-bit indices (pk12).
+ *   codebook2 [4096][2] float32 pairs (HXQ whitepaper, "2D vector quantization").
+ *             Weights (2j, 2j+1) of a row take components 0 and 1 of the entry
+ *             selected by that row's index j.
+ *   packed    [N][3*ceil(K/4)] uint8.  Group t of a row (its bytes 3t..3t+2)
+ *             holds the row's indices 2t (a) and 2t+1 (b) as the little-endian
+ *             24-bit word v = a | b << 12: byte0 = a[7:0], byte1 = a[11:8] | b[3:0] << 4,
+ *             byte2 = b[11:4].  When K = 2 (mod 4) the last group's b is 0 and unused
+ *             (HXQ whitepaper, "Method", 12-bit index packing; the byte order is this
+ *             library's choice).
+ *   K must be even.  All other arguments as for hxq_linear_fwd_u8.  bf16 x is
+ *   accepted at every M and always takes the fp32 path. */
+int hxq_linear_fwd_pk12(const float* codebook2, const uint8_t* packed,
+                        const int32_t* sc_rows, const int32_t* sc_cols,
+                        const float* sc_deltas, int64_t nnz,
+                        const void* x, int x_dtype, const float* bias, float* y,
+                        int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/* The sidecar term alone, accumulated into y:
+ *     y[m][r] += sum over triplets (r, c, d) of d * x[m][c]      (fp32)
+ * (HXQ whitepaper, "Method", sidecar outlier correction, applied to the
+ * activations instead of the weights).  y [M][N] is read and written; the
+ * sidecar must be sorted as above.  Deterministic: each output element is
+ * summed in triplet order by one thread. */
+int hxq_sidecar_add(const int32_t* sc_rows, const int32_t* sc_cols,
+                    const float* sc_deltas, int64_t nnz,
+                    const void* x, int x_dtype, float* y,
+                    int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/* Kernel selection, for tests and measurement.  HXQ_VARIANT_AUTO is what the
+ * entry points above use; the others force one kernel family and return
+ * HXQ_ERR_UNSUPPORTED when it cannot take the call. */
+enum hxq_variant {
+  HXQ_VARIANT_AUTO = 0,
+  HXQ_VARIANT_GEMV_VALU = 1,  /* fp32 FMA on the vector ALUs */
+  HXQ_VARIANT_GEMV_MFMA = 2,  /* fp32 matrix-core GEMV (4x4x1 fp32 MFMA) */
+  HXQ_VARIANT_GEMM_BF16 = 3,  /* bf16 matrix-core GEMM (u8, bf16 x only) */
+  HXQ_VARIANT_GENERIC = 4     /* any shape or alignment, one wave per output row */
+};
+
+int hxq_linear_fwd_u8_ex(const float* codebook, const uint8_t* indices,
+                         const int32_t* sc_rows, const int32_t* sc_cols,
+                         const float* sc_deltas, int64_t nnz,
+                         const void* x, int x_dtype, const float* bias, float* y,
+                         int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                         int variant);
+
+int hxq_linear_fwd_pk12_ex(const float* codebook2, const uint8_t* packed,
+                           const int32_t* sc_rows, const int32_t* sc_cols,
+                           const float* sc_deltas, int64_t nnz,
+                           const void* x, int x_dtype, const float* bias, float* y,
+                           int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                           int variant);
+
+/* The kernel family AUTO picks for these arguments (an hxq_variant), or a
+ * negative hxq_status if the call would be rejected.  Host only. */
+int hxq_select_variant(int fmt_pk12, int x_dtype, int64_t M, int64_t N, int64_t K);
+
+/* Static text for a status code. */
+const char* hxq_status_str(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int hxq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HXQ_H */

@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares,
+and rejects bad arguments on the host before anything is launched."""
+
+import ctypes
+
+import pytest
+
+from vq_compressed_linear_amd import _binding as B
+
+
+@pytest.fixture(scope="module")
+def L():
+    try:
+        return B.lib()
+    except RuntimeError as e:  # pragma: no cover - build() runs before the suite
+        pytest.fail(str(e))
+
+
+def test_exports_every_declared_symbol(L):
+    names = B.header_symbols()
+    assert "hxq_linear_fwd_u8" in names and "hxq_linear_fwd_pk12" in names
+    assert "hxq_sidecar_add" in names
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in B.SIGNATURES, "binding lacks a signature for %s" % n
+
+
+def test_status_strings(L):
+    for st in range(-6, 1):
+        assert L.hxq_status_str(st)
+    assert L.hxq_version() >= 100
+
+
+FAKE = 0x100000  # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def fwd(L, fn="hxq_linear_fwd_u8_ex", codebook=FAKE, indices=FAKE, rows=FAKE, cols=FAKE,
+        deltas=FAKE, nnz=0, x=FAKE, x_dtype=0, bias=FAKE, y=FAKE, M=1, N=1, K=16, variant=0):
+    return getattr(L, fn)(codebook, indices, rows, cols, deltas, nnz, x, x_dtype, bias, y,
+                          M, N, K, None, variant)
+
+
+# Each case must fail validation, so no kernel is ever queued.
+BAD = [
+    (dict(x_dtype=2), B.HXQ_ERR_DTYPE),
+    (dict(x_dtype=-1), B.HXQ_ERR_DTYPE),
+    (dict(M=-1), B.HXQ_ERR_SHAPE),
+    (dict(N=-5), B.HXQ_ERR_SHAPE),
+    (dict(K=-16), B.HXQ_ERR_SHAPE),
+    (dict(nnz=-1), B.HXQ_ERR_SHAPE),
+    (dict(M=2 ** 31), B.HXQ_ERR_SHAPE),
+    (dict(y=None), B.HXQ_ERR_NULL),
+    (dict(x=None), B.HXQ_ERR_NULL),
+    (dict(indices=None), B.HXQ_ERR_NULL),
+    (dict(codebook=None), B.HXQ_ERR_NULL),
+    (dict(nnz=3, rows=None), B.HXQ_ERR_NULL),
+    (dict(nnz=3, deltas=None), B.HXQ_ERR_NULL),
+    (dict(x=FAKE + 2), B.HXQ_ERR_ALIGN),
+    (dict(x=FAKE + 1, x_dtype=1), B.HXQ_ERR_ALIGN),
+    (dict(y=FAKE + 2), B.HXQ_ERR_ALIGN),
+    (dict(bias=FAKE + 1), B.HXQ_ERR_ALIGN),
+    (dict(nnz=1, cols=FAKE + 2), B.HXQ_ERR_ALIGN),
+    (dict(variant=9), B.HXQ_ERR_UNSUPPORTED),
+    (dict(variant=-1), B.HXQ_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,want", BAD)
+def test_u8_rejects(L, kw, want):
+    assert fwd(L, **kw) == want
+
+
+@pytest.mark.parametrize("kw,want", BAD)
+def test_pk12_rejects(L, kw, want):
+    assert fwd(L, fn="hxq_linear_fwd_pk12_ex", **kw) == want
+
+
+def test_pk12_odd_k(L):
+    assert fwd(L, fn="hxq_linear_fwd_pk12_ex", K=7) == B.HXQ_ERR_SHAPE
+
+
+def test_empty_is_a_no_op(L):
+    # M == 0 or N == 0 returns before any launch, NULL pointers allowed
+    assert fwd(L, M=0, x=None, y=None, codebook=None, indices=None) == B.HXQ_OK
+    assert fwd(L, N=0, x=None, y=None, codebook=None, indices=None) == B.HXQ_OK
+    assert fwd(L, fn="hxq_linear_fwd_pk12_ex", M=0, y=None) == B.HXQ_OK
+    assert L.hxq_sidecar_add(None, None, None, 0, None, 0, None, 4, 4, 4, None) == B.HXQ_OK
+
+
+def test_sidecar_add_rejects(L):
+    f = L.hxq_sidecar_add
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 3, FAKE, 1, 1, 1, None) == B.HXQ_ERR_DTYPE
+    assert f(FAKE, FAKE, FAKE, -1, FAKE, 0, FAKE, 1, 1, 1, None) == B.HXQ_ERR_SHAPE
+    assert f(None, FAKE, FAKE, 1, FAKE, 0, FAKE, 1, 1, 1, None) == B.HXQ_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 0, None, 1, 1, 1, None) == B.HXQ_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 1, FAKE + 2, 0, FAKE, 1, 1, 1, None) == B.HXQ_ERR_ALIGN
+
+
+def test_variant_selection(L):
+    sel = L.hxq_select_variant
+    # u8: bf16 x with M > 16 goes to the matrix-core GEMM, everything else to a GEMV
+    assert sel(0, B.HXQ_BF16, 2048, 11008, 2048) == B.HXQ_VARIANT_GEMM_BF16
+    assert sel(0, B.HXQ_BF16, 16, 11008, 2048) != B.HXQ_VARIANT_GEMM_BF16
+    assert sel(0, B.HXQ_F32, 64, 8512, 2048) != B.HXQ_VARIANT_GEMM_BF16
+    assert sel(1, B.HXQ_BF16, 2048, 11008, 2048) != B.HXQ_VARIANT_GEMM_BF16
+    # shapes the fast kernels do not take go to the generic kernel
+    assert sel(0, B.HXQ_F32, 1, 100, 100) == B.HXQ_VARIANT_GENERIC
+    assert sel(1, B.HXQ_F32, 1, 100, 6) == B.HXQ_VARIANT_GENERIC
+    assert sel(0, B.HXQ_F32, 1, 100, 0) == B.HXQ_VARIANT_GENERIC
+    assert sel(1, B.HXQ_F32, 1, 100, 7) == B.HXQ_ERR_SHAPE
+    assert sel(0, 5, 1, 1, 16) == B.HXQ_ERR_DTYPE
+
+
+def test_ctypes_signatures_match_header():
+    # the binding's argument counts follow the header's parameter lists
+    import re
+    with open(B.HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    for name, (_, args) in B.SIGNATURES.items():
+        m = re.search(r"\b%s\s*\(([^)]*)\)" % name, text)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(params) == len(args), name
+    assert ctypes.sizeof(ctypes.c_int64) == 8

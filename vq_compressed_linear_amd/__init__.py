@@ -1,0 +1,26 @@
+"""MI355X-native HelixLinear (HXQ) forward pass.
+
+The compute lives in libhxq (HIP kernels for gfx950 behind the C ABI declared
+in include/hxq.h); this package is its Python binding plus a thin layer
+object.  Importing it does not load the library; the first call does, and
+raises if the library has not been built.
+"""
+
+from ._binding import (  # noqa: F401
+    HXQ_BF16,
+    HXQ_F32,
+    HXQ_VARIANT_AUTO,
+    HXQ_VARIANT_GEMM_BF16,
+    HXQ_VARIANT_GEMV_MFMA,
+    HXQ_VARIANT_GEMV_VALU,
+    HXQ_VARIANT_GENERIC,
+    VARIANT_NAMES,
+    HxqError,
+    hxq_linear_fwd_pk12,
+    hxq_linear_fwd_u8,
+    hxq_select_variant,
+    hxq_sidecar_add,
+    hxq_version,
+    lib,
+)
+from .layer import HelixLinear  # noqa: F401

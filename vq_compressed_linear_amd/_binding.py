@@ -1,0 +1,213 @@
+"""ctypes binding of libhxq: argument marshalling only.
+
+Every function here checks tensor shapes and dtypes on the host, takes the raw
+device pointers and the current HIP stream, and calls the C entry point of the
+same name.  All arithmetic happens in the library's kernels; when the library
+is missing the calls raise instead of computing anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhxq.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "hxq.h")
+
+HXQ_OK = 0
+HXQ_ERR_NULL = -1
+HXQ_ERR_SHAPE = -2
+HXQ_ERR_DTYPE = -3
+HXQ_ERR_ALIGN = -4
+HXQ_ERR_UNSUPPORTED = -5
+HXQ_ERR_HIP = -6
+
+HXQ_F32 = 0
+HXQ_BF16 = 1
+
+HXQ_VARIANT_AUTO = 0
+HXQ_VARIANT_GEMV_VALU = 1
+HXQ_VARIANT_GEMV_MFMA = 2
+HXQ_VARIANT_GEMM_BF16 = 3
+HXQ_VARIANT_GENERIC = 4
+
+VARIANT_NAMES = {
+    HXQ_VARIANT_AUTO: "auto",
+    HXQ_VARIANT_GEMV_VALU: "gemv_valu",
+    HXQ_VARIANT_GEMV_MFMA: "gemv_mfma",
+    HXQ_VARIANT_GEMM_BF16: "gemm_bf16",
+    HXQ_VARIANT_GENERIC: "generic",
+}
+
+
+class HxqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (what, status_str(status), status))
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+
+_FWD_ARGS = [_P, _P, _P, _P, _P, _I64, _P, _INT, _P, _P, _I64, _I64, _I64, _P]
+SIGNATURES = {
+    "hxq_linear_fwd_u8": (_INT, _FWD_ARGS),
+    "hxq_linear_fwd_pk12": (_INT, _FWD_ARGS),
+    "hxq_linear_fwd_u8_ex": (_INT, _FWD_ARGS + [_INT]),
+    "hxq_linear_fwd_pk12_ex": (_INT, _FWD_ARGS + [_INT]),
+    "hxq_sidecar_add": (_INT, [_P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P]),
+    "hxq_select_variant": (_INT, [_INT, _INT, _I64, _I64, _I64]),
+    "hxq_status_str": (ctypes.c_char_p, [_INT]),
+    "hxq_version": (_INT, []),
+}
+
+
+def header_symbols(path: str = HEADER):
+    """Names of the functions include/hxq.h declares."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hxq_\w+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libhxq.so is not built (%s); run python -m vq_compressed_linear_amd.build"
+                               % LIB_PATH)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_str(status: int) -> str:
+    try:
+        return lib().hxq_status_str(status).decode()
+    except Exception:  # the library itself could not be loaded
+        return "status %d" % status
+
+
+# ------------------------------------------------------------ torch marshalling
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _x_dtype(x) -> int:
+    torch = _torch()
+    if x.dtype == torch.float32:
+        return HXQ_F32
+    if x.dtype == torch.bfloat16:
+        return HXQ_BF16
+    raise TypeError("x must be float32 or bfloat16, got %s" % x.dtype)
+
+
+def _check_sidecar(sc_rows, sc_cols, sc_deltas):
+    torch = _torch()
+    if sc_rows is None:
+        return 0
+    if sc_rows.dtype != torch.int32 or sc_cols.dtype != torch.int32 or sc_deltas.dtype != torch.float32:
+        raise TypeError("sidecar rows/cols must be int32 and deltas float32")
+    nnz = sc_rows.numel()
+    if sc_cols.numel() != nnz or sc_deltas.numel() != nnz:
+        raise ValueError("sidecar arrays differ in length")
+    for t in (sc_rows, sc_cols, sc_deltas):
+        if not t.is_contiguous():
+            raise ValueError("sidecar arrays must be contiguous")
+    return nnz
+
+
+def _check_common(x, bias, y, N):
+    torch = _torch()
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    M, K = x.shape
+    if y.dtype != torch.float32 or tuple(y.shape) != (M, N) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous float32 [M, N] tensor")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 [N] tensor")
+    return M, K
+
+
+def hxq_linear_fwd_u8(codebook, indices, sc_rows, sc_cols, sc_deltas, x, bias, y,
+                      stream=None, variant: int = HXQ_VARIANT_AUTO) -> None:
+    """y <- (C[indices] + S) x^T + bias on the device (u8 format)."""
+    torch = _torch()
+    if codebook.dtype != torch.float32 or codebook.numel() != 256:
+        raise ValueError("codebook must be 256 float32 values")
+    if indices.dtype != torch.uint8 or indices.dim() != 2 or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous uint8 [N, K] tensor")
+    N, K = indices.shape
+    M, Kx = _check_common(x, bias, y, N)
+    if Kx != K:
+        raise ValueError("x has K=%d, indices K=%d" % (Kx, K))
+    nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
+    st = lib().hxq_linear_fwd_u8_ex(
+        _ptr(codebook), _ptr(indices), _ptr(sc_rows), _ptr(sc_cols), _ptr(sc_deltas), nnz,
+        _ptr(x), _x_dtype(x), _ptr(bias), _ptr(y), M, N, K, _stream(stream), variant)
+    if st != HXQ_OK:
+        raise HxqError(st, "hxq_linear_fwd_u8")
+
+
+def hxq_linear_fwd_pk12(codebook2, packed, sc_rows, sc_cols, sc_deltas, x, bias, y,
+                        stream=None, variant: int = HXQ_VARIANT_AUTO) -> None:
+    """y <- (C2[unpack(packed)] + S) x^T + bias on the device (pk12 format)."""
+    torch = _torch()
+    if codebook2.dtype != torch.float32 or codebook2.numel() != 4096 * 2:
+        raise ValueError("codebook2 must be 4096 x 2 float32 values")
+    if packed.dtype != torch.uint8 or packed.dim() != 2 or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous uint8 [N, 3*ceil(K/4)] tensor")
+    N = packed.shape[0]
+    M, K = _check_common(x, bias, y, N)
+    if packed.shape[1] != 3 * ((K + 3) // 4):
+        raise ValueError("packed rows must hold 3*ceil(K/4) = %d bytes" % (3 * ((K + 3) // 4)))
+    nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
+    st = lib().hxq_linear_fwd_pk12_ex(
+        _ptr(codebook2), _ptr(packed), _ptr(sc_rows), _ptr(sc_cols), _ptr(sc_deltas), nnz,
+        _ptr(x), _x_dtype(x), _ptr(bias), _ptr(y), M, N, K, _stream(stream), variant)
+    if st != HXQ_OK:
+        raise HxqError(st, "hxq_linear_fwd_pk12")
+
+
+def hxq_sidecar_add(sc_rows, sc_cols, sc_deltas, x, y, stream=None) -> None:
+    """y <- y + S x^T on the device."""
+    nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
+    N = y.shape[1]
+    M, K = _check_common(x, None, y, N)
+    st = lib().hxq_sidecar_add(_ptr(sc_rows), _ptr(sc_cols), _ptr(sc_deltas), nnz, _ptr(x),
+                               _x_dtype(x), _ptr(y), M, N, K, _stream(stream))
+    if st != HXQ_OK:
+        raise HxqError(st, "hxq_sidecar_add")
+
+
+def hxq_select_variant(fmt_pk12: bool, x_dtype: int, M: int, N: int, K: int) -> int:
+    return lib().hxq_select_variant(int(bool(fmt_pk12)), x_dtype, M, N, K)
+
+
+def hxq_version() -> int:
+    return lib().hxq_version()

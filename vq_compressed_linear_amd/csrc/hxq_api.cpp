@@ -1,0 +1,177 @@
+// C entry points of libhxq: argument validation on the host, then dispatch to
+// one kernel family.  Nothing here touches device memory or allocates.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "../../include/hxq.h"
+#include "hxq_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)INT32_MAX - 65536;  // room for tile rounding in int32
+
+bool misaligned(const void* p, uintptr_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+// Checks shared by the forward entry points.  Returns HXQ_OK or an error.
+int validate_forward(const void* codebook, const uint8_t* indices, const int32_t* sc_rows,
+                     const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* x,
+                     int x_dtype, const float* bias, const float* y, int64_t M, int64_t N,
+                     int64_t K, bool pk12) {
+  if (x_dtype != HXQ_F32 && x_dtype != HXQ_BF16) return HXQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || nnz < 0) return HXQ_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim || nnz > kMaxDim) return HXQ_ERR_SHAPE;
+  if (pk12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return HXQ_OK;
+  if (!y) return HXQ_ERR_NULL;
+  if (K > 0 && (!x || !indices || !codebook)) return HXQ_ERR_NULL;
+  if (nnz > 0 && (!sc_rows || !sc_cols || !sc_deltas)) return HXQ_ERR_NULL;
+  const uintptr_t xs = x_dtype == HXQ_BF16 ? 2 : 4;
+  if (misaligned(x, xs) || misaligned(y, 4) || misaligned(codebook, 4) || misaligned(bias, 4) ||
+      misaligned(sc_rows, 4) || misaligned(sc_cols, 4) || misaligned(sc_deltas, 4))
+    return HXQ_ERR_ALIGN;
+  return HXQ_OK;
+}
+
+int select(bool pk12, bool x_bf16, int64_t M, int64_t K, bool gemv_ok, bool gemm_ok) {
+  if (K == 0) return HXQ_VARIANT_GENERIC;
+  if (!pk12 && x_bf16 && M > 16 && gemm_ok) return HXQ_VARIANT_GEMM_BF16;
+  if (gemv_ok) return HXQ_VARIANT_GEMV_VALU;
+  return HXQ_VARIANT_GENERIC;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? HXQ_OK : HXQ_ERR_HIP; }
+
+int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32_t* sc_rows,
+            const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* x, int x_dtype,
+            const float* bias, float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+            int variant) {
+  int st = validate_forward(codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, x, x_dtype, bias,
+                            y, M, N, K, pk12);
+  if (st != HXQ_OK) return st;
+  if (variant < HXQ_VARIANT_AUTO || variant > HXQ_VARIANT_GENERIC) return HXQ_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return HXQ_OK;
+  hxq::LayerArgs a;
+  a.codebook = codebook;
+  a.indices = indices;
+  a.sc_rows = sc_rows;
+  a.sc_cols = sc_cols;
+  a.sc_deltas = sc_deltas;
+  a.nnz = nnz;
+  a.x = x;
+  a.x_bf16 = x_dtype == HXQ_BF16;
+  a.bias = bias;
+  a.y = y;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  const bool gemv_ok = K > 0 && hxq::gemv_fast_path_ok(a, pk12);
+  const bool gemm_ok = K > 0 && !pk12 && hxq::gemm_path_ok(a);
+  int v = variant;
+  if (v == HXQ_VARIANT_AUTO) v = select(pk12, a.x_bf16, M, K, gemv_ok, gemm_ok);
+  (void)hipGetLastError();  // start from a clean error state
+  switch (v) {
+    case HXQ_VARIANT_GEMV_VALU:
+      if (!gemv_ok) return HXQ_ERR_UNSUPPORTED;
+      return status_of(hxq::launch_gemv_valu(a, pk12, stream));
+    case HXQ_VARIANT_GEMM_BF16:
+      if (!gemm_ok) return HXQ_ERR_UNSUPPORTED;
+      return status_of(hxq::launch_gemm_bf16(a, stream));
+    case HXQ_VARIANT_GENERIC:
+      return status_of(hxq::launch_generic(a, pk12, stream));
+    default:
+      return HXQ_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int hxq_linear_fwd_u8_ex(const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
+                         const int32_t* sc_cols, const float* sc_deltas, int64_t nnz,
+                         const void* x, int x_dtype, const float* bias, float* y, int64_t M,
+                         int64_t N, int64_t K, hipStream_t stream, int variant) {
+  return forward(false, codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, x, x_dtype, bias, y,
+                 M, N, K, stream, variant);
+}
+
+int hxq_linear_fwd_pk12_ex(const float* codebook2, const uint8_t* packed, const int32_t* sc_rows,
+                           const int32_t* sc_cols, const float* sc_deltas, int64_t nnz,
+                           const void* x, int x_dtype, const float* bias, float* y, int64_t M,
+                           int64_t N, int64_t K, hipStream_t stream, int variant) {
+  return forward(true, codebook2, packed, sc_rows, sc_cols, sc_deltas, nnz, x, x_dtype, bias, y, M,
+                 N, K, stream, variant);
+}
+
+int hxq_linear_fwd_u8(const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
+                      const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* x,
+                      int x_dtype, const float* bias, float* y, int64_t M, int64_t N, int64_t K,
+                      hipStream_t stream) {
+  return forward(false, codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, x, x_dtype, bias, y,
+                 M, N, K, stream, HXQ_VARIANT_AUTO);
+}
+
+int hxq_linear_fwd_pk12(const float* codebook2, const uint8_t* packed, const int32_t* sc_rows,
+                        const int32_t* sc_cols, const float* sc_deltas, int64_t nnz,
+                        const void* x, int x_dtype, const float* bias, float* y, int64_t M,
+                        int64_t N, int64_t K, hipStream_t stream) {
+  return forward(true, codebook2, packed, sc_rows, sc_cols, sc_deltas, nnz, x, x_dtype, bias, y, M,
+                 N, K, stream, HXQ_VARIANT_AUTO);
+}
+
+int hxq_sidecar_add(const int32_t* sc_rows, const int32_t* sc_cols, const float* sc_deltas,
+                    int64_t nnz, const void* x, int x_dtype, float* y, int64_t M, int64_t N,
+                    int64_t K, hipStream_t stream) {
+  if (x_dtype != HXQ_F32 && x_dtype != HXQ_BF16) return HXQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || nnz < 0) return HXQ_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim || nnz > kMaxDim) return HXQ_ERR_SHAPE;
+  if (M == 0 || N == 0 || nnz == 0) return HXQ_OK;
+  if (!sc_rows || !sc_cols || !sc_deltas || !y) return HXQ_ERR_NULL;
+  if (K > 0 && !x) return HXQ_ERR_NULL;
+  const uintptr_t xs = x_dtype == HXQ_BF16 ? 2 : 4;
+  if (misaligned(x, xs) || misaligned(y, 4) || misaligned(sc_rows, 4) || misaligned(sc_cols, 4) ||
+      misaligned(sc_deltas, 4))
+    return HXQ_ERR_ALIGN;
+  hxq::LayerArgs a = {};
+  a.sc_rows = sc_rows;
+  a.sc_cols = sc_cols;
+  a.sc_deltas = sc_deltas;
+  a.nnz = nnz;
+  a.x = x;
+  a.x_bf16 = x_dtype == HXQ_BF16;
+  a.y = y;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  (void)hipGetLastError();
+  return status_of(hxq::launch_sidecar_add(a, stream));
+}
+
+int hxq_select_variant(int fmt_pk12, int x_dtype, int64_t M, int64_t N, int64_t K) {
+  if (x_dtype != HXQ_F32 && x_dtype != HXQ_BF16) return HXQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return HXQ_ERR_SHAPE;
+  if (fmt_pk12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
+  const bool gemv_ok = K > 0 && K % 16 == 0;
+  const bool gemm_ok = !fmt_pk12 && x_dtype == HXQ_BF16 && K > 0 && K % 32 == 0;
+  return select(fmt_pk12 != 0, x_dtype == HXQ_BF16, M, K, gemv_ok, gemm_ok);
+}
+
+const char* hxq_status_str(int status) {
+  switch (status) {
+    case HXQ_OK: return "ok";
+    case HXQ_ERR_NULL: return "required pointer is NULL";
+    case HXQ_ERR_SHAPE: return "invalid shape";
+    case HXQ_ERR_DTYPE: return "unknown activation dtype";
+    case HXQ_ERR_ALIGN: return "misaligned pointer";
+    case HXQ_ERR_UNSUPPORTED: return "unsupported combination";
+    case HXQ_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int hxq_version(void) { return 100; }
+
+}  // extern "C"

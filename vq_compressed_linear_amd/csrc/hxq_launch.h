@@ -1,0 +1,43 @@
+// Host-side launchers of the libhxq kernels.  Arguments are validated by the
+// C entry points before any of these is called; each launcher only computes a
+// grid and queues the kernel on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hxq {
+
+struct LayerArgs {
+  const void* codebook;      // u8: float[256]; pk12: float[4096][2]
+  const uint8_t* indices;    // u8: [N][K]; pk12: [N][3*ceil(K/4)]
+  const int32_t* sc_rows;
+  const int32_t* sc_cols;
+  const float* sc_deltas;
+  int64_t nnz;
+  const void* x;             // [M][K] fp32 or bf16 bits
+  bool x_bf16;
+  const float* bias;         // [N] or nullptr
+  float* y;                  // [M][N]
+  int M, N, K;
+};
+
+int device_cu_count();
+
+// fp32-arithmetic GEMV on the vector ALUs, u8 or pk12; needs K % 16 == 0 and
+// 16-byte (u8) / 4-byte (pk12) aligned index rows, 16-byte aligned x rows.
+hipError_t launch_gemv_valu(const LayerArgs& a, bool pk12, hipStream_t stream);
+bool gemv_fast_path_ok(const LayerArgs& a, bool pk12);
+
+// Any shape and alignment: one wave per output row.
+hipError_t launch_generic(const LayerArgs& a, bool pk12, hipStream_t stream);
+
+// bf16 matrix-core GEMM for u8 with bf16 x; needs K % 32 == 0 and 16-byte
+// aligned index and x rows.
+hipError_t launch_gemm_bf16(const LayerArgs& a, hipStream_t stream);
+bool gemm_path_ok(const LayerArgs& a);
+
+// y += S x.
+hipError_t launch_sidecar_add(const LayerArgs& a, hipStream_t stream);
+
+}  // namespace hxq
