@@ -165,7 +165,7 @@ def build_set(torch, L, layers, M, xdt, cfg_x, copies, stream):
     return launch, devs, xs, ys
 
 
-def cpu_baseline(layers, M, budget_s=12.0):
+def cpu_baseline(layers, M, budget_s=15.0):
     """The CPU oracle over the same layer set, as many whole steps as fit in
     about `budget_s` seconds (at least one)."""
     import numpy as np
@@ -181,7 +181,7 @@ def cpu_baseline(layers, M, budget_s=12.0):
                                      "f32", lay.bias, want_bound=False)
         steps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 20:
+        if el >= budget_s or steps >= 500:
             break
     try:
         from threadpoolctl import threadpool_info
@@ -202,6 +202,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 10 times (for HBM counter scaling)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -217,6 +219,16 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "launches": 10}))
+        return 0
     L = hx.lib()
     stream = torch.cuda.current_stream().cuda_stream
     props = torch.cuda.get_device_properties(0)

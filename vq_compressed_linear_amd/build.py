@@ -18,7 +18,7 @@ OUT = os.path.join(HERE, "libhxq.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["hxq_gemv.hip", "hxq_gemm.hip", "hxq_api.cpp"]
+SOURCES = ["hxq_gemv.hip", "hxq_gemv_wg.hip", "hxq_gemm.hip", "hxq_api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -48,7 +48,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 namespace hxq {
 
 constexpr int kWave = 64;
@@ -55,6 +57,35 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// DPP lane exchange: lanes outside the enabled rows (or reading out of range) get 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Sum over the 64 lanes with DPP (no LDS traffic); the total is returned
+// wave-uniform (read from lane 63).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0xb1>(v);        // quad_perm(1,0,3,2): pairs
+  v += dpp_f<0x4e>(v);        // quad_perm(2,3,0,1): quads
+  v += dpp_f<0x141>(v);       // row_half_mirror: 8 lanes
+  v += dpp_f<0x140>(v);       // row_mirror: every lane holds its 16-lane row sum
+  v += dpp_f<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3; lane 63 holds the total
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Integer sum over the 64 lanes (wave-uniform result).
+__device__ __forceinline__ int wave_sum_dpp_i(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 // First sidecar entry with row >= target, searched by one wave in parallel:
 // each round the 64 lanes probe 64 evenly spaced positions of [lo, hi).
 // Every lane returns the same value.
@@ -77,6 +108,110 @@ __device__ __forceinline__ int64_t wave_lower_bound_rows(const int32_t* rows, in
   const int64_t p = lo + lane;
   const bool below = (p < hi) && (rows[p] < target);
   return lo + __popcll(__ballot(below));
+}
+
+// The same lower bound, first tried in one round: the wave reads the 1024
+// triplet rows around the position a uniform spread would put `target` at
+// (`guess`), 16 consecutive ones per lane.  When the answer is strictly inside
+// that window it is the number of rows below `target` there; otherwise the
+// general search runs.
+__device__ __forceinline__ int64_t wave_lower_bound_rows_near(const int32_t* rows, int64_t nnz,
+                                                              int32_t target, int64_t guess) {
+  constexpr int64_t WIN = 16 * kWave;
+  if (nnz <= WIN) {
+    // the whole array fits the window
+    const int lane = lane_id();
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t p = (int64_t)lane * 16 + j;
+      c += (p < nnz && rows[p] < target) ? 1 : 0;
+    }
+    return wave_sum_dpp_i(c);
+  }
+  int64_t ws = guess - WIN / 2;
+  if (ws < 0) ws = 0;
+  if (ws > nnz - WIN) ws = nnz - WIN;
+  const int lane = lane_id();
+  const int4* base = reinterpret_cast<const int4*>(rows + ws + (int64_t)lane * 16);
+  int c = 0;
+  if (((uintptr_t)(rows + ws) & 15) == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int4 v = base[q];
+      c += (v.x < target) + (v.y < target) + (v.z < target) + (v.w < target);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c += rows[ws + (int64_t)lane * 16 + j] < target ? 1 : 0;
+  }
+  const int total = wave_sum_dpp_i(c);
+  const bool lo_ok = total > 0 || ws == 0;
+  const bool hi_ok = total < WIN || ws + WIN == nnz;
+  if (lo_ok && hi_ok) return ws + total;
+  return wave_lower_bound_rows(rows, nnz, target);
+}
+
+// Asynchronous copies global -> LDS (LDS DMA).  Each active lane moves its 4 or
+// 16 bytes; lane i's bytes land at lds_base + i * size.  The LDS base must be
+// wave-uniform.  Completion is tracked by the vector-memory counter.
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+__device__ __forceinline__ void lds_dma16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void_ptr)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void lds_dma4(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void_ptr)lds_base, 4, 0, 0);
+}
+
+// Split form of the window lookup, so its loads can be issued ahead of other
+// traffic and resolved later: `issue` reads the 1024 triplet rows around
+// `guess` (16 consecutive per lane), `resolve` counts those below `target`
+// and falls back to the general search when the answer is not inside.
+struct WindowProbe {
+  int64_t ws;
+  int4 v[4];
+};
+
+__device__ __forceinline__ void window_issue(WindowProbe& w, const int32_t* rows, int64_t nnz, int64_t guess) {
+  constexpr int64_t WIN = 16 * kWave;
+  int64_t ws = 0;
+  if (nnz > WIN) {
+    ws = (guess - WIN / 2) & ~(int64_t)3;
+    if (ws < 0) ws = 0;
+    if (ws > nnz - WIN) ws = nnz - WIN;
+  }
+  w.ws = ws;
+  const int64_t p0 = ws + (int64_t)lane_id() * 16;
+  if (nnz >= WIN && ((reinterpret_cast<uintptr_t>(rows + ws) & 15) == 0)) {
+    const int4* b = reinterpret_cast<const int4*>(rows + p0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w.v[q] = b[q];
+  } else {
+    int t[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t[j] = (p0 + j < nnz) ? rows[p0 + j] : INT_MAX;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w.v[q] = make_int4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);
+  }
+}
+
+__device__ __forceinline__ int64_t window_resolve(const WindowProbe& w, const int32_t* rows, int64_t nnz,
+                                                  int32_t target) {
+  constexpr int64_t WIN = 16 * kWave;
+  const int64_t p0 = w.ws + (int64_t)lane_id() * 16;
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t p = p0 + 4 * q;
+    c += (p + 0 < nnz && w.v[q].x < target) + (p + 1 < nnz && w.v[q].y < target) +
+         (p + 2 < nnz && w.v[q].z < target) + (p + 3 < nnz && w.v[q].w < target);
+  }
+  const int64_t total = wave_sum_dpp_i(c);
+  const int64_t wend = w.ws + WIN < nnz ? w.ws + WIN : nnz;
+  if ((total > 0 || w.ws == 0) && (w.ws + total < wend || wend == nnz)) return w.ws + total;
+  return wave_lower_bound_rows(rows, nnz, target);
 }
 
 }  // namespace hxq

@@ -27,6 +27,10 @@ int device_cu_count();
 // fp32-arithmetic GEMV on the vector ALUs, u8 or pk12; needs K % 16 == 0 and
 // 16-byte (u8) / 4-byte (pk12) aligned index rows, 16-byte aligned x rows.
 hipError_t launch_gemv_valu(const LayerArgs& a, bool pk12, hipStream_t stream);
+
+// One 1024-thread workgroup per CU with x staged in LDS (M <= 4); returns
+// false without launching when x does not fit.
+bool launch_gemv_wg(const LayerArgs& a, bool pk12, hipStream_t stream, hipError_t& err);
 bool gemv_fast_path_ok(const LayerArgs& a, bool pk12);
 
 // Any shape and alignment: one wave per output row.
