@@ -107,6 +107,43 @@ int hxq_sidecar_add(const int32_t* sc_rows, const int32_t* sc_cols,
                     const void* x, int x_dtype, float* y,
                     int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/* Several layers applied to the same activations in one call, for instance
+ * the query, key and value projections of an attention block or the gate and
+ * up projections of an MLP block.  Each layer keeps its own codebook, indices,
+ * sidecar, bias and output (the HXQ whitepaper fits one codebook per weight
+ * tensor, "Method"); all share the format, x, M and K.  Each layer's y is what
+ * hxq_linear_fwd_u8 / hxq_linear_fwd_pk12 would compute for it, within the
+ * same tolerance; for M <= 4 the layers normally run in a single launch, and
+ * otherwise one after another on `stream`.
+ *   fmt     HXQ_FMT_U8 or HXQ_FMT_PK12.
+ *   layers  host array of `count` descriptors, 1 <= count <= HXQ_MAX_GROUP,
+ *           read during the call only.  Each field means what the argument of
+ *           the same name means for the single-layer entry points; a layer
+ *           with N == 0 is skipped.
+ *   x, x_dtype, M, K, stream as for the single-layer entry points.
+ * Errors: HXQ_ERR_SHAPE for count out of range or an unknown fmt, otherwise the
+ * first error the single-layer entry point would return for any layer;
+ * nothing is launched when an error is returned. */
+enum hxq_format { HXQ_FMT_U8 = 0, HXQ_FMT_PK12 = 1 };
+
+#define HXQ_MAX_GROUP 8
+
+typedef struct hxq_layer {
+  const void* codebook;     /* u8: float[256]; pk12: float[4096][2] */
+  const uint8_t* indices;   /* u8: [N][K]; pk12: [N][3*ceil(K/4)] */
+  const int32_t* sc_rows;
+  const int32_t* sc_cols;
+  const float* sc_deltas;
+  int64_t nnz;
+  const float* bias;        /* [N] or NULL */
+  float* y;                 /* [M][N] float32, overwritten */
+  int64_t N;
+} hxq_layer;
+
+int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count,
+                           const void* x, int x_dtype, int64_t M, int64_t K,
+                           hipStream_t stream);
+
 /* Kernel selection, for tests and measurement.  HXQ_VARIANT_AUTO is what the
  * entry points above use; the others force one kernel family and return
  * HXQ_ERR_UNSUPPORTED when it cannot take the call. */

@@ -122,3 +122,51 @@ def test_ctypes_signatures_match_header():
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         assert len(params) == len(args), name
     assert ctypes.sizeof(ctypes.c_int64) == 8
+
+
+def _layers(n, **kw):
+    arr = (B.HxqLayer * n)()
+    for i in range(n):
+        d = dict(codebook=FAKE, indices=FAKE, sc_rows=FAKE, sc_cols=FAKE, sc_deltas=FAKE, nnz=0,
+                 bias=FAKE, y=FAKE, N=8)
+        d.update(kw if i == n - 1 else {})
+        arr[i] = B.HxqLayer(**d)
+    return arr
+
+
+def test_grouped_struct_layout():
+    # struct hxq_layer: eight 8-byte fields and N, no padding
+    assert ctypes.sizeof(B.HxqLayer) == 9 * 8
+    assert B.HxqLayer.N.offset == 64 and B.HxqLayer.nnz.offset == 40
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(y=None), B.HXQ_ERR_NULL),
+    (dict(indices=None), B.HXQ_ERR_NULL),
+    (dict(nnz=2, sc_cols=None), B.HXQ_ERR_NULL),
+    (dict(N=-1), B.HXQ_ERR_SHAPE),
+    (dict(nnz=-1), B.HXQ_ERR_SHAPE),
+    (dict(y=FAKE + 2), B.HXQ_ERR_ALIGN),
+    (dict(bias=FAKE + 1), B.HXQ_ERR_ALIGN),
+])
+def test_grouped_rejects(L, kw, want):
+    # the last of three layers is bad: nothing may be launched for the others
+    f = L.hxq_linear_fwd_grouped
+    assert f(B.HXQ_FMT_U8, _layers(3, **kw), 3, FAKE, B.HXQ_F32, 1, 16, None) == want
+    assert f(B.HXQ_FMT_PK12, _layers(3, **kw), 3, FAKE, B.HXQ_F32, 1, 16, None) == want
+
+
+def test_grouped_rejects_call_arguments(L):
+    f = L.hxq_linear_fwd_grouped
+    good = _layers(2)
+    assert f(2, good, 2, FAKE, B.HXQ_F32, 1, 16, None) == B.HXQ_ERR_SHAPE
+    assert f(B.HXQ_FMT_U8, good, 0, FAKE, B.HXQ_F32, 1, 16, None) == B.HXQ_ERR_SHAPE
+    assert f(B.HXQ_FMT_U8, _layers(9), 9, FAKE, B.HXQ_F32, 1, 16, None) == B.HXQ_ERR_SHAPE
+    assert f(B.HXQ_FMT_U8, None, 1, FAKE, B.HXQ_F32, 1, 16, None) == B.HXQ_ERR_NULL
+    assert f(B.HXQ_FMT_U8, good, 2, FAKE, 7, 1, 16, None) == B.HXQ_ERR_DTYPE
+    assert f(B.HXQ_FMT_U8, good, 2, FAKE + 2, B.HXQ_F32, 1, 16, None) == B.HXQ_ERR_ALIGN
+    assert f(B.HXQ_FMT_PK12, good, 2, FAKE, B.HXQ_F32, 1, 15, None) == B.HXQ_ERR_SHAPE
+    assert f(B.HXQ_FMT_U8, good, 2, FAKE, B.HXQ_F32, -1, 16, None) == B.HXQ_ERR_SHAPE
+    # M == 0 and all-empty layers launch nothing
+    assert f(B.HXQ_FMT_U8, good, 2, FAKE, B.HXQ_F32, 0, 16, None) == B.HXQ_OK
+    assert f(B.HXQ_FMT_U8, _layers(2, N=0), 1, FAKE, B.HXQ_F32, 0, 16, None) == B.HXQ_OK

@@ -9,6 +9,9 @@ raises if the library has not been built.
 from ._binding import (  # noqa: F401
     HXQ_BF16,
     HXQ_F32,
+    HXQ_FMT_PK12,
+    HXQ_FMT_U8,
+    HXQ_MAX_GROUP,
     HXQ_VARIANT_AUTO,
     HXQ_VARIANT_GEMM_BF16,
     HXQ_VARIANT_GEMV_MFMA,
@@ -16,6 +19,8 @@ from ._binding import (  # noqa: F401
     HXQ_VARIANT_GENERIC,
     VARIANT_NAMES,
     HxqError,
+    HxqLayer,
+    hxq_linear_fwd_grouped,
     hxq_linear_fwd_pk12,
     hxq_linear_fwd_u8,
     hxq_select_variant,

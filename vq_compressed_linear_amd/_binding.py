@@ -34,6 +34,10 @@ HXQ_VARIANT_GEMV_MFMA = 2
 HXQ_VARIANT_GEMM_BF16 = 3
 HXQ_VARIANT_GENERIC = 4
 
+HXQ_FMT_U8 = 0
+HXQ_FMT_PK12 = 1
+HXQ_MAX_GROUP = 8
+
 VARIANT_NAMES = {
     HXQ_VARIANT_AUTO: "auto",
     HXQ_VARIANT_GEMV_VALU: "gemv_valu",
@@ -55,6 +59,15 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _INT = ctypes.c_int
 
+class HxqLayer(ctypes.Structure):
+    """struct hxq_layer of include/hxq.h."""
+
+    _fields_ = [("codebook", ctypes.c_void_p), ("indices", ctypes.c_void_p),
+                ("sc_rows", ctypes.c_void_p), ("sc_cols", ctypes.c_void_p),
+                ("sc_deltas", ctypes.c_void_p), ("nnz", ctypes.c_int64),
+                ("bias", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64)]
+
+
 _FWD_ARGS = [_P, _P, _P, _P, _P, _I64, _P, _INT, _P, _P, _I64, _I64, _I64, _P]
 SIGNATURES = {
     "hxq_linear_fwd_u8": (_INT, _FWD_ARGS),
@@ -62,6 +75,7 @@ SIGNATURES = {
     "hxq_linear_fwd_u8_ex": (_INT, _FWD_ARGS + [_INT]),
     "hxq_linear_fwd_pk12_ex": (_INT, _FWD_ARGS + [_INT]),
     "hxq_sidecar_add": (_INT, [_P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P]),
+    "hxq_linear_fwd_grouped": (_INT, [_INT, ctypes.POINTER(HxqLayer), _INT, _P, _INT, _I64, _I64, _P]),
     "hxq_select_variant": (_INT, [_INT, _INT, _I64, _I64, _I64]),
     "hxq_status_str": (ctypes.c_char_p, [_INT]),
     "hxq_version": (_INT, []),
@@ -203,6 +217,45 @@ def hxq_sidecar_add(sc_rows, sc_cols, sc_deltas, x, y, stream=None) -> None:
                                _x_dtype(x), _ptr(y), M, N, K, _stream(stream))
     if st != HXQ_OK:
         raise HxqError(st, "hxq_sidecar_add")
+
+
+def grouped_layers(fmt: int, layers, M: int, K: int):
+    """HxqLayer array for hxq_linear_fwd_grouped from dicts holding the
+    tensors codebook, indices, sc_rows, sc_cols, sc_deltas, bias (or None) and
+    y.  Checks dtypes and shapes like the single-layer functions."""
+    torch = _torch()
+    if not 1 <= len(layers) <= HXQ_MAX_GROUP:
+        raise ValueError("between 1 and %d layers per call" % HXQ_MAX_GROUP)
+    arr = (HxqLayer * len(layers))()
+    for i, l in enumerate(layers):
+        cb, idx, y, bias = l["codebook"], l["indices"], l["y"], l.get("bias")
+        if cb.dtype != torch.float32 or cb.numel() != (256 if fmt == HXQ_FMT_U8 else 8192):
+            raise ValueError("layer %d: wrong codebook size or dtype" % i)
+        if idx.dtype != torch.uint8 or idx.dim() != 2 or not idx.is_contiguous():
+            raise ValueError("layer %d: indices must be a contiguous uint8 matrix" % i)
+        N = idx.shape[0]
+        row = K if fmt == HXQ_FMT_U8 else 3 * ((K + 3) // 4)
+        if idx.shape[1] != row:
+            raise ValueError("layer %d: index rows hold %d bytes, expected %d" % (i, idx.shape[1], row))
+        if y.dtype != torch.float32 or tuple(y.shape) != (M, N) or not y.is_contiguous():
+            raise ValueError("layer %d: y must be a contiguous float32 [M, N] tensor" % i)
+        if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N):
+            raise ValueError("layer %d: bias must be float32 [N]" % i)
+        nnz = _check_sidecar(l.get("sc_rows"), l.get("sc_cols"), l.get("sc_deltas"))
+        arr[i] = HxqLayer(_ptr(cb), _ptr(idx), _ptr(l.get("sc_rows")), _ptr(l.get("sc_cols")),
+                          _ptr(l.get("sc_deltas")), nnz, _ptr(bias), _ptr(y), N)
+    return arr
+
+
+def hxq_linear_fwd_grouped(fmt: int, layers, x, stream=None) -> None:
+    """Each layer's y <- (codebook[indices] + S) x^T + bias, all from one x."""
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    M, K = x.shape
+    arr = grouped_layers(fmt, layers, M, K)
+    st = lib().hxq_linear_fwd_grouped(fmt, arr, len(layers), _ptr(x), _x_dtype(x), M, K, _stream(stream))
+    if st != HXQ_OK:
+        raise HxqError(st, "hxq_linear_fwd_grouped")
 
 
 def hxq_select_variant(fmt_pk12: bool, x_dtype: int, M: int, N: int, K: int) -> int:

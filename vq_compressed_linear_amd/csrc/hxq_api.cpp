@@ -122,6 +122,53 @@ int hxq_linear_fwd_pk12(const float* codebook2, const uint8_t* packed, const int
                  N, K, stream, HXQ_VARIANT_AUTO);
 }
 
+int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const void* x, int x_dtype,
+                           int64_t M, int64_t K, hipStream_t stream) {
+  if (fmt != HXQ_FMT_U8 && fmt != HXQ_FMT_PK12) return HXQ_ERR_SHAPE;
+  if (count < 1 || count > HXQ_MAX_GROUP) return HXQ_ERR_SHAPE;
+  if (!layers) return HXQ_ERR_NULL;
+  const bool pk12 = fmt == HXQ_FMT_PK12;
+  for (int i = 0; i < count; ++i) {
+    const hxq_layer& l = layers[i];
+    const int st = validate_forward(l.codebook, l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz, x,
+                                    x_dtype, l.bias, l.y, M, l.N, K, pk12);
+    if (st != HXQ_OK) return st;
+  }
+  if (M == 0) return HXQ_OK;
+  // one launch when every non-empty layer fits the decode kernel
+  hxq::DecodeSeg segs[hxq::kMaxSegments];
+  int nseg = 0;
+  bool fast = K > 0 && M <= 4;
+  for (int i = 0; i < count && fast; ++i) {
+    const hxq_layer& l = layers[i];
+    if (l.N == 0) continue;
+    hxq::LayerArgs a = {};
+    a.codebook = l.codebook;
+    a.indices = l.indices;
+    a.x = x;
+    a.x_bf16 = x_dtype == HXQ_BF16;
+    a.M = (int)M;
+    a.N = (int)l.N;
+    a.K = (int)K;
+    if (!hxq::gemv_fast_path_ok(a, pk12)) fast = false;
+    segs[nseg++] = {l.codebook, l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz, l.bias, l.y, (int)l.N, 0, 0, 0.f};
+  }
+  if (fast && nseg == 0) return HXQ_OK;
+  if (fast && hxq::decode_fits(segs, nseg, pk12, x_dtype == HXQ_BF16, (int)M, (int)K)) {
+    (void)hipGetLastError();
+    hipError_t err = hipSuccess;
+    if (hxq::launch_decode(segs, nseg, pk12, x, x_dtype == HXQ_BF16, (int)M, (int)K, stream, err))
+      return status_of(err);
+  }
+  for (int i = 0; i < count; ++i) {
+    const hxq_layer& l = layers[i];
+    const int st = forward(pk12, l.codebook, l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz, x, x_dtype,
+                           l.bias, l.y, M, l.N, K, stream, HXQ_VARIANT_AUTO);
+    if (st != HXQ_OK) return st;
+  }
+  return HXQ_OK;
+}
+
 int hxq_sidecar_add(const int32_t* sc_rows, const int32_t* sc_cols, const float* sc_deltas,
                     int64_t nnz, const void* x, int x_dtype, float* y, int64_t M, int64_t N,
                     int64_t K, hipStream_t stream) {

@@ -165,51 +165,63 @@ __device__ __forceinline__ void lds_dma4(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (lds_void_ptr)lds_base, 4, 0, 0);
 }
 
+// A flag in LDS shared by the waves of one workgroup, read and written as
+// LDS accesses (a volatile access through a generic pointer becomes a flat
+// access, whose completion is tracked on the vector-memory counter as well,
+// so every wait for it would also wait for all loads in flight).
+typedef __attribute__((address_space(3))) int lds_int;
+
+__device__ __forceinline__ int lds_flag_load(int* p) {
+  return __hip_atomic_load((lds_int*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void lds_flag_store(int* p, int v) {
+  __hip_atomic_store((lds_int*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // Split form of the window lookup, so its loads can be issued ahead of other
 // traffic and resolved later: `issue` reads the 1024 triplet rows around
-// `guess` (16 consecutive per lane), `resolve` counts those below `target`
-// and falls back to the general search when the answer is not inside.
+// `guess` (entry ws + 64 j + lane in load j, so each load instruction covers
+// 256 consecutive bytes; positions past the end re-read the last entry, so
+// the loads are unconditional); `resolve` counts those below `target` and
+// falls back to the general search when the answer is not inside the window.
 struct WindowProbe {
   int64_t ws;
-  int4 v[4];
+  int v[16];
 };
 
 __device__ __forceinline__ void window_issue(WindowProbe& w, const int32_t* rows, int64_t nnz, int64_t guess) {
   constexpr int64_t WIN = 16 * kWave;
   int64_t ws = 0;
   if (nnz > WIN) {
-    ws = (guess - WIN / 2) & ~(int64_t)3;
+    ws = guess - WIN / 2;
     if (ws < 0) ws = 0;
     if (ws > nnz - WIN) ws = nnz - WIN;
   }
   w.ws = ws;
-  const int64_t p0 = ws + (int64_t)lane_id() * 16;
-  if (nnz >= WIN && ((reinterpret_cast<uintptr_t>(rows + ws) & 15) == 0)) {
-    const int4* b = reinterpret_cast<const int4*>(rows + p0);
+  // wave-uniform base and 32-bit lane offsets, clamped to the last entry
+  const int32_t* base = rows + ws;
+  const int lim = (int)(nnz - ws < WIN ? nnz - ws : WIN) - 1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w.v[q] = b[q];
-  } else {
-    int t[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) t[j] = (p0 + j < nnz) ? rows[p0 + j] : INT_MAX;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w.v[q] = make_int4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);
-  }
+  for (int j = 0; j < 16; ++j) w.v[j] = base[min(lane_id() + j * kWave, lim)];
 }
 
 __device__ __forceinline__ int64_t window_resolve(const WindowProbe& w, const int32_t* rows, int64_t nnz,
                                                   int32_t target) {
   constexpr int64_t WIN = 16 * kWave;
-  const int64_t p0 = w.ws + (int64_t)lane_id() * 16;
+  const int n = (int)(nnz - w.ws < WIN ? nnz - w.ws : WIN);  // entries in the window
   int c = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t p = p0 + 4 * q;
-    c += (p + 0 < nnz && w.v[q].x < target) + (p + 1 < nnz && w.v[q].y < target) +
-         (p + 2 < nnz && w.v[q].z < target) + (p + 3 < nnz && w.v[q].w < target);
+  for (int j = 0; j < 16; ++j) {
+    // an empty asm that "modifies" the value keeps the compiler from hoisting
+    // this comparison (and so the wait for the load) above the caller's
+    // barrier, which would stall the issue of loads placed after the probe
+    int v = w.v[j];
+    asm volatile("" : "+v"(v));
+    c += (lane_id() + j * kWave < n && v < target) ? 1 : 0;
   }
   const int64_t total = wave_sum_dpp_i(c);
-  const int64_t wend = w.ws + WIN < nnz ? w.ws + WIN : nnz;
+  const int64_t wend = w.ws + n;
   if ((total > 0 || w.ws == 0) && (w.ws + total < wend || wend == nnz)) return w.ws + total;
   return wave_lower_bound_rows(rows, nnz, target);
 }

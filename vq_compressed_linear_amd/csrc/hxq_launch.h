@@ -28,10 +28,42 @@ int device_cu_count();
 // 16-byte (u8) / 4-byte (pk12) aligned index rows, 16-byte aligned x rows.
 hipError_t launch_gemv_valu(const LayerArgs& a, bool pk12, hipStream_t stream);
 
-// One 1024-thread workgroup per CU with x staged in LDS (M <= 4); returns
-// false without launching when x does not fit.
-bool launch_gemv_wg(const LayerArgs& a, bool pk12, hipStream_t stream, hipError_t& err);
 bool gemv_fast_path_ok(const LayerArgs& a, bool pk12);
+
+// One layer of a decode launch.  The launcher fills in the row split and the
+// sidecar density.
+constexpr int kMaxSegments = 8;
+struct DecodeSeg {
+  const void* codebook;
+  const uint8_t* indices;
+  const int32_t* sc_rows;
+  const int32_t* sc_cols;
+  const float* sc_deltas;
+  int64_t nnz;
+  const float* bias;
+  float* y;  // [M][N]
+  int N;
+  int rows_q, rows_r;  // workgroup j owns rows_q rows, plus one when j < rows_r
+  float side_per_row;  // nnz / N, to guess where a row's triplets start
+};
+
+struct DecodeArgs {
+  int wg0[kMaxSegments];  // first workgroup of each layer; INT_MAX past the last
+  int grid;               // workgroups in the launch
+  int M, K;
+  int S;                  // K slices
+  int rows_cap;           // most rows owned by one workgroup
+  const void* x;          // [M][K], shared by all layers
+  DecodeSeg seg[kMaxSegments];
+};
+
+// Decode GEMV for M <= 4 over up to kMaxSegments layers that share x and K
+// (one 1024-thread workgroup per CU, x and the codebook staged in LDS).
+// Returns false without launching when the call does not fit (M > 4, x too
+// large for LDS); needs the fast-path shape and alignment rules.
+bool launch_decode(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
+                   hipStream_t stream, hipError_t& err);
+bool decode_fits(const DecodeSeg* segs, int nseg, bool pk12, bool xbf, int M, int K);
 
 // Any shape and alignment: one wave per output row.
 hipError_t launch_generic(const LayerArgs& a, bool pk12, hipStream_t stream);
