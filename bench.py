@@ -1,17 +1,22 @@
 #!/usr/bin/env python3
 """HelixLinear forward throughput on one MI355X.
 
-Workload (default): the Qwen2.5-3B-shaped u8 layer set (q, k, v, o, gate, up,
-down; 7 HelixLinear layers with their own 256-entry codebooks and 0.1%
-sidecars), decode with one token (M = 1), fp32 activations.  A step is one
-forward through all 7 layers.  Inputs are seeded synthetic data resident in HBM
-before timing; the compressed weights rotate over enough copies (>= 512 MB)
-that no layer is served from the 256 MB Infinity Cache.
+Workload: the Qwen2.5-3B-shaped u8 layer set (q, k, v, o, gate, up, down:
+seven HelixLinear layers, each with its own 256-entry codebook and a 0.1%
+sidecar), decode with one token (M = 1), fp32 activations.  A step is one
+forward through all seven layers, issued the way a decoder layer issues them:
+the projections that read the same activations share a launch
+(hxq_linear_fwd_grouped for q|k|v and gate|up; o and down alone), four
+launches in all.  Inputs are seeded synthetic data resident in HBM before
+timing; the compressed weights rotate over enough copies (>= 512 MB) that no
+step is served from the 256 MB Infinity Cache.
 
-Reported value: algorithmic GB/s of the step (compressed bytes the method must
-move: indices, codebook, sidecar triplets, x, bias, y) over the GPU time of the
-timed steps.  Extra fields carry the M = 8 decode set and the bf16 prefill
-GEMM at M = 2048 (TFLOP/s), the roofline of the dominant kernel and the CPU
+value: algorithmic GB/s of the step (the compressed bytes the method must
+move: indices, codebooks, sidecar triplets, x once per launch, bias, y) over
+the GPU time of the timed steps.  Also reported: the same step issued as seven
+single-layer calls, the M = 8 step, the bf16 prefill GEMM at M = 2048
+(TFLOP/s), the read bandwidth of a plain streaming kernel over the same
+rotated buffers, the roofline of the dominant launch (gate|up) and the CPU
 oracle baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -34,32 +39,40 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2516.6   # MI355X dense bf16 matrix (256 CU x 2.4 GHz x 4096 flop/clk)
 MALL_BYTES = 256 << 20
 ROTATE_BYTES = 2 * MALL_BYTES
+GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+DOMINANT = 2                  # gate|up: the largest launch of the step
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(fmt, N, K, nnz, M, x_bytes, bias=True):
-    """Bytes the forward must move for one layer: index storage, codebook,
-    sidecar triplets (12 B each), activations, bias and the fp32 output."""
+def layer_bytes(fmt, N, K, nnz, M, x_bytes, bias=True, with_x=True):
+    """Bytes one layer's forward must move: index storage, codebook, sidecar
+    triplets (12 B each), activations (unless another layer of the same
+    launch reads them), bias and the fp32 output."""
     if fmt == "u8":
         idx, cb = N * K, 256 * 4
     else:
         idx, cb = N * 3 * ((K + 3) // 4), 4096 * 8
-    return idx + cb + 12 * nnz + M * K * x_bytes + (4 * N if bias else 0) + 4 * M * N
+    return idx + cb + 12 * nnz + (M * K * x_bytes if with_x else 0) + (4 * N if bias else 0) + 4 * M * N
+
+
+def group_bytes(layers, M, x_bytes):
+    return sum(layer_bytes(l.fmt, l.N, l.K, l.nnz, M, x_bytes, with_x=(i == 0)) for i, l in enumerate(layers))
 
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("hxq_device.h", "hxq_gemv.hip", "hxq_gemm.hip", "hxq_launch.h", "hxq_api.cpp"):
-        with open(os.path.join(ROOT, "vq_compressed_linear_amd", "csrc", f), "rb") as fh:
+    csrc = os.path.join(ROOT, "vq_compressed_linear_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def load_traffic(kernel_key):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, or
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when absent or taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -74,24 +87,6 @@ def load_traffic(kernel_key):
     return rec.get("hbm_bytes_per_launch")
 
 
-class Launcher:
-    """Pre-marshalled C-ABI calls for one layer copy (keeps host overhead low)."""
-
-    def __init__(self, L, fmt, d, x, y, M, N, K, stream):
-        import vq_compressed_linear_amd as hx
-
-        self.fn = L.hxq_linear_fwd_u8 if fmt == "u8" else L.hxq_linear_fwd_pk12
-        self.args = (d["codebook"].data_ptr(), d["indices"].data_ptr(), d["rows"].data_ptr(),
-                     d["cols"].data_ptr(), d["deltas"].data_ptr(), d["rows"].numel(),
-                     x.data_ptr(), hx.HXQ_BF16 if x.dtype.is_floating_point and x.element_size() == 2
-                     else hx.HXQ_F32, d["bias"].data_ptr(), y.data_ptr(), M, N, K, stream)
-
-    def __call__(self):
-        st = self.fn(*self.args)
-        if st != 0:
-            raise RuntimeError("libhxq call failed with status %d" % st)
-
-
 def to_dev(lay, torch):
     import numpy as np
 
@@ -102,74 +97,137 @@ def to_dev(lay, torch):
                 cols=t(lay.cols, np.int32), deltas=t(lay.deltas, np.float32), bias=t(lay.bias, np.float32))
 
 
+class GroupCall:
+    """One pre-marshalled hxq_linear_fwd_grouped call (keeps host overhead low)."""
+
+    def __init__(self, L, B, devs, ys, x, M, K, stream):
+        arr = (B.HxqLayer * len(devs))()
+        for i, (d, y) in enumerate(zip(devs, ys)):
+            arr[i] = B.HxqLayer(d["codebook"].data_ptr(), d["indices"].data_ptr(), d["rows"].data_ptr(),
+                                d["cols"].data_ptr(), d["deltas"].data_ptr(), d["rows"].numel(),
+                                d["bias"].data_ptr(), y.data_ptr(), y.shape[1])
+        self.fn = L.hxq_linear_fwd_grouped
+        xdt = B.HXQ_BF16 if x.element_size() == 2 else B.HXQ_F32
+        self.args = (B.HXQ_FMT_U8, arr, len(devs), x.data_ptr(), xdt, M, K, stream)
+        self.keep = arr
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError("hxq_linear_fwd_grouped failed with status %d" % st)
+
+
+class LayerCall:
+    """One pre-marshalled single-layer call."""
+
+    def __init__(self, L, B, d, y, x, M, N, K, stream):
+        self.fn = L.hxq_linear_fwd_u8
+        xdt = B.HXQ_BF16 if x.element_size() == 2 else B.HXQ_F32
+        self.args = (d["codebook"].data_ptr(), d["indices"].data_ptr(), d["rows"].data_ptr(), d["cols"].data_ptr(),
+                     d["deltas"].data_ptr(), d["rows"].numel(), x.data_ptr(), xdt, d["bias"].data_ptr(),
+                     y.data_ptr(), M, N, K, stream)
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError("hxq_linear_fwd_u8 failed with status %d" % st)
+
+
 def hold_gpu(torch, ms):
     """Keep the GPU busy for about `ms` so the host can queue a timed region
     ahead of execution (launch latency then stays out of the event times)."""
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(ms * 2.0e6))
-        return
-    a = torch.randn(4096, 4096, device="cuda")
-    for _ in range(max(1, int(ms / 0.5))):
-        a = a @ a
-        a = a / a.norm()
+    torch.cuda._sleep(int(ms * 2.0e6))
 
 
-def time_steps(torch, launchers, steps, warmup, per_kernel=True):
-    """launchers[r][i]: copy r, layer i.  Returns (total_ms, [per-launch ms by layer])."""
-    R = len(launchers)
-    nl = len(launchers[0])
+def time_steps(torch, calls, steps, warmup):
+    """calls[r][i]: copy r, launch i.  Times `steps` steps (copy s % R at step
+    s) between two events on the launch stream, with nothing between the
+    launches.  Returns the total in ms."""
+    R = len(calls)
     for s in range(warmup):
-        for f in launchers[s % R]:
+        for f in calls[s % R]:
             f()
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nl)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    hold_gpu(torch, 20 + steps * nl * 0.05)
+    hold_gpu(torch, 20 + steps * len(calls[0]) * 0.05)
     t0.record()
     for s in range(steps):
-        row = launchers[s % R]
-        for i in range(nl):
-            if per_kernel:
-                ev[s][i][0].record()
-            row[i]()
-            if per_kernel:
-                ev[s][i][1].record()
+        for f in calls[s % R]:
+            f()
     t1.record()
     torch.cuda.synchronize()
-    total = t0.elapsed_time(t1)
-    per = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)] for i in range(nl)] if per_kernel else None
-    return total, per
+    return t0.elapsed_time(t1)
 
 
-def build_set(torch, L, layers, M, xdt, cfg_x, copies, stream):
+class LayerSet:
+    """Device copies of the layer set, activations and outputs for one M."""
+
+    def __init__(self, torch, L, B, layers, M, xdt, cfg_x, copies, stream):
+        import numpy as np
+
+        from hxq_synth import gen
+
+        self.layers = layers
+        self.by_name = {l.name: i for i, l in enumerate(layers)}
+        self.devs = [[to_dev(l, torch) for l in layers] for _ in range(copies)]
+        self.xs, self.ys = [], []
+        for i, lay in enumerate(layers):
+            xf = gen.synth_x(cfg_x, i, M, lay.K)
+            if xdt == "bf16":
+                x = torch.from_numpy(gen.to_bf16_bits(xf).view(np.int16)).cuda().view(torch.bfloat16)
+            else:
+                x = torch.from_numpy(xf).cuda()
+            self.xs.append(x)
+            self.ys.append(torch.empty((M, lay.N), dtype=torch.float32, device="cuda"))
+        self.grouped = []
+        self.single = []
+        for r in range(copies):
+            row = []
+            for g in GROUPS:
+                idx = [self.by_name[n] for n in g]
+                row.append(GroupCall(L, B, [self.devs[r][i] for i in idx], [self.ys[i] for i in idx],
+                                     self.xs[idx[0]], M, layers[idx[0]].K, stream))
+            self.grouped.append(row)
+            self.single.append([LayerCall(L, B, self.devs[r][i], self.ys[i], self.xs[i], M, l.N, l.K, stream)
+                                for i, l in enumerate(layers)])
+        xb = 2 if xdt == "bf16" else 4
+        self.group_bytes = [group_bytes([layers[self.by_name[n]] for n in g], M, xb) for g in GROUPS]
+        self.layer_bytes = [layer_bytes(l.fmt, l.N, l.K, l.nnz, M, xb) for l in layers]
+
+
+def stream_ceiling(torch, L, sets, steps):
+    """GB/s of hxq_stream_read over the gate and up index buffers of every
+    rotating copy (each launch reads one of them: the same bytes the
+    dominant launch streams, in the same rotation)."""
     import numpy as np
 
-    from hxq_synth import gen
+    bufs = []
+    for devs in sets.devs:
+        for n in GROUPS[DOMINANT]:
+            bufs.append(devs[sets.by_name[n]]["indices"])
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
 
-    launch = [[] for _ in range(copies)]
-    devs = [[to_dev(l, torch) for l in layers] for _ in range(copies)]
-    xs, ys = [], []
-    for i, lay in enumerate(layers):
-        xf = gen.synth_x(cfg_x, i, M, lay.K)
-        if xdt == "bf16":
-            x = torch.from_numpy(gen.to_bf16_bits(xf).view(np.int16)).cuda().view(torch.bfloat16)
-        else:
-            x = torch.from_numpy(xf).cuda()
-        xs.append(x)
-        ys.append(torch.empty((M, lay.N), dtype=torch.float32, device="cuda"))
-    for r in range(copies):
-        for i, lay in enumerate(layers):
-            launch[r].append(Launcher(L, lay.fmt, devs[r][i], xs[i], ys[i], M, lay.N, lay.K, stream))
-    return launch, devs, xs, ys
+    def reader(b):
+        def f():
+            st = L.hxq_stream_read(b.data_ptr(), b.numel(), sink.data_ptr(), 4096, stream)
+            if st != 0:
+                raise RuntimeError("hxq_stream_read failed with status %d" % st)
+        return f
+
+    calls = [[reader(b)] for b in bufs]
+    n = max(steps, len(bufs))
+    total = time_steps(torch, calls, n, 2)
+    avg = total / n
+    nbytes = bufs[0].numel()
+    return dict(kernel="stream_read_kernel (hxq_stream_read)", bytes_per_launch=nbytes,
+                avg_us=round(avg * 1e3, 3), gbs=round(nbytes / (avg * 1e-3) / 1e9, 1))
 
 
 def cpu_baseline(layers, M, budget_s=15.0):
     """The CPU oracle over the same layer set, as many whole steps as fit in
     about `budget_s` seconds (at least one)."""
-    import numpy as np
-
     import oracle
     from hxq_synth import gen
 
@@ -189,7 +247,7 @@ def cpu_baseline(layers, M, budget_s=15.0):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = 1
-    byts = sum(algorithmic_bytes(l.fmt, l.N, l.K, l.nnz, M, 4) for l in layers)
+    byts = sum(layer_bytes(l.fmt, l.N, l.K, l.nnz, M, 4) for l in layers)
     return dict(value=round(byts * steps / el / 1e9, 4), unit="GB/s", cores=int(cores), kind="oracle",
                 sample="%d full step(s) of the 7-layer set at M=%d (fp64 numpy oracle), %.1f s"
                        % (steps, M, el))
@@ -198,10 +256,11 @@ def cpu_baseline(layers, M, budget_s=15.0):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="only the headline step (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -215,6 +274,7 @@ def main(argv=None):
 
     import vq_compressed_linear_amd as hx
     from hxq_synth import gen
+    from vq_compressed_linear_amd import _binding as B
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -242,46 +302,79 @@ def main(argv=None):
     copies = max(1, -(-ROTATE_BYTES // set_bytes))
     log("set %.1f MB compressed, %d rotating copies" % (set_bytes / 1e6, copies))
 
-    results = {}
-    for M in (1, 8):
-        launch, devs, xs, ys = build_set(torch, L, layers, M, "f32", 1, copies, stream)
-        # pass 1: the step as it runs (no per-kernel events); pass 2: per-launch events
-        total_ms, _ = time_steps(torch, launch, args.steps, args.warmup, per_kernel=False)
-        _, per = time_steps(torch, launch, args.steps, 2, per_kernel=True)
-        byts = [algorithmic_bytes(l.fmt, l.N, l.K, l.nnz, M, 4) for l in layers]
-        step_ms = total_ms / args.steps
-        med = [float(np.median(p)) for p in per]
-        results[M] = dict(step_ms=step_ms, bytes=sum(byts), per_layer=[
-            dict(layer=l.name, N=l.N, K=l.K, bytes=b, median_us=round(m * 1e3, 3),
-                 gbs=round(b / (m * 1e-3) / 1e9, 1)) for l, b, m in zip(layers, byts, med)],
-            kernel_total_ms=sum(sum(p) for p in per), launches=args.steps * len(layers),
-            kernel_bytes=sum(byts) * args.steps)
-        log("M=%d step %.2f us, %.1f GB/s" % (M, step_ms * 1e3, sum(byts) / (step_ms * 1e-3) / 1e9))
-        del launch, devs, xs, ys
+    # ---- headline: M = 1, grouped launches
+    s1 = LayerSet(torch, L, B, layers, 1, "f32", 1, copies, stream)
+    total_ms = time_steps(torch, s1.grouped, args.steps, args.warmup)
+    step_ms = total_ms / args.steps
+    bytes_step = sum(s1.group_bytes)
+    value = bytes_step / (step_ms * 1e-3) / 1e9
+    log("M=1 grouped step %.2f us, %.1f GB/s" % (step_ms * 1e3, value))
+    # each launch type timed on its own, back to back over the rotating copies
+    # (events around the whole run, so no event sits between two launches)
+    avg = []
+    for g in range(len(GROUPS)):
+        tg = time_steps(torch, [[row[g]] for row in s1.grouped], args.steps, 2)
+        avg.append(tg / args.steps)
+    per_group = [dict(launch="|".join(g), bytes=b, avg_us=round(m * 1e3, 3),
+                      gbs=round(b / (m * 1e-3) / 1e9, 1)) for g, b, m in zip(GROUPS, s1.group_bytes, avg)]
+    dom_avg_s = avg[DOMINANT] * 1e-3
+    dom_bytes = s1.group_bytes[DOMINANT]
+    achieved = dom_bytes / dom_avg_s / 1e9
+
+    extras = {}
+    if not args.no_extras:
+        total1 = time_steps(torch, s1.single, args.steps, args.warmup)
+        avg1 = []
+        for i in range(len(layers)):
+            ti = time_steps(torch, [[row[i]] for row in s1.single], args.steps, 2)
+            avg1.append(ti / args.steps)
+        extras["per_layer_step_m1"] = dict(
+            step_us=round(total1 / args.steps * 1e3, 3),
+            gbs=round(sum(s1.layer_bytes) / (total1 / args.steps * 1e-3) / 1e9, 1),
+            layers=[dict(layer=l.name, N=l.N, K=l.K, bytes=b, avg_us=round(m * 1e3, 3),
+                         gbs=round(b / (m * 1e-3) / 1e9, 1))
+                    for l, b, m in zip(layers, s1.layer_bytes, avg1)])
+        extras["stream_ceiling"] = stream_ceiling(torch, L, s1, args.steps)
+        log("stream ceiling %.1f GB/s" % extras["stream_ceiling"]["gbs"])
+    del s1
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        s8 = LayerSet(torch, L, B, layers, 8, "f32", 1, copies, stream)
+        total8 = time_steps(torch, s8.grouped, args.steps, args.warmup)
+        avg8 = []
+        for g in range(len(GROUPS)):
+            tg = time_steps(torch, [[row[g]] for row in s8.grouped], args.steps, 2)
+            avg8.append(tg / args.steps)
+        extras["decode_m8"] = dict(
+            step_us=round(total8 / args.steps * 1e3, 3),
+            gbs=round(sum(s8.group_bytes) / (total8 / args.steps * 1e-3) / 1e9, 1),
+            launches=[dict(launch="|".join(g), avg_us=round(m * 1e3, 3)) for g, m in zip(GROUPS, avg8)])
+        log("M=8 grouped step %.2f us" % (total8 / args.steps * 1e3))
+        del s8
         torch.cuda.empty_cache()
 
-    prefill = None
-    if not args.no_prefill:
+    if not args.no_extras and not args.no_prefill:
         M = 2048
-        launch, devs, xs, ys = build_set(torch, L, layers, M, "bf16", 4, 1, stream)
-        steps = max(3, args.steps // 5)
-        total_ms, per = time_steps(torch, launch, steps, max(1, args.warmup // 5))
+        sp = LayerSet(torch, L, B, layers, M, "bf16", 4, 1, stream)
+        steps = max(3, args.steps // 10)
+        total_p = time_steps(torch, sp.single, steps, max(1, args.warmup // 5))
+        avgp = []
+        for i in range(len(layers)):
+            ti = time_steps(torch, [[row[i]] for row in sp.single], steps, 1)
+            avgp.append(ti / steps)
         flops = sum(2.0 * M * l.N * l.K for l in layers)
-        tfs = flops / (total_ms / steps * 1e-3) / 1e12
-        prefill = dict(workload="Qwen2.5-3B-shaped u8 layer set, prefill M=2048, bf16 x", M=M,
-                       step_ms=round(total_ms / steps, 4), tflops=round(tfs, 2),
-                       frac_of_mfma_peak=round(tfs / MFMA_BF16_PEAK_TFS, 4),
-                       per_layer_median_us=[round(float(np.median(p)) * 1e3, 2) for p in per])
-        log("prefill M=2048 step %.1f us, %.1f TFLOP/s" % (total_ms / steps * 1e3, tfs))
-        del launch, devs, xs, ys
+        tfs = flops / (total_p / steps * 1e-3) / 1e12
+        extras["prefill"] = dict(workload="Qwen2.5-3B-shaped u8 layer set, prefill M=2048, bf16 x", M=M,
+                                 step_us=round(total_p / steps * 1e3, 2), tflops=round(tfs, 2),
+                                 frac_of_mfma_peak=round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                                 layers=[dict(layer=l.name, avg_us=round(m * 1e3, 2),
+                                              tflops=round(2.0 * M * l.N * l.K / (m * 1e-3) / 1e12, 1))
+                                         for l, m in zip(layers, avgp)])
+        log("prefill M=2048 step %.1f us, %.1f TFLOP/s" % (total_p / steps * 1e3, tfs))
+        del sp
         torch.cuda.empty_cache()
 
-    r1 = results[1]
-    value = r1["bytes"] / (r1["step_ms"] * 1e-3) / 1e9
-    avg_launch_s = r1["kernel_total_ms"] * 1e-3 / r1["launches"]
-    avg_bytes = r1["kernel_bytes"] / r1["launches"]
-    achieved = avg_bytes / avg_launch_s / 1e9
-    traffic = load_traffic("gemv_u8_valu_m1")
     out = {
         "metric": "HelixLinear decode GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak)",
         "value": round(value, 2),
@@ -289,28 +382,26 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r1["step_ms"], 5),
+        "ms_per_step": round(step_ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded; k-means codebooks fit on N(0, 0.02^2) weights with 0.1% outliers)",
         "config": {"workload": "Qwen2.5-3B-shaped HelixLinear layer set (q,k,v,o,gate,up,down), "
-                               "u8 1D VQ + 0.1% sidecar, decode M=1, fp32 x",
-                   "M": 1, "layers": len(layers), "bytes_per_step": r1["bytes"],
-                   "rotating_copies": copies},
-        "roofline": {"bound": "hbm", "kernel": "gemv_u8_valu<MT=1,R=4>",
+                               "u8 1D VQ + 0.1% sidecar, decode M=1, fp32 x; launches q|k|v, o, gate|up, down",
+                   "M": 1, "layers": len(layers), "launches_per_step": len(GROUPS),
+                   "bytes_per_step": bytes_step, "rotating_copies": copies},
+        "roofline": {"bound": "hbm", "kernel": "decode_gemv (gate|up launch)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "avg_launch_us": round(avg_launch_s * 1e6, 3),
-                     "algorithmic_bytes_per_launch": int(avg_bytes)},
-        "decode_m8": {"step_ms": round(results[8]["step_ms"], 5),
-                      "gbs": round(results[8]["bytes"] / (results[8]["step_ms"] * 1e-3) / 1e9, 1),
-                      "per_layer": results[8]["per_layer"]},
-        "per_layer_m1": r1["per_layer"],
-        "prefill": prefill,
+                     "traffic": load_traffic("decode_gemv_gate_up_m1"),
+                     "avg_launch_us": round(dom_avg_s * 1e6, 3),
+                     "algorithmic_bytes_per_launch": int(dom_bytes)},
+        "per_launch_m1": per_group,
         "cpu_baseline": None,
     }
+    out.update(extras)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(layers, 1)

@@ -144,6 +144,19 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count,
                            const void* x, int x_dtype, int64_t M, int64_t K,
                            hipStream_t stream);
 
+/* Measurement helper, not part of the forward pass: reads `bytes` bytes of
+ * device memory at `src` once, with the decode kernels' grid shape (one
+ * 512-thread workgroup per CU, 16-byte loads, each wave a contiguous stretch),
+ * and writes one 32-bit digest of what it read per workgroup into `sink`
+ * (device memory, `sink_words` entries; the launch uses at most that many
+ * workgroups).  Its duration is the attainable read bandwidth that the decode
+ * GEMV's HBM fraction is compared against.
+ * Errors: HXQ_ERR_SHAPE if bytes < 0 or not a multiple of 16 or sink_words < 1,
+ * HXQ_ERR_NULL for a NULL pointer with bytes > 0, HXQ_ERR_ALIGN if src is not
+ * 16-byte aligned or sink not 4-byte aligned. */
+int hxq_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words,
+                    hipStream_t stream);
+
 /* Kernel selection, for tests and measurement.  HXQ_VARIANT_AUTO is what the
  * entry points above use; the others force one kernel family and return
  * HXQ_ERR_UNSUPPORTED when it cannot take the call. */

@@ -170,3 +170,15 @@ def test_grouped_rejects_call_arguments(L):
     # M == 0 and all-empty layers launch nothing
     assert f(B.HXQ_FMT_U8, good, 2, FAKE, B.HXQ_F32, 0, 16, None) == B.HXQ_OK
     assert f(B.HXQ_FMT_U8, _layers(2, N=0), 1, FAKE, B.HXQ_F32, 0, 16, None) == B.HXQ_OK
+
+
+def test_stream_read_rejects(L):
+    f = L.hxq_stream_read
+    assert f(FAKE, 15, FAKE, 4, None) == B.HXQ_ERR_SHAPE
+    assert f(FAKE, -16, FAKE, 4, None) == B.HXQ_ERR_SHAPE
+    assert f(FAKE, 16, FAKE, 0, None) == B.HXQ_ERR_SHAPE
+    assert f(None, 16, FAKE, 4, None) == B.HXQ_ERR_NULL
+    assert f(FAKE, 16, None, 4, None) == B.HXQ_ERR_NULL
+    assert f(FAKE + 4, 16, FAKE, 4, None) == B.HXQ_ERR_ALIGN
+    assert f(FAKE, 16, FAKE + 2, 4, None) == B.HXQ_ERR_ALIGN
+    assert f(None, 0, None, 4, None) == B.HXQ_OK

@@ -129,3 +129,19 @@ def test_grouped_is_deterministic():
         b = _grouped("u8", lays, ds, xd)
         for ya, yb in zip(a, b):
             assert G.torch().equal(ya, yb)
+
+
+@pytest.mark.parametrize("nbytes", [16, 1024 * 1024 + 48, 23 * 1000 * 1000 // 16 * 16])
+def test_stream_read_digest(nbytes):
+    # the measurement helper reads every byte once: XOR of the digests is the
+    # XOR of all 32-bit words
+    t = G.torch()
+    rng = np.random.Generator(np.random.PCG64(nbytes))
+    host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    src = t.from_numpy(host.view(np.int32)).cuda()
+    sink = t.zeros(1024, dtype=t.int32, device="cuda")
+    st = hx.lib().hxq_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), 1024,
+                                  t.cuda.current_stream().cuda_stream)
+    assert st == 0
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host)

@@ -76,6 +76,7 @@ SIGNATURES = {
     "hxq_linear_fwd_pk12_ex": (_INT, _FWD_ARGS + [_INT]),
     "hxq_sidecar_add": (_INT, [_P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P]),
     "hxq_linear_fwd_grouped": (_INT, [_INT, ctypes.POINTER(HxqLayer), _INT, _P, _INT, _I64, _I64, _P]),
+    "hxq_stream_read": (_INT, [_P, _I64, _P, _INT, _P]),
     "hxq_select_variant": (_INT, [_INT, _INT, _I64, _I64, _I64]),
     "hxq_status_str": (ctypes.c_char_p, [_INT]),
     "hxq_version": (_INT, []),

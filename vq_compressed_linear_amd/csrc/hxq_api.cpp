@@ -169,6 +169,15 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
   return HXQ_OK;
 }
 
+int hxq_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream) {
+  if (bytes < 0 || bytes % 16 != 0 || sink_words < 1) return HXQ_ERR_SHAPE;
+  if (bytes == 0) return HXQ_OK;
+  if (!src || !sink) return HXQ_ERR_NULL;
+  if (misaligned(src, 16) || misaligned(sink, 4)) return HXQ_ERR_ALIGN;
+  (void)hipGetLastError();
+  return status_of(hxq::launch_stream_read(src, bytes, sink, sink_words, stream));
+}
+
 int hxq_sidecar_add(const int32_t* sc_rows, const int32_t* sc_cols, const float* sc_deltas,
                     int64_t nnz, const void* x, int x_dtype, float* y, int64_t M, int64_t N,
                     int64_t K, hipStream_t stream) {

@@ -206,12 +206,11 @@ bool gemm_path_ok(const LayerArgs& a) {
 }
 
 hipError_t launch_gemm_bf16(const LayerArgs& a, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_u8_bf16),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, gemm::LDS_TOTAL);
-    attr_set = true;
-  }
+  // once per process (a function-local static is initialised exactly once,
+  // also under concurrent first calls)
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_u8_bf16),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, gemm::LDS_TOTAL);
+  if (attr != hipSuccess) return attr;
   const int tiles_m = (a.M + gemm::BM - 1) / gemm::BM;
   const int tiles_n = (a.N + gemm::BN - 1) / gemm::BN;
   const dim3 grid((unsigned)(tiles_m * tiles_n));

@@ -545,3 +545,55 @@ hipError_t launch_sidecar_add(const LayerArgs& a, hipStream_t stream) {
 }
 
 }  // namespace hxq
+
+// ------------------------------------------------------------ stream read
+// Reference for the attainable read bandwidth: reads `bytes` of `src` once,
+// 16 bytes per lane per request, each wave a contiguous stretch with eight
+// requests in flight, and folds what it read into one word per workgroup
+// (so no load can be dropped): the XOR of all sink words is the XOR of all
+// 32-bit words of the buffer.  Same grid shape as the decode kernel.
+
+namespace hxq {
+
+__global__ __launch_bounds__(512) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                           uint32_t* __restrict__ sink) {
+  constexpr int P = 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t per = (n16 + waves - 1) / waves;  // 16-byte pieces per wave
+  const int64_t b = w * per, e = b + per < n16 ? b + per : n16;
+  uint32_t acc = 0;
+  for (int64_t i0 = b; i0 < e; i0 += (int64_t)P * kWave) {
+    u32x4 v[P];
+    uint32_t keep[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int64_t i = i0 + p * kWave + lane;
+      keep[p] = i < e ? 0xffffffffu : 0u;  // a lane past the end re-reads a valid piece and drops it
+      v[p] = src[i < e ? i : (e > b ? e - 1 : 0)];
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) acc ^= (v[p].x ^ v[p].y ^ v[p].z ^ v[p].w) & keep[p];
+  }
+  // fold across the wave and the block; one word per block
+  for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, kWave);
+  __shared__ uint32_t red[8];
+  if (lane == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t ^= red[i];
+    sink[blockIdx.x] = t;
+  }
+}
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream) {
+  int grid = device_cu_count();
+  if (grid > sink_words) grid = sink_words;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(512), 0, stream,
+                     static_cast<const u32x4*>(src), bytes / 16, sink);
+  return hipGetLastError();
+}
+
+}  // namespace hxq

@@ -76,4 +76,8 @@ bool gemm_path_ok(const LayerArgs& a);
 // y += S x.
 hipError_t launch_sidecar_add(const LayerArgs& a, hipStream_t stream);
 
+// Reads `bytes` (a multiple of 16) of src once; one word per workgroup into
+// sink (at most sink_words workgroups).
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream);
+
 }  // namespace hxq
