@@ -100,6 +100,16 @@ def test_gemm_small_m_forced(M):
     _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=M, what="gemm small m")
 
 
+@pytest.mark.parametrize("N,K,nnz,M", [
+    (64, 1024, 8192, 150),    # more triplets in one tile than the patch area holds
+    (96, 33024, 3000, 130),   # more stages than the patch bins cover
+    (300, 4096, 12000, 200)])  # dense sidecar, patch path in some tiles and walk path in others
+def test_gemm_sidecar_paths(N, K, nnz, M):
+    G.say("gemm sidecar paths N=%d K=%d nnz=%d" % (N, K, nnz))
+    lay = gen.random_layer(N + K, N, K, "u8", nnz=nnz, duplicates=True)
+    _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=M, what="gemm sidecar paths")
+
+
 def test_gemm_rejects_fp32_x():
     lay = gen.random_layer(22, 64, 64, "u8")
     d = G.dev_layer(lay)
@@ -256,8 +266,18 @@ def test_constant_index_bit_exact(fmt, variant, xdt, M):
 def test_one_hot_dequant_bit_exact(fmt, variant):
     """x = e_k reads column k of the weight: y[k][n] = fp32(C[idx] + delta) on the
     fp32 paths and bf16(fp32(C[idx] + delta)) on the matrix-core path."""
-    N, K = 260, 96
-    lay = gen.random_layer(37, N, K, fmt, nnz=200)  # unique coordinates
+    _one_hot_case(fmt, variant, 260, 96, 200)
+
+
+@pytest.mark.parametrize("N,K,nnz", [(260, 128, 300), (40, 256, 6000)])
+def test_one_hot_gemm_k64(N, K, nnz):
+    """The same probe on the K % 64 == 0 matrix-core kernel: sidecar patches
+    (few triplets) and the per-row walk (more triplets than the patch area)."""
+    _one_hot_case("u8", hx.HXQ_VARIANT_GEMM_BF16, N, K, nnz)
+
+
+def _one_hot_case(fmt, variant, N, K, nnz):
+    lay = gen.random_layer(37, N, K, fmt, nnz=nnz)  # unique coordinates
     W = (oracle.dequant_u8(lay.codebook, oracle.unpack_u8(lay.indices)) if fmt == "u8" else
          oracle.dequant_pk12(lay.codebook, oracle.unpack_pk12(lay.indices, N, K), K)).astype(np.float32)
     Wf = W.copy()

@@ -78,6 +78,7 @@ int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32
       return status_of(hxq::launch_gemv_valu(a, pk12, stream));
     case HXQ_VARIANT_GEMM_BF16:
       if (!gemm_ok) return HXQ_ERR_UNSUPPORTED;
+      if (hxq::gemm2_path_ok(a)) return status_of(hxq::launch_gemm2_bf16(a, stream));
       return status_of(hxq::launch_gemm_bf16(a, stream));
     case HXQ_VARIANT_GENERIC:
       return status_of(hxq::launch_generic(a, pk12, stream));

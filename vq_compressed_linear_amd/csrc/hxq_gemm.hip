@@ -218,4 +218,434 @@ hipError_t launch_gemm_bf16(const LayerArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+
+
+// ---------------------------------------------------------------- pipelined GEMM
+//
+// The same product and rounding as above, arranged so that the matrix cores
+// are not left waiting.  With one wave per SIMD nothing hides a stall, so all
+// per-stage work sits in the same straight-line block as the MFMAs.
+//   - Workgroup tile 128 tokens x (64 * FN) outputs.  The four waves sit side
+//     by side along the outputs; each owns 16 * FN outputs for all 128 tokens
+//     (8 x FN MFMA tiles, accumulators in AGPRs).
+//   - A k-stage is 64 deep.  x reaches the MFMAs through a ring of four LDS
+//     tiles; stages go in pairs with one barrier per pair, and the x of a
+//     stage is loaded into registers two stages before it is stored.  The
+//     16-byte pieces of a tile row are XOR-swizzled by row so that the operand
+//     reads of 16 rows hit 16 different bank groups.
+//   - Each lane turns its own 16 index bytes per fragment into bf16 operands
+//     with codebook gathers from LDS, one stage ahead of the MFMAs that use
+//     them; index bytes are loaded two stages ahead.  No weight tile is
+//     written and no gather is repeated by another wave.  Lane group g
+//     (lane / 16) covers k = 16 g + 8 u + [0, 8) in MFMA sub-step u, for A and
+//     B alike, so the sum over k is unchanged.
+//   - Sidecar triplets are turned into patches before the main loop: for each
+//     distinct (row, col) of the tile, the bf16 of fp32 C[idx] + deltas
+//     (triplet order), binned by (stage, wave) in LDS.  A wave reads the
+//     patches of the next stage while its MFMAs run and overwrites the operand
+//     halves they name.  A tile with more triplets than the patch area holds,
+//     or a very long K, walks its sidecar rows from global memory instead
+//     (slower, same values).
+
+namespace gemm3 {
+constexpr int THREADS = 256, BM = 128, BK = 64, FM = BM / 16;
+constexpr int AROW = BK * 2;           // x-tile row: 64 bf16, pieces swizzled instead of padded
+constexpr int ATILE = BM * AROW;       // 16 KB
+constexpr int RING = 4;                // x tiles in LDS
+constexpr int MAXBINS = 1024;          // 4 bins per stage: K <= 16384 on the patch path
+constexpr int QMAX = 16;               // triplets per thread on the patch path
+constexpr int CAP = QMAX * THREADS;    // patches per tile
+constexpr int PRE = 8;                 // patches a wave reads ahead per stage
+constexpr int OFF_CBF = RING * ATILE;
+constexpr int OFF_BINS = OFF_CBF + 1024;
+constexpr int OFF_PATCH = OFF_BINS + (MAXBINS + 4) * 4;
+constexpr int OFF_MISC = OFF_PATCH + (CAP + PRE) * 4;
+constexpr int LDS_DYN = OFF_MISC + 64;
+static_assert(2 * 256 * 4 <= CAP * 4, "walk-path row ranges overlay the patch area");
+static_assert(CAP <= ATILE, "head flags overlay an x tile");
+}  // namespace gemm3
+
+template <int FN>
+__global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, int tiles_m) {
+  using namespace gemm3;
+  constexpr int BN = 64 * FN;
+  typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+  typedef u32x8 vecB[FN];  // operands of one stage: fragment j, words 0-3 sub-step 0, 4-7 sub-step 1
+  __shared__ __align__(16) unsigned char cbs[256 * 256];  // 64 copies per entry, bf16 in the upper half
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* cbf = reinterpret_cast<float*>(smem + OFF_CBF);
+  int* bins = reinterpret_cast<int*>(smem + OFF_BINS);  // bin b spans patch[bins[b] .. bins[b + 1])
+  uint32_t* patch = reinterpret_cast<uint32_t*>(smem + OFF_PATCH);
+  int64_t* lohi = reinterpret_cast<int64_t*>(smem + OFF_MISC);
+  int* wsum = reinterpret_cast<int*>(smem + OFF_MISC + 16);
+  unsigned char* hflag = smem + 2 * ATILE;  // head flags of the tile's triplets (prologue only)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int M = a.M, N = a.N, K = a.K;
+  const int G = gridDim.x, bx = blockIdx.x;
+  const int per = G / 8, full = per * 8;
+  const int L = (bx < full) ? (bx % 8) * per + bx / 8 : bx;  // each XCD a contiguous run of tiles
+  const int tm = L % tiles_m, tn = L / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = K / BK;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int nw = wave * 16 * FN;  // the wave's first output within the tile
+  const uint32_t lane4 = (uint32_t)lane << 2;
+
+  // ---- operand addresses
+  // x piece p = tid + 256 i: tile row p / 8, 16-byte piece p % 8
+  const unsigned char* xb = static_cast<const unsigned char*>(a.x);
+  uint32_t xoff[4];
+  int xst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + THREADS * i, r = p >> 3, c = p & 7;
+    xoff[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)(K * 2) + c * 16;
+    xst[i] = r * AROW + ((c ^ ((r >> 1) & 7)) << 4);
+  }
+  // index bytes of fragment j: output n0 + nw + 16 j + l16, k = 16 g .. 16 g + 15 of the stage
+  const uint8_t* irow[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) irow[j] = a.indices + (int64_t)min(n0 + nw + 16 * j + l16, N - 1) * K + 16 * g;
+  // A operand of tile i, sub-step u: row 16 i + l16, piece 2 g + u (the swizzle only depends on l16)
+  const int swz = (l16 >> 1) & 7;
+  const int aoff0 = l16 * AROW + (((2 * g) ^ swz) << 4);
+  const int aoff1 = l16 * AROW + (((2 * g + 1) ^ swz) << 4);
+
+  u32x4 XA[4], XB[4], IQ[FN];
+  auto load_x = [&](int st, u32x4* d) {
+    const uint32_t kx = (uint32_t)min(st, nk - 1) * (BK * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = *reinterpret_cast<const u32x4*>(xb + xoff[i] + kx);
+  };
+  auto store_x = [&](int st, const u32x4* d) {
+    unsigned char* t = smem + (st & (RING - 1)) * ATILE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(t + xst[i]) = d[i];
+  };
+  auto load_iq = [&](int st, u32x4* d) {
+    const int kn = min(st, nk - 1) * BK;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) d[j] = *reinterpret_cast<const u32x4*>(irow[j] + kn);
+  };
+  load_x(0, XA);
+  load_x(1, XB);
+  load_iq(0, IQ);
+
+  // ---- codebook: thread t stages entry t (64 bf16 copies, pieces rotated
+  // against bank conflicts) and its fp32 value
+  {
+    const float cv = static_cast<const float*>(a.codebook)[tid];
+    const float vb = __uint_as_float(f32_to_bf16_rne(cv) << 16);
+    const float4 v4 = make_float4(vb, vb, vb, vb);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) *reinterpret_cast<float4*>(cbs + tid * 256 + (((q + tid) & 15) << 4)) = v4;
+    cbf[tid] = cv;
+  }
+  // ---- sidecar: the tile's triplet range [lo, hi)
+  const int nbins = nk * 4;
+  const bool long_k = nbins > MAXBINS;
+  if (!long_k)
+    for (int i = tid; i <= nbins; i += THREADS) bins[i] = 0;
+  if (a.nnz > 0 && wave < 2) {
+    const int target = wave == 0 ? n0 : min(n0 + BN, N);
+    const int64_t guess = (int64_t)((double)a.nnz * (double)target / (double)N);
+    const int64_t v = wave_lower_bound_rows_near(a.sc_rows, a.nnz, target, guess);
+    if (lane == 0) lohi[wave] = v;
+  }
+  __syncthreads();
+  int64_t lo = 0, hi = 0;
+  if (a.nnz > 0) {
+    lo = lohi[0];
+    hi = lohi[1];
+  }
+  const int64_t cnt = hi - lo;
+  const bool walk = long_k || cnt > CAP;  // uniform
+
+  if (!walk && cnt > 0) {
+    // patches: thread t takes triplets lo + t + 256 q
+    int tr[QMAX], tc[QMAX], pr[QMAX], pc[QMAX];
+    float td[QMAX];
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+      const int64_t e = lo + tid + (int64_t)THREADS * q;
+      const int64_t ec = e < hi ? e : lo;
+      const int64_t ep = ec > lo ? ec - 1 : lo;
+      tr[q] = a.sc_rows[ec];
+      tc[q] = a.sc_cols[ec];
+      pr[q] = a.sc_rows[ep];
+      pc[q] = a.sc_cols[ep];
+      td[q] = a.sc_deltas[ec];
+    }
+    uint32_t tb[QMAX];
+    bool head[QMAX];
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+      const int64_t e = lo + tid + (int64_t)THREADS * q;
+      head[q] = e < hi && (e == lo || pr[q] != tr[q] || pc[q] != tc[q]);
+      tb[q] = a.indices[(int64_t)tr[q] * K + tc[q]];
+      if (e < hi) hflag[e - lo] = head[q] ? 1 : 0;
+      if (head[q]) atomicAdd(&bins[1 + (tc[q] / BK) * 4 + (tr[q] - n0) / (16 * FN)], 1);
+    }
+    __syncthreads();
+    // exclusive prefix over the counts in bins[1 ..]: thread t owns four of them
+    {
+      int c4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c4[i] = 4 * tid + i < nbins ? bins[1 + 4 * tid + i] : 0;
+      const int tot = c4[0] + c4[1] + c4[2] + c4[3];
+      int inc = tot;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(inc, d);
+        if (lane >= d) inc += o;
+      }
+      if (lane == 63) wsum[wave] = inc;
+      __syncthreads();
+      int base = inc - tot;
+      for (int w = 0; w < wave; ++w) base += wsum[w];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * tid + i < nbins) bins[1 + 4 * tid + i] = base;
+        base += c4[i];
+      }
+    }
+    __syncthreads();
+    // place; afterwards bins[1 + b] is the end of bin b, i.e. the start of bin b + 1
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+      if (!head[q]) continue;
+      const int64_t e = lo + tid + (int64_t)THREADS * q;
+      float v = cbf[tb[q]] + td[q];
+      for (int64_t e2 = e + 1; e2 < hi && !hflag[e2 - lo]; ++e2) v += a.sc_deltas[e2];
+      // patch word: lane (bits 0-5), column in the lane's 16 (bits 6-9), fragment (10-11), bf16 (16-31)
+      const int rl = tr[q] - n0, cl = tc[q] % BK;
+      const uint32_t w = (uint32_t)(rl % 16 + 16 * (cl / 16)) | ((uint32_t)(cl % 16) << 6) |
+                         ((uint32_t)((rl / 16) % FN) << 10) | (f32_to_bf16_rne(v) << 16);
+      patch[atomicAdd(&bins[1 + (tc[q] / BK) * 4 + rl / (16 * FN)], 1)] = w;
+    }
+  }
+  // walk path: triplet range of every tile row (overlays the patch area)
+  int* rsb = reinterpret_cast<int*>(patch);
+  int* rse = rsb + BN;
+  if (walk) {
+    for (int i = tid; i < BN; i += THREADS) rsb[i] = rse[i] = 0;
+    __syncthreads();
+    for (int64_t e = lo + tid; e < hi; e += THREADS) {
+      const int r = a.sc_rows[e];
+      if (e == lo || a.sc_rows[e - 1] != r) rsb[r - n0] = (int)(e - lo);
+      if (e == hi - 1 || a.sc_rows[e + 1] != r) rse[r - n0] = (int)(e - lo + 1);
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // operands of one stage from its index bytes: 16 gathers and 8 packs per fragment
+  auto build = [&](const u32x4* iq, vecB& out) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t wd = iq[j][d];
+        const uint32_t f0 = lds_load<uint32_t>(byte_addr256<0>(wd, lane4), cbs);
+        const uint32_t f1 = lds_load<uint32_t>(byte_addr256<1>(wd, lane4), cbs);
+        const uint32_t f2 = lds_load<uint32_t>(byte_addr256<2>(wd, lane4), cbs);
+        const uint32_t f3 = lds_load<uint32_t>(byte_addr256<3>(wd, lane4), cbs);
+        out[j][2 * d] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+        out[j][2 * d + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+      }
+  };
+  // patches: the bin of (stage st, this wave) and its first PRE words, read early
+  struct PatchPre {
+    int q0, q1;
+    uint32_t w[PRE];
+  };
+  auto patch_read = [&](int st, PatchPre& pp) {
+    const int b = min(st, nk - 1) * 4 + wave;
+    pp.q0 = bins[b];
+    pp.q1 = st < nk ? bins[b + 1] : pp.q0;
+#pragma unroll
+    for (int t = 0; t < PRE; ++t) pp.w[t] = patch[pp.q0 + t];
+  };
+  auto patch_one = [&](uint32_t ent, vecB& v) {
+    const uint32_t e = (ent >> 7) & 7u;  // uniform: the word is picked by register index
+    const uint32_t jj = (ent >> 10) & 3u;
+    const uint32_t keep = (ent & 64u) ? 0x0000ffffu : 0xffff0000u;
+    const uint32_t put = ((ent >> 16) * 0x10001u) & ~keep;
+    const bool mine = lane == (int)(ent & 63u);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const uint32_t old = v[j][e];
+      v[j][e] = (mine && jj == (uint32_t)j) ? ((old & keep) | put) : old;
+    }
+  };
+  auto patch_apply = [&](const PatchPre& pp, vecB& v) {
+    const int q0 = __builtin_amdgcn_readfirstlane(pp.q0);
+    const int n = __builtin_amdgcn_readfirstlane(pp.q1) - q0;
+    if (n <= 0) return;
+#pragma unroll
+    for (int t = 0; t < PRE; ++t)
+      if (t < n) patch_one(__builtin_amdgcn_readfirstlane(pp.w[t]), v);
+    for (int q = PRE; q < n; ++q) patch_one(__builtin_amdgcn_readfirstlane(patch[q0 + q]), v);
+  };
+  // walk path: per-lane cursors over the sidecar row of each fragment
+  int64_t scur[FN], send[FN];
+  int snc[FN];
+  auto walk_init = [&]() {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int rl = nw + 16 * j + l16;
+      scur[j] = lo + rsb[rl];
+      send[j] = lo + rse[rl];
+      snc[j] = scur[j] < send[j] ? a.sc_cols[scur[j]] : INT_MAX;
+    }
+  };
+  auto walk_stage = [&](int st, const u32x4* iq, vecB& v) {
+    if (st >= nk) return;
+    const int c0 = st * BK + 16 * g, c1 = c0 + 16;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      while (snc[j] < c1) {
+        const int c = snc[j];
+        if (c >= c0) {
+          const int p = c - c0;
+          const uint32_t word = iq[j][p >> 2];
+          float val = cbf[(word >> ((p & 3) * 8)) & 0xffu] + a.sc_deltas[scur[j]];
+          while (scur[j] + 1 < send[j] && a.sc_cols[scur[j] + 1] == c) {
+            ++scur[j];
+            val += a.sc_deltas[scur[j]];
+          }
+          const uint32_t h = f32_to_bf16_rne(val);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e == (p >> 1)) {
+              const uint32_t old = v[j][e];
+              v[j][e] = (p & 1) ? ((old & 0xffffu) | (h << 16)) : ((old & 0xffff0000u) | h);
+            }
+        }
+        ++scur[j];
+        snc[j] = scur[j] < send[j] ? a.sc_cols[scur[j]] : INT_MAX;
+      }
+    }
+  };
+
+  vecB B0, B1;
+  auto run = [&](auto walk_c) {
+    constexpr bool WALK = decltype(walk_c)::value;
+    if (WALK) walk_init();
+    // x(0), x(1) into the ring, operands of stage 0 into B0
+    store_x(0, XA);
+    store_x(1, XB);
+    load_x(2, XA);
+    load_x(3, XB);
+    build(IQ, B0);
+    if (WALK) {
+      walk_stage(0, IQ, B0);
+    } else {
+      PatchPre pp;
+      patch_read(0, pp);
+      patch_apply(pp, B0);
+    }
+    load_iq(1, IQ);
+    __syncthreads();
+
+    // stage s: x(s) in ring slot s % 4, operands of s in B[s & 1]; the index
+    // bytes of s + 1 in IQ (loaded a stage ago).  The first stage of a pair
+    // stores x(s + 2), x(s + 3) (loaded two stages ago) and loads x(s + 4),
+    // x(s + 5).
+    auto stage = [&](auto par_c, int s, bool top, bool bar) {
+      constexpr int P = decltype(par_c)::value;
+      vecB& Bc = P ? B1 : B0;
+      vecB& Bn = P ? B0 : B1;
+      const unsigned char* abuf = smem + (s & (RING - 1)) * ATILE;
+      if (top) {
+        store_x(s + 2, XA);
+        load_x(s + 4, XA);
+        store_x(s + 3, XB);
+        load_x(s + 5, XB);
+      }
+      PatchPre pp;
+      if (!WALK) patch_read(s + 1, pp);
+      build(IQ, Bn);
+      if (!WALK) load_iq(s + 2, IQ);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const bf16x8 aop = *reinterpret_cast<const bf16x8*>(abuf + (u ? aoff1 : aoff0) + i * 16 * AROW);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const u32x4 bw = u ? __builtin_shufflevector(Bc[j], Bc[j], 4, 5, 6, 7)
+                               : __builtin_shufflevector(Bc[j], Bc[j], 0, 1, 2, 3);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bw), acc[i][j], 0, 0, 0);
+          }
+        }
+      if (WALK) {
+        walk_stage(s + 1, IQ, Bn);
+        load_iq(s + 2, IQ);
+      } else {
+        patch_apply(pp, Bn);
+      }
+      if (bar) __syncthreads();
+    };
+    int s = 0;
+    for (; s + 1 < nk; s += 2) {
+      stage(std::integral_constant<int, 0>{}, s, true, false);
+      stage(std::integral_constant<int, 1>{}, s + 1, false, true);
+    }
+    if (s < nk) stage(std::integral_constant<int, 0>{}, s, true, false);
+  };
+  if (walk) run(std::true_type{});
+  else run(std::false_type{});
+
+  // ---- epilogue: lane l, register r of tile (i, j): token 16 i + 4 (l / 16) + r, output 16 j + l % 16
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = n0 + nw + 16 * j + l16;
+    if (n >= N) continue;
+    const float bn = a.bias ? a.bias[n] : 0.f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * i + 4 * g + r;
+        if (m < M) a.y[(int64_t)m * N + n] = acc[i][j][r] + bn;
+      }
+  }
+}
+
+template <int FN>
+static hipError_t launch_gemm3(const LayerArgs& a, hipStream_t stream) {
+  using namespace gemm3;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm3_u8_bf16<FN>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_DYN);
+  if (attr != hipSuccess) return attr;
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + 64 * FN - 1) / (64 * FN);
+  hipLaunchKernelGGL((gemm3_u8_bf16<FN>), dim3((unsigned)(tiles_m * tiles_n)), dim3(THREADS), LDS_DYN, stream, a,
+                     tiles_m);
+  return hipGetLastError();
+}
+
+bool gemm2_path_ok(const LayerArgs& a) {
+  if (!gemm_path_ok(a) || a.K % gemm3::BK != 0 || a.K < gemm3::BK) return false;
+  // x offsets are 32-bit
+  return (int64_t)a.M * a.K * 2 < ((int64_t)1 << 32);
+}
+
+// Output tile width by how many tiles the layer has: 256 outputs when that
+// still gives every CU a tile, else 128.
+hipError_t launch_gemm2_bf16(const LayerArgs& a, hipStream_t stream) {
+  const int64_t tiles_m = ((int64_t)a.M + gemm3::BM - 1) / gemm3::BM;
+  const int64_t wide = tiles_m * (((int64_t)a.N + 255) / 256);
+  if (wide >= device_cu_count()) return launch_gemm3<4>(a, stream);
+  return launch_gemm3<2>(a, stream);
+}
+
 }  // namespace hxq

@@ -72,6 +72,10 @@ hipError_t launch_generic(const LayerArgs& a, bool pk12, hipStream_t stream);
 // aligned index and x rows.
 hipError_t launch_gemm_bf16(const LayerArgs& a, hipStream_t stream);
 bool gemm_path_ok(const LayerArgs& a);
+// The same product with per-wave weight operands built in registers; needs
+// K % 64 == 0 as well.
+hipError_t launch_gemm2_bf16(const LayerArgs& a, hipStream_t stream);
+bool gemm2_path_ok(const LayerArgs& a);
 
 // y += S x.
 hipError_t launch_sidecar_add(const LayerArgs& a, hipStream_t stream);
