@@ -223,16 +223,16 @@ hipError_t launch_gemm_bf16(const LayerArgs& a, hipStream_t stream) {
 // ---------------------------------------------------------------- pipelined GEMM
 //
 // The same product and rounding as above, arranged so that the matrix cores
-// are not left waiting.  With one wave per SIMD nothing hides a stall, so all
-// per-stage work sits in the same straight-line block as the MFMAs.
-//   - Workgroup tile 128 tokens x (64 * FN) outputs.  The four waves sit side
-//     by side along the outputs; each owns 16 * FN outputs for all 128 tokens
-//     (8 x FN MFMA tiles, accumulators in AGPRs).
+// are not left waiting.
+//   - Workgroup tile 128 tokens x (128 * FN) outputs.  Eight waves (two per
+//     SIMD, so one can issue while the other waits) sit side by side along the
+//     outputs; each owns 16 * FN outputs for all 128 tokens (8 x FN MFMA
+//     tiles, accumulators in AGPRs).
 //   - A k-stage is 64 deep.  x reaches the MFMAs through a ring of four LDS
 //     tiles; stages go in pairs with one barrier per pair, and the x of a
 //     stage is loaded into registers two stages before it is stored.  The
 //     16-byte pieces of a tile row are XOR-swizzled by row so that the operand
-//     reads of 16 rows hit 16 different bank groups.
+//     reads of 16 rows spread over the banks.
 //   - Each lane turns its own 16 index bytes per fragment into bf16 operands
 //     with codebook gathers from LDS, one stage ahead of the MFMAs that use
 //     them; index bytes are loaded two stages ahead.  No weight tile is
@@ -248,27 +248,30 @@ hipError_t launch_gemm_bf16(const LayerArgs& a, hipStream_t stream) {
 //     (slower, same values).
 
 namespace gemm3 {
-constexpr int THREADS = 256, BM = 128, BK = 64, FM = BM / 16;
+constexpr int THREADS = 512, WAVES = THREADS / 64, BM = 128, BK = 64, FM = BM / 16;
 constexpr int AROW = BK * 2;           // x-tile row: 64 bf16, pieces swizzled instead of padded
 constexpr int ATILE = BM * AROW;       // 16 KB
 constexpr int RING = 4;                // x tiles in LDS
-constexpr int MAXBINS = 1024;          // 4 bins per stage: K <= 16384 on the patch path
-constexpr int QMAX = 16;               // triplets per thread on the patch path
+constexpr int MAXBINS = 2048;          // 8 bins per stage: K <= 16384 on the patch path
+constexpr int QMAX = 8;                // triplets per thread on the patch path
 constexpr int CAP = QMAX * THREADS;    // patches per tile
 constexpr int PRE = 8;                 // patches a wave reads ahead per stage
 constexpr int OFF_CBF = RING * ATILE;
 constexpr int OFF_BINS = OFF_CBF + 1024;
 constexpr int OFF_PATCH = OFF_BINS + (MAXBINS + 4) * 4;
+constexpr int XPT = ATILE / 16 / THREADS;  // 16-byte x pieces per thread per stage
+static_assert(XPT * THREADS * 16 == ATILE, "the x stores cover the tile");
 constexpr int OFF_MISC = OFF_PATCH + (CAP + PRE) * 4;
 constexpr int LDS_DYN = OFF_MISC + 64;
 static_assert(2 * 256 * 4 <= CAP * 4, "walk-path row ranges overlay the patch area");
+static_assert(MAXBINS % THREADS == 0, "bin prefix: whole bins per thread");
 static_assert(CAP <= ATILE, "head flags overlay an x tile");
 }  // namespace gemm3
 
 template <int FN>
 __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, int tiles_m) {
   using namespace gemm3;
-  constexpr int BN = 64 * FN;
+  constexpr int BN = 16 * WAVES * FN;
   typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
   typedef u32x8 vecB[FN];  // operands of one stage: fragment j, words 0-3 sub-step 0, 4-7 sub-step 1
   __shared__ __align__(16) unsigned char cbs[256 * 256];  // 64 copies per entry, bf16 in the upper half
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
   int* bins = reinterpret_cast<int*>(smem + OFF_BINS);  // bin b spans patch[bins[b] .. bins[b + 1])
   uint32_t* patch = reinterpret_cast<uint32_t*>(smem + OFF_PATCH);
   int64_t* lohi = reinterpret_cast<int64_t*>(smem + OFF_MISC);
-  int* wsum = reinterpret_cast<int*>(smem + OFF_MISC + 16);
+  int* wsum = reinterpret_cast<int*>(smem + OFF_MISC + 16);  // one per wave
   unsigned char* hflag = smem + 2 * ATILE;  // head flags of the tile's triplets (prologue only)
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -294,12 +297,12 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
   const uint32_t lane4 = (uint32_t)lane << 2;
 
   // ---- operand addresses
-  // x piece p = tid + 256 i: tile row p / 8, 16-byte piece p % 8
+  // x piece p = tid + 512 i: tile row p / 8, 16-byte piece p % 8
   const unsigned char* xb = static_cast<const unsigned char*>(a.x);
-  uint32_t xoff[4];
-  int xst[4];
+  uint32_t xoff[XPT];
+  int xst[XPT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < XPT; ++i) {
     const int p = tid + THREADS * i, r = p >> 3, c = p & 7;
     xoff[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)(K * 2) + c * 16;
     xst[i] = r * AROW + ((c ^ ((r >> 1) & 7)) << 4);
@@ -313,16 +316,16 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
   const int aoff0 = l16 * AROW + (((2 * g) ^ swz) << 4);
   const int aoff1 = l16 * AROW + (((2 * g + 1) ^ swz) << 4);
 
-  u32x4 XA[4], XB[4], IQ[FN];
+  u32x4 XA[XPT], XB[XPT], IQ[FN];
   auto load_x = [&](int st, u32x4* d) {
     const uint32_t kx = (uint32_t)min(st, nk - 1) * (BK * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = *reinterpret_cast<const u32x4*>(xb + xoff[i] + kx);
+    for (int i = 0; i < XPT; ++i) d[i] = *reinterpret_cast<const u32x4*>(xb + xoff[i] + kx);
   };
   auto store_x = [&](int st, const u32x4* d) {
     unsigned char* t = smem + (st & (RING - 1)) * ATILE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(t + xst[i]) = d[i];
+    for (int i = 0; i < XPT; ++i) *reinterpret_cast<u32x4*>(t + xst[i]) = d[i];
   };
   auto load_iq = [&](int st, u32x4* d) {
     const int kn = min(st, nk - 1) * BK;
@@ -333,18 +336,19 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
   load_x(1, XB);
   load_iq(0, IQ);
 
-  // ---- codebook: thread t stages entry t (64 bf16 copies, pieces rotated
-  // against bank conflicts) and its fp32 value
+  // ---- codebook: threads t and t + 256 stage half of entry t's 64 bf16
+  // copies each (pieces rotated against bank conflicts); fp32 values too
   {
-    const float cv = static_cast<const float*>(a.codebook)[tid];
+    const int e = tid & 255, h = tid >> 8;
+    const float cv = static_cast<const float*>(a.codebook)[e];
     const float vb = __uint_as_float(f32_to_bf16_rne(cv) << 16);
     const float4 v4 = make_float4(vb, vb, vb, vb);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) *reinterpret_cast<float4*>(cbs + tid * 256 + (((q + tid) & 15) << 4)) = v4;
-    cbf[tid] = cv;
+    for (int q = 0; q < 8; ++q) *reinterpret_cast<float4*>(cbs + e * 256 + (((8 * h + q + e) & 15) << 4)) = v4;
+    if (h == 0) cbf[e] = cv;
   }
   // ---- sidecar: the tile's triplet range [lo, hi)
-  const int nbins = nk * 4;
+  const int nbins = nk * WAVES;
   const bool long_k = nbins > MAXBINS;
   if (!long_k)
     for (int i = tid; i <= nbins; i += THREADS) bins[i] = 0;
@@ -386,15 +390,19 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
       head[q] = e < hi && (e == lo || pr[q] != tr[q] || pc[q] != tc[q]);
       tb[q] = a.indices[(int64_t)tr[q] * K + tc[q]];
       if (e < hi) hflag[e - lo] = head[q] ? 1 : 0;
-      if (head[q]) atomicAdd(&bins[1 + (tc[q] / BK) * 4 + (tr[q] - n0) / (16 * FN)], 1);
+      if (head[q]) atomicAdd(&bins[1 + (tc[q] / BK) * WAVES + (tr[q] - n0) / (16 * FN)], 1);
     }
     __syncthreads();
-    // exclusive prefix over the counts in bins[1 ..]: thread t owns four of them
+    // exclusive prefix over the counts in bins[1 ..]: thread t owns PT of them
     {
-      int c4[4];
+      constexpr int PT = MAXBINS / THREADS;
+      int c4[PT];
+      int tot = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) c4[i] = 4 * tid + i < nbins ? bins[1 + 4 * tid + i] : 0;
-      const int tot = c4[0] + c4[1] + c4[2] + c4[3];
+      for (int i = 0; i < PT; ++i) {
+        c4[i] = PT * tid + i < nbins ? bins[1 + PT * tid + i] : 0;
+        tot += c4[i];
+      }
       int inc = tot;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -406,8 +414,8 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
       int base = inc - tot;
       for (int w = 0; w < wave; ++w) base += wsum[w];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (4 * tid + i < nbins) bins[1 + 4 * tid + i] = base;
+      for (int i = 0; i < PT; ++i) {
+        if (PT * tid + i < nbins) bins[1 + PT * tid + i] = base;
         base += c4[i];
       }
     }
@@ -423,7 +431,7 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
       const int rl = tr[q] - n0, cl = tc[q] % BK;
       const uint32_t w = (uint32_t)(rl % 16 + 16 * (cl / 16)) | ((uint32_t)(cl % 16) << 6) |
                          ((uint32_t)((rl / 16) % FN) << 10) | (f32_to_bf16_rne(v) << 16);
-      patch[atomicAdd(&bins[1 + (tc[q] / BK) * 4 + rl / (16 * FN)], 1)] = w;
+      patch[atomicAdd(&bins[1 + (tc[q] / BK) * WAVES + rl / (16 * FN)], 1)] = w;
     }
   }
   // walk path: triplet range of every tile row (overlays the patch area)
@@ -467,7 +475,7 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
     uint32_t w[PRE];
   };
   auto patch_read = [&](int st, PatchPre& pp) {
-    const int b = min(st, nk - 1) * 4 + wave;
+    const int b = min(st, nk - 1) * WAVES + wave;
     pp.q0 = bins[b];
     pp.q1 = st < nk ? bins[b + 1] : pp.q0;
 #pragma unroll
@@ -583,7 +591,9 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
           for (int j = 0; j < FN; ++j) {
             const u32x4 bw = u ? __builtin_shufflevector(Bc[j], Bc[j], 4, 5, 6, 7)
                                : __builtin_shufflevector(Bc[j], Bc[j], 0, 1, 2, 3);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bw), acc[i][j], 0, 0, 0);
+            // weights as the A operand, x as B: the result tile is y transposed,
+            // so each lane ends up with four consecutive outputs of one token
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bw), aop, acc[i][j], 0, 0, 0);
           }
         }
       if (WALK) {
@@ -604,19 +614,35 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
   if (walk) run(std::true_type{});
   else run(std::false_type{});
 
-  // ---- epilogue: lane l, register r of tile (i, j): token 16 i + 4 (l / 16) + r, output 16 j + l % 16
+  // ---- epilogue: lane l, register r of tile (i, j): output 16 j + 4 (l / 16) + r, token 16 i + l % 16
+  const bool vec_ok = (N & 3) == 0;
+  const bool bias_vec = vec_ok && a.bias && (reinterpret_cast<uintptr_t>(a.bias) & 15) == 0;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int n = n0 + nw + 16 * j + l16;
+    const int n = n0 + nw + 16 * j + 4 * g;
     if (n >= N) continue;
-    const float bn = a.bias ? a.bias[n] : 0.f;
+    float bv[4];
+    if (bias_vec) {
+      const float4 b4 = *reinterpret_cast<const float4*>(a.bias + n);
+      bv[0] = b4.x, bv[1] = b4.y, bv[2] = b4.z, bv[3] = b4.w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int r = 0; r < 4; ++r) bv[r] = (a.bias && n + r < N) ? a.bias[n + r] : 0.f;
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 16 * i + 4 * g + r;
-        if (m < M) a.y[(int64_t)m * N + n] = acc[i][j][r] + bn;
+    for (int i = 0; i < FM; ++i) {
+      const int m = m0 + 16 * i + l16;
+      if (m >= M) continue;
+      float* yp = a.y + (int64_t)m * N + n;
+      if (vec_ok) {
+        *reinterpret_cast<float4*>(yp) =
+            make_float4(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1], acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) yp[r] = acc[i][j][r] + bv[r];
       }
+    }
   }
 }
 
@@ -627,7 +653,7 @@ static hipError_t launch_gemm3(const LayerArgs& a, hipStream_t stream) {
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS_DYN);
   if (attr != hipSuccess) return attr;
   const int tiles_m = (a.M + BM - 1) / BM;
-  const int tiles_n = (a.N + 64 * FN - 1) / (64 * FN);
+  const int tiles_n = (a.N + 16 * WAVES * FN - 1) / (16 * WAVES * FN);
   hipLaunchKernelGGL((gemm3_u8_bf16<FN>), dim3((unsigned)(tiles_m * tiles_n)), dim3(THREADS), LDS_DYN, stream, a,
                      tiles_m);
   return hipGetLastError();
@@ -644,8 +670,8 @@ bool gemm2_path_ok(const LayerArgs& a) {
 hipError_t launch_gemm2_bf16(const LayerArgs& a, hipStream_t stream) {
   const int64_t tiles_m = ((int64_t)a.M + gemm3::BM - 1) / gemm3::BM;
   const int64_t wide = tiles_m * (((int64_t)a.N + 255) / 256);
-  if (wide >= device_cu_count()) return launch_gemm3<4>(a, stream);
-  return launch_gemm3<2>(a, stream);
+  if (wide >= device_cu_count()) return launch_gemm3<2>(a, stream);
+  return launch_gemm3<1>(a, stream);
 }
 
 }  // namespace hxq
