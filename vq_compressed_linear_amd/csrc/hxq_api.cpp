@@ -139,7 +139,7 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
   // one launch when every non-empty layer fits the decode kernel
   hxq::DecodeSeg segs[hxq::kMaxSegments];
   int nseg = 0;
-  bool fast = K > 0 && M <= 4;
+  bool fast = K > 0 && M <= hxq::kChunkMaxM;
   for (int i = 0; i < count && fast; ++i) {
     const hxq_layer& l = layers[i];
     if (l.N == 0) continue;
@@ -155,11 +155,14 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
     segs[nseg++] = {l.codebook, l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz, l.bias, l.y, (int)l.N, 0, 0, 0.f};
   }
   if (fast && nseg == 0) return HXQ_OK;
-  if (fast && hxq::decode_fits(segs, nseg, pk12, x_dtype == HXQ_BF16, (int)M, (int)K)) {
+  if (fast) {
     (void)hipGetLastError();
     hipError_t err = hipSuccess;
-    if (hxq::launch_decode(segs, nseg, pk12, x, x_dtype == HXQ_BF16, (int)M, (int)K, stream, err))
-      return status_of(err);
+    const bool xbf = x_dtype == HXQ_BF16;
+    const bool done = M <= 4 ? hxq::decode_fits(segs, nseg, pk12, xbf, (int)M, (int)K) &&
+                                   hxq::launch_decode(segs, nseg, pk12, x, xbf, (int)M, (int)K, stream, err)
+                             : hxq::launch_decode_chunked(segs, nseg, pk12, x, xbf, (int)M, (int)K, stream, err);
+    if (done) return status_of(err);
   }
   for (int i = 0; i < count; ++i) {
     const hxq_layer& l = layers[i];
