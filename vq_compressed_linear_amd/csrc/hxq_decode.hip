@@ -700,15 +700,22 @@ bool decode_fits(const DecodeSeg* segs, int nseg, bool pk12, bool xbf, int M, in
   return plan(segs, nseg, pk12, xbf, M, K, 256, a, p);
 }
 
-// More tokens than one pass takes: consecutive groups of at most four rows.
-// Rows m0 .. m0 + 3 of x and of every y are contiguous, so a group is the
-// same call on x + m0 K and y + m0 N; each group streams the indices again.
+// More tokens than one pass takes: consecutive groups of G rows, G the
+// largest of 4, 2, 1 whose group (and remainder) fits the kernel.  Rows
+// m0 .. m0 + G - 1 of x and of every y are contiguous, so a group is the same
+// call on x + m0 K and y + m0 N; each group streams the indices again.
 bool launch_decode_chunked(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
                            hipStream_t stream, hipError_t& err) {
-  constexpr int G = 4;
-  if (nseg < 1 || nseg > kMaxSegments) return false;
-  if (!decode_fits(segs, nseg, pk12, xbf, M < G ? M : G, K)) return false;
-  if (M % G != 0 && !decode_fits(segs, nseg, pk12, xbf, M % G, K)) return false;
+  if (nseg < 1 || nseg > kMaxSegments || M < 1) return false;
+  int G = 0;
+  for (int c : {4, 2, 1}) {
+    const int g = M < c ? M : c;
+    if (decode_fits(segs, nseg, pk12, xbf, g, K) && (M % g == 0 || decode_fits(segs, nseg, pk12, xbf, M % g, K))) {
+      G = g;
+      break;
+    }
+  }
+  if (G == 0) return false;
   const size_t xrow = (size_t)K * (xbf ? 2 : 4);
   for (int m0 = 0; m0 < M; m0 += G) {
     const int mc = M - m0 < G ? M - m0 : G;

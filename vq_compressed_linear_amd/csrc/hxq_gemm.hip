@@ -230,9 +230,13 @@ hipError_t launch_gemm_bf16(const LayerArgs& a, hipStream_t stream) {
 //     tiles, accumulators in AGPRs).
 //   - A k-stage is 64 deep.  x reaches the MFMAs through a ring of four LDS
 //     tiles; stages go in pairs with one barrier per pair, and the x of a
-//     stage is loaded into registers two stages before it is stored.  The
-//     16-byte pieces of a tile row are XOR-swizzled by row so that the operand
-//     reads of 16 rows spread over the banks.
+//     stage is loaded into registers two stages before it is stored.  A tile
+//     is kept in operand order: 1 KB block (i, u) holds the 16 bytes lane
+//     (g, l16) reads for token block i and sub-step u at position
+//     16 g + (l16 ^ (2 g + u)), so every eight lanes of an operand read cover
+//     one 128-byte segment (128-bit reads of rows 128 bytes apart run at half
+//     rate), while the eight pieces a row's global load brings land in eight
+//     different bank groups.
 //   - Each lane turns its own 16 index bytes per fragment into bf16 operands
 //     with codebook gathers from LDS, one stage ahead of the MFMAs that use
 //     them; index bytes are loaded two stages ahead.  No weight tile is
@@ -249,8 +253,7 @@ hipError_t launch_gemm_bf16(const LayerArgs& a, hipStream_t stream) {
 
 namespace gemm3 {
 constexpr int THREADS = 512, WAVES = THREADS / 64, BM = 128, BK = 64, FM = BM / 16;
-constexpr int AROW = BK * 2;           // x-tile row: 64 bf16, pieces swizzled instead of padded
-constexpr int ATILE = BM * AROW;       // 16 KB
+constexpr int ATILE = BM * BK * 2;     // 16 KB: 16 operand blocks of 1 KB
 constexpr int RING = 4;                // x tiles in LDS
 constexpr int MAXBINS = 2048;          // 8 bins per stage: K <= 16384 on the patch path
 constexpr int QMAX = 8;                // triplets per thread on the patch path
@@ -297,7 +300,8 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
   const uint32_t lane4 = (uint32_t)lane << 2;
 
   // ---- operand addresses
-  // x piece p = tid + 512 i: tile row p / 8, 16-byte piece p % 8
+  // x piece p = tid + 512 i: tile row r = p / 8, 16-byte piece c = p % 8, stored at
+  // block (r / 16, c % 2), position 16 (c / 2) + ((r % 16) ^ c)
   const unsigned char* xb = static_cast<const unsigned char*>(a.x);
   uint32_t xoff[XPT];
   int xst[XPT];
@@ -305,16 +309,14 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
   for (int i = 0; i < XPT; ++i) {
     const int p = tid + THREADS * i, r = p >> 3, c = p & 7;
     xoff[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)(K * 2) + c * 16;
-    xst[i] = r * AROW + ((c ^ ((r >> 1) & 7)) << 4);
+    xst[i] = ((r >> 4) * 2 + (c & 1)) * 1024 + (((c >> 1) * 16 + ((r & 15) ^ c)) << 4);
   }
   // index bytes of fragment j: output n0 + nw + 16 j + l16, k = 16 g .. 16 g + 15 of the stage
   const uint8_t* irow[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) irow[j] = a.indices + (int64_t)min(n0 + nw + 16 * j + l16, N - 1) * K + 16 * g;
-  // A operand of tile i, sub-step u: row 16 i + l16, piece 2 g + u (the swizzle only depends on l16)
-  const int swz = (l16 >> 1) & 7;
-  const int aoff0 = l16 * AROW + (((2 * g) ^ swz) << 4);
-  const int aoff1 = l16 * AROW + (((2 * g + 1) ^ swz) << 4);
+  // A operand of token block i, sub-step u: block 2 i + u
+  const int aoff0 = (g * 16 + (l16 ^ (2 * g))) * 16, aoff1 = 1024 + (g * 16 + (l16 ^ (2 * g + 1))) * 16;
 
   u32x4 XA[XPT], XB[XPT], IQ[FN];
   auto load_x = [&](int st, u32x4* d) {
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const bf16x8 aop = *reinterpret_cast<const bf16x8*>(abuf + (u ? aoff1 : aoff0) + i * 16 * AROW);
+          const bf16x8 aop = *reinterpret_cast<const bf16x8*>(abuf + (u ? aoff1 : aoff0) + i * 2048);
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const u32x4 bw = u ? __builtin_shufflevector(Bc[j], Bc[j], 4, 5, 6, 7)

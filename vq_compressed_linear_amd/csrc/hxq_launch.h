@@ -64,7 +64,7 @@ struct DecodeArgs {
 bool launch_decode(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
                    hipStream_t stream, hipError_t& err);
 bool decode_fits(const DecodeSeg* segs, int nseg, bool pk12, bool xbf, int M, int K);
-// M up to kChunkMaxM through the decode kernel in groups of four tokens
+// M up to kChunkMaxM through the decode kernel in groups of up to four tokens
 // (indices streamed once per group); false when it does not fit.
 constexpr int kChunkMaxM = 16;
 bool launch_decode_chunked(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
