@@ -358,19 +358,29 @@ def main(argv=None):
         M = 2048
         sp = LayerSet(torch, L, B, layers, M, "bf16", 4, 1, stream)
         steps = max(3, args.steps // 10)
-        total_p = time_steps(torch, sp.single, steps, max(1, args.warmup // 5))
+        # the step as launches that share x (q|k|v, o, gate|up, down), like the decode step
+        total_p = time_steps(torch, sp.grouped, steps, max(1, args.warmup // 5))
+        avg_g = []
+        for g in range(len(GROUPS)):
+            tg = time_steps(torch, [[row[g]] for row in sp.grouped], steps, 1)
+            avg_g.append(tg / steps)
         avgp = []
         for i in range(len(layers)):
             ti = time_steps(torch, [[row[i]] for row in sp.single], steps, 1)
             avgp.append(ti / steps)
         flops = sum(2.0 * M * l.N * l.K for l in layers)
         tfs = flops / (total_p / steps * 1e-3) / 1e12
-        extras["prefill"] = dict(workload="Qwen2.5-3B-shaped u8 layer set, prefill M=2048, bf16 x", M=M,
+        gfl = [sum(2.0 * M * layers[sp.by_name[n]].N * layers[sp.by_name[n]].K for n in g) for g in GROUPS]
+        extras["prefill"] = dict(workload="Qwen2.5-3B-shaped u8 layer set, prefill M=2048, bf16 x; launches "
+                                          "q|k|v, o, gate|up, down", M=M,
                                  step_us=round(total_p / steps * 1e3, 2), tflops=round(tfs, 2),
                                  frac_of_mfma_peak=round(tfs / MFMA_BF16_PEAK_TFS, 4),
-                                 layers=[dict(layer=l.name, avg_us=round(m * 1e3, 2),
-                                              tflops=round(2.0 * M * l.N * l.K / (m * 1e-3) / 1e12, 1))
-                                         for l, m in zip(layers, avgp)])
+                                 launches=[dict(launch="|".join(g), avg_us=round(m * 1e3, 2),
+                                                tflops=round(f / (m * 1e-3) / 1e12, 1))
+                                           for g, m, f in zip(GROUPS, avg_g, gfl)],
+                                 single_layer_calls=[dict(layer=l.name, avg_us=round(m * 1e3, 2),
+                                                          tflops=round(2.0 * M * l.N * l.K / (m * 1e-3) / 1e12, 1))
+                                                     for l, m in zip(layers, avgp)])
         log("prefill M=2048 step %.1f us, %.1f TFLOP/s" % (total_p / steps * 1e3, tfs))
         del sp
         torch.cuda.empty_cache()

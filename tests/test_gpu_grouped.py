@@ -63,6 +63,21 @@ def test_grouped_matches_oracle_and_single_calls(fmt, x_dtype, M):
         assert G.torch().equal(y, y1), "grouped and single-layer results differ bitwise"
 
 
+@pytest.mark.parametrize("M,K", [(17, 2048), (130, 2048), (300, 1024), (130, 96)])
+def test_grouped_prefill_gemm(M, K):
+    # bf16 x past the decode sizes: one matrix-core launch over all layers
+    # (K % 64 == 0), else one call per layer; both equal single-layer calls bitwise
+    G.say("grouped gemm M=%d K=%d" % (M, K))
+    lays, ds = _group("u8", [1000, 96, 2500], K, seed=M + K)
+    x_np = _x(M + 1, M, K, "bf16")
+    xd = G.dev_x(x_np, "bf16")
+    ys = _grouped("u8", lays, ds, xd)
+    for lay, d, y in zip(lays, ds, ys):
+        Y, B = G.oracle_fwd(lay, x_np, "bf16")
+        G.check(y, Y, B, G.TOL_BF16, "grouped gemm N=%d" % lay.N)
+        assert G.torch().equal(y, G.run(lay, d, xd)), "grouped and single-layer results differ bitwise"
+
+
 @pytest.mark.parametrize("fmt,K", [("u8", 11008), ("pk12", 11008), ("u8", 16), ("u8", 4096 + 16)])
 @pytest.mark.parametrize("M", [1, 2, 4])
 def test_decode_k_range(fmt, K, M):

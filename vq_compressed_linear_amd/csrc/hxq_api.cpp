@@ -164,6 +164,33 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
                              : hxq::launch_decode_chunked(segs, nseg, pk12, x, xbf, (int)M, (int)K, stream, err);
     if (done) return status_of(err);
   }
+  // one matrix-core launch for bf16 x past the decode sizes when every layer takes it
+  if (!pk12 && x_dtype == HXQ_BF16 && M > 16 && K > 0) {
+    hxq::GemmSeg gs[hxq::kMaxSegments];
+    int ng = 0;
+    bool ok = true;
+    for (int i = 0; i < count && ok; ++i) {
+      const hxq_layer& l = layers[i];
+      if (l.N == 0) continue;
+      hxq::LayerArgs a = {};
+      a.codebook = l.codebook;
+      a.indices = l.indices;
+      a.x = x;
+      a.x_bf16 = true;
+      a.y = l.y;
+      a.M = (int)M;
+      a.N = (int)l.N;
+      a.K = (int)K;
+      ok = hxq::gemm2_path_ok(a);
+      gs[ng++] = {static_cast<const float*>(l.codebook), l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz,
+                  l.bias, l.y, (int)l.N, 0};
+    }
+    if (ok && ng == 0) return HXQ_OK;
+    if (ok) {
+      (void)hipGetLastError();
+      return status_of(hxq::launch_gemm_grouped(gs, ng, x, (int)M, (int)K, stream));
+    }
+  }
   for (int i = 0; i < count; ++i) {
     const hxq_layer& l = layers[i];
     const int st = forward(pk12, l.codebook, l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz, x, x_dtype,

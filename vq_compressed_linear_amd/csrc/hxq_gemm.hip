@@ -272,7 +272,7 @@ static_assert(CAP <= ATILE, "head flags overlay an x tile");
 }  // namespace gemm3
 
 template <int FN>
-__global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, int tiles_m) {
+__global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(GemmArgs ga) {
   using namespace gemm3;
   constexpr int BN = 16 * WAVES * FN;
   typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
@@ -288,11 +288,32 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int M = a.M, N = a.N, K = a.K;
   const int G = gridDim.x, bx = blockIdx.x;
   const int per = G / 8, full = per * 8;
   const int L = (bx < full) ? (bx % 8) * per + bx / 8 : bx;  // each XCD a contiguous run of tiles
-  const int tm = L % tiles_m, tn = L / tiles_m;
+  // the layer this tile belongs to: segments own consecutive tile ranges
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSegments; ++i)
+    if (i < ga.nseg && L >= ga.seg[i].tile0) si = i;
+  const GemmSeg& sg = ga.seg[si];
+  LayerArgs a;
+  a.codebook = sg.codebook;
+  a.indices = sg.indices;
+  a.sc_rows = sg.sc_rows;
+  a.sc_cols = sg.sc_cols;
+  a.sc_deltas = sg.sc_deltas;
+  a.nnz = sg.nnz;
+  a.x = ga.x;
+  a.x_bf16 = true;
+  a.bias = sg.bias;
+  a.y = sg.y;
+  a.M = ga.M;
+  a.N = sg.N;
+  a.K = ga.K;
+  const int M = a.M, N = a.N, K = a.K;
+  const int tiles_m = ga.tiles_m;
+  const int tm = (L - sg.tile0) % tiles_m, tn = (L - sg.tile0) / tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
   const int nk = K / BK;
   const int g = lane >> 4, l16 = lane & 15;
@@ -649,15 +670,18 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(LayerArgs a, 
 }
 
 template <int FN>
-static hipError_t launch_gemm3(const LayerArgs& a, hipStream_t stream) {
+static hipError_t launch_gemm3(GemmArgs& ga, hipStream_t stream) {
   using namespace gemm3;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm3_u8_bf16<FN>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS_DYN);
   if (attr != hipSuccess) return attr;
-  const int tiles_m = (a.M + BM - 1) / BM;
-  const int tiles_n = (a.N + 16 * WAVES * FN - 1) / (16 * WAVES * FN);
-  hipLaunchKernelGGL((gemm3_u8_bf16<FN>), dim3((unsigned)(tiles_m * tiles_n)), dim3(THREADS), LDS_DYN, stream, a,
-                     tiles_m);
+  int64_t tiles = 0;
+  for (int i = 0; i < ga.nseg; ++i) {
+    ga.seg[i].tile0 = (int)tiles;
+    tiles += (int64_t)ga.tiles_m * ((ga.seg[i].N + 16 * WAVES * FN - 1) / (16 * WAVES * FN));
+    if (tiles > INT_MAX) return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((gemm3_u8_bf16<FN>), dim3((unsigned)tiles), dim3(THREADS), LDS_DYN, stream, ga);
   return hipGetLastError();
 }
 
@@ -667,13 +691,30 @@ bool gemm2_path_ok(const LayerArgs& a) {
   return (int64_t)a.M * a.K * 2 < ((int64_t)1 << 32);
 }
 
-// Output tile width by how many tiles the layer has: 256 outputs when that
+// Output tile width by how many tiles the launch has: 256 outputs when that
 // still gives every CU a tile, else 128.
+hipError_t launch_gemm_grouped(const GemmSeg* segs, int nseg, const void* x, int M, int K, hipStream_t stream) {
+  if (nseg < 1 || nseg > kMaxSegments) return hipErrorInvalidValue;
+  GemmArgs ga;
+  ga.x = x;
+  ga.M = M;
+  ga.K = K;
+  ga.tiles_m = (M + gemm3::BM - 1) / gemm3::BM;
+  ga.nseg = nseg;
+  int64_t wide = 0;
+  for (int i = 0; i < nseg; ++i) {
+    ga.seg[i] = segs[i];
+    wide += (int64_t)ga.tiles_m * ((segs[i].N + 255) / 256);
+  }
+  for (int i = nseg; i < kMaxSegments; ++i) ga.seg[i] = segs[0];
+  if (wide >= device_cu_count()) return launch_gemm3<2>(ga, stream);
+  return launch_gemm3<1>(ga, stream);
+}
+
 hipError_t launch_gemm2_bf16(const LayerArgs& a, hipStream_t stream) {
-  const int64_t tiles_m = ((int64_t)a.M + gemm3::BM - 1) / gemm3::BM;
-  const int64_t wide = tiles_m * (((int64_t)a.N + 255) / 256);
-  if (wide >= device_cu_count()) return launch_gemm3<2>(a, stream);
-  return launch_gemm3<1>(a, stream);
+  const GemmSeg sg = {static_cast<const float*>(a.codebook), a.indices, a.sc_rows, a.sc_cols, a.sc_deltas,
+                      a.nnz, a.bias, a.y, a.N, 0};
+  return launch_gemm_grouped(&sg, 1, a.x, a.M, a.K, stream);
 }
 
 }  // namespace hxq

@@ -82,6 +82,29 @@ bool gemm_path_ok(const LayerArgs& a);
 hipError_t launch_gemm2_bf16(const LayerArgs& a, hipStream_t stream);
 bool gemm2_path_ok(const LayerArgs& a);
 
+// Several u8 layers sharing bf16 x in one launch of that kernel (each must
+// pass gemm2_path_ok); tile0 is filled in by the launcher.
+struct GemmSeg {
+  const float* codebook;
+  const uint8_t* indices;
+  const int32_t* sc_rows;
+  const int32_t* sc_cols;
+  const float* sc_deltas;
+  int64_t nnz;
+  const float* bias;
+  float* y;
+  int N;
+  int tile0;
+};
+struct GemmArgs {
+  const void* x;
+  int M, K;
+  int tiles_m;
+  int nseg;
+  GemmSeg seg[kMaxSegments];
+};
+hipError_t launch_gemm_grouped(const GemmSeg* segs, int nseg, const void* x, int M, int K, hipStream_t stream);
+
 // y += S x.
 hipError_t launch_sidecar_add(const LayerArgs& a, hipStream_t stream);
 
