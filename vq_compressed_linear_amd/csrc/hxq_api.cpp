@@ -155,6 +155,38 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
     segs[nseg++] = {l.codebook, l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz, l.bias, l.y, (int)l.N, 0, 0, 0.f};
   }
   if (fast && nseg == 0) return HXQ_OK;
+  if (fast && M > 4) {
+    // the matrix-core GEMV when every layer takes it: one launch when the
+    // layers fit one workgroup per CU, else one launch per layer
+    hxq::GemvSeg gs[hxq::kMaxSegments];
+    int ng = 0;
+    bool mfma = true;
+    for (int i = 0; i < count && mfma; ++i) {
+      const hxq_layer& l = layers[i];
+      if (l.N == 0) continue;
+      hxq::LayerArgs a = {};
+      a.indices = l.indices;
+      a.x = x;
+      a.x_bf16 = x_dtype == HXQ_BF16;
+      a.M = (int)M;
+      a.N = (int)l.N;
+      a.K = (int)K;
+      mfma = hxq::gemv_mfma_ok(a, pk12);
+      gs[ng++] = {static_cast<const float*>(l.codebook), l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz,
+                  l.bias, l.y, (int)l.N, 0};
+    }
+    if (mfma) {
+      (void)hipGetLastError();
+      const bool xbf = x_dtype == HXQ_BF16;
+      if (hxq::gemv_mfma_group_fits(gs, ng))
+        return status_of(hxq::launch_gemv_mfma_grouped(gs, ng, x, xbf, (int)M, (int)K, stream));
+      for (int i = 0; i < ng; ++i) {
+        const hipError_t err = hxq::launch_gemv_mfma_grouped(&gs[i], 1, x, xbf, (int)M, (int)K, stream);
+        if (err != hipSuccess) return status_of(err);
+      }
+      return HXQ_OK;
+    }
+  }
   if (fast) {
     (void)hipGetLastError();
     hipError_t err = hipSuccess;

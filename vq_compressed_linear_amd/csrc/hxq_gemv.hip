@@ -507,13 +507,14 @@ static hipError_t launch_valu_fmt(const LayerArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_gemv_valu(const LayerArgs& a, bool pk12, hipStream_t stream) {
-  if (a.M <= kChunkMaxM) {
-    DecodeSeg sg = {a.codebook, a.indices, a.sc_rows, a.sc_cols, a.sc_deltas, a.nnz, a.bias, a.y, a.N, 0, 0, 0.f};
-    hipError_t err = hipSuccess;
-    if (a.M <= 4 ? launch_decode(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream, err)
-                 : launch_decode_chunked(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream, err))
-      return err;
-  }
+  // up to 4 tokens: the decode kernel; from 5 (or where it does not fit) the
+  // matrix-core GEMV; then token groups through the decode kernel
+  DecodeSeg sg = {a.codebook, a.indices, a.sc_rows, a.sc_cols, a.sc_deltas, a.nnz, a.bias, a.y, a.N, 0, 0, 0.f};
+  hipError_t err = hipSuccess;
+  if (a.M <= 4 && launch_decode(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream, err)) return err;
+  if (gemv_mfma_ok(a, pk12)) return launch_gemv_mfma(a, stream);
+  if (a.M > 4 && a.M <= kChunkMaxM && launch_decode_chunked(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream, err))
+    return err;
   return pk12 ? launch_valu_fmt<true>(a, stream) : launch_valu_fmt<false>(a, stream);
 }
 

@@ -1,0 +1,371 @@
+// Matrix-core HelixLinear GEMV for up to 16 tokens (used from 5, and below
+// that where the decode kernel does not fit), u8 format, fp32 or bf16 x.
+//
+// y[m][n] = sum_k (C[idx[n][k]] + S[n][k]) x[m][k] + b[n] with fp32 products
+// and fp32 sums: the codebook values (fp32) and x (fp32, or bf16 upcast
+// exactly) go into v_mfma_f32_16x16x4_f32, so the arithmetic is the fp32
+// arithmetic of the vector paths, in another summation order.  (The model
+// cards' "codebook[indices] @ x" with no dense weight; the HXQ whitepaper's
+// inference paragraph: gather + sidecar + matmul.)
+//
+// At a handful of tokens the vector kernel spends M fused multiply-adds per
+// gathered weight and becomes ALU-bound; here one gather feeds a 16-token
+// matrix-core step, and the index stream stays the bottleneck up to M = 16.
+//
+// Work split: a workgroup owns whole fragments of 16 rows (at most FMAX) and
+// all of K; its eight waves split K, wave w taking the 64-deep chunk w of
+// every 512-deep slice.  Lane (g, l16) holds the 16 index bytes of row l16,
+// k = 16 g .. 16 g + 15 of its chunk; matrix-core step s sums k = 16 g + s
+// over g, with x read as the B operand for the same k.  x is staged per slice
+// in LDS (double-buffered, one barrier per slice) from registers loaded three
+// slices ahead.  The eight waves' partial
+// tiles are added in wave order at the end; sidecar terms delta * x are added
+// after them in stored order, then the bias.
+
+#include "hxq_device.h"
+#include "hxq_launch.h"
+
+#include <climits>
+
+namespace hxq {
+
+namespace gmv {
+constexpr int THREADS = 512, WAVES = THREADS / 64;
+constexpr int KC = 64;                 // k per wave chunk: 16 index bytes per lane
+constexpr int KS = KC * WAVES;         // k per slice: one chunk per wave
+constexpr int FMAX = 4;                // 16-row fragments per workgroup
+constexpr int XSL = 16 * KS * 4;       // one fp32 x slice for 16 tokens: 32 KB
+constexpr int SCAP = 256;              // sidecar triplets per epilogue pass
+constexpr int OFF_MISC = 2 * XSL;      // lo, hi (int64), row ranges
+constexpr int LDS_DYN = OFF_MISC + 16 + 2 * FMAX * 16 * 4;
+static_assert(WAVES * FMAX * 64 * 16 + SCAP * 16 * 4 <= 2 * XSL, "partials and sidecar terms fit the x buffers");
+}  // namespace gmv
+
+// FN: fragments per workgroup (the launch's largest; a workgroup may own one
+// fewer); MX: x rows staged per slice (8 or 16, at least M)
+template <bool XBF, int FN, int MX>
+__global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma_u8(GemvMArgs ga) {
+  using namespace gmv;
+  __shared__ __align__(16) unsigned char cbs[256 * 256];  // fp32 codebook, 64 copies per entry
+  extern __shared__ __align__(16) unsigned char smem[];
+  int64_t* lohi = reinterpret_cast<int64_t*>(smem + OFF_MISC);
+  int* rsb = reinterpret_cast<int*>(smem + OFF_MISC + 16);  // per row of the block: first, end term
+  int* rse = rsb + FMAX * 16;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  const uint32_t lane4 = (uint32_t)lane << 2;
+  const int G = gridDim.x, bx = blockIdx.x;
+  const int per = G / 8, full = per * 8;
+  const int bb = (bx < full) ? (bx % 8) * per + bx / 8 : bx;  // each XCD a contiguous run of rows
+  // the layer: workgroups wg0[i] .. wg0[i + 1] - 1 belong to layer i
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSegments; ++i)
+    if (i < ga.nseg && bb >= ga.wg0[i]) si = i;
+  const GemvSeg& a = ga.seg[si];
+  const int Gl = (si + 1 < ga.nseg ? ga.wg0[si + 1] : G) - ga.wg0[si];
+  const int b = bb - ga.wg0[si];
+  const int M = ga.M, N = a.N, K = ga.K;
+  const int f0 = (int)((int64_t)b * a.nfrag / Gl), f1 = (int)((int64_t)(b + 1) * a.nfrag / Gl);
+  const int F = f1 - f0;  // FN - 1 .. FN, uniform
+  const int r0 = f0 * 16, r1 = min(f1 * 16, N);
+  const int nsl = (K + KS - 1) / KS;
+
+  // ---- index bytes of (slice s, fragment f): row of fragment f, this wave's chunk
+  const uint8_t* irow[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    const int row = min((f0 + min(f, max(F - 1, 0))) * 16 + l16, N - 1);
+    irow[f] = a.indices + (int64_t)row * K + 16 * g;
+  }
+  auto load_iq = [&](int s, u32x4* d) {
+    const int k0 = min(s * KS + wave * KC, K - KC);  // chunks past K read a valid one, unused
+#pragma unroll
+    for (int f = 0; f < FN; ++f) d[f] = *reinterpret_cast<const u32x4*>(irow[f] + k0);
+  };
+  // ---- x slice: piece p = tid + 512 i covers token p / 128, k = 4 (p % 128) .. + 3 of
+  // the slice; stored at ((k / 16) * 16 + token) * 64 + (k % 16) * 4.  Rows MX .. 15 of
+  // the LDS slice are never written: they only reach result columns that are not stored.
+  constexpr int XPT = MX * KS / 4 / THREADS;  // 4-wide pieces per thread
+  auto load_x = [&](int s, u32x4* XR) {
+    const int sc = min(s, nsl - 1);
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int p = tid + THREADS * i, t = p >> 7, kq = p & 127;
+      const int k = min(sc * KS + 4 * kq, K - 4);
+      const int tm = min(t, M - 1);
+      // (no zeroing: tokens past M repeat row M - 1 into result columns that are
+      // never stored, and k past K only reaches chunks whose steps are skipped;
+      // a select on the loaded value would become a branch around the load)
+      if (XBF) {
+        const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(ga.x) + (int64_t)tm * K + k);
+        XR[i] = u32x4{h.x << 16, h.x & 0xffff0000u, h.y << 16, h.y & 0xffff0000u};
+      } else {
+        XR[i] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(ga.x) + (int64_t)tm * K + k);
+      }
+    }
+  };
+  auto store_x = [&](int s, const u32x4* XR) {
+    unsigned char* buf = smem + (s & 1) * XSL;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int p = tid + THREADS * i, t = p >> 7, kq = p & 127;
+      *reinterpret_cast<u32x4*>(buf + (((kq >> 2) * 16 + t) << 6) + ((kq & 3) << 4)) = XR[i];
+    }
+  };
+
+  // x and index bytes of slice j live in register set j % 3, loaded three
+  // slices ahead (a slice's own work is short next to a memory round trip)
+  // (x of slice 0 and the codebook first: their LDS stores wait for them, and
+  // loads complete in order)
+  u32x4 IQ[3][FN], XR[3][XPT];
+  load_x(0, XR[0]);
+  const float cv = a.codebook[tid & 255];
+  load_iq(0, IQ[0]);
+  load_iq(1, IQ[1]);
+  load_iq(2, IQ[2]);
+  load_x(1, XR[1]);
+  load_x(2, XR[2]);
+
+  // ---- codebook: entry e, copy j at byte e * 256 + 4 j; threads t, t + 256 write half each
+  {
+    const int e = tid & 255, h = tid >> 8;
+    const float4 v4 = make_float4(cv, cv, cv, cv);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) *reinterpret_cast<float4*>(cbs + e * 256 + (((8 * h + q + e) & 15) << 4)) = v4;
+  }
+  // ---- sidecar: the block's triplet range [lo, hi)
+  if (a.nnz > 0 && wave < 2 && F > 0) {
+    const int target = wave == 0 ? r0 : r1;
+    const int64_t guess = (int64_t)((double)a.nnz * (double)target / (double)N);
+    const int64_t v = wave_lower_bound_rows_near(a.sc_rows, a.nnz, target, guess);
+    if (lane == 0) lohi[wave] = v;
+  }
+  store_x(0, XR[0]);
+  load_x(3, XR[0]);
+  __syncthreads();
+
+  f32x4 acc[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one slice: x(s) in buffer s & 1, its index bytes in IQ[s % 3]; stores
+  // x(s + 1), loads x(s + 4) and the index bytes of slice s + 3
+  auto slice = [&](auto r_c, int s) {
+    constexpr int R = decltype(r_c)::value;  // s % 3
+    u32x4* iq = IQ[R];
+    store_x(s + 1, XR[(R + 1) % 3]);
+    load_x(s + 4, XR[(R + 1) % 3]);
+    const bool live = s * KS + wave * KC < K;  // uniform
+    const unsigned char* xb = smem + (s & 1) * XSL + (((4 * wave + g) * 16 + l16) << 6);
+    const u32x4 xq0 = *reinterpret_cast<const u32x4*>(xb);
+    const u32x4 xq1 = *reinterpret_cast<const u32x4*>(xb + 16);
+    const u32x4 xq2 = *reinterpret_cast<const u32x4*>(xb + 32);
+    const u32x4 xq3 = *reinterpret_cast<const u32x4*>(xb + 48);
+    const u32x4 xq[4] = {xq0, xq1, xq2, xq3};
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+      if (f < F && live) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t wd = iq[f][d];
+          const float w0 = lds_load<float>(byte_addr256<0>(wd, lane4), cbs);
+          const float w1 = lds_load<float>(byte_addr256<1>(wd, lane4), cbs);
+          const float w2 = lds_load<float>(byte_addr256<2>(wd, lane4), cbs);
+          const float w3 = lds_load<float>(byte_addr256<3>(wd, lane4), cbs);
+          acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(w0, __uint_as_float(xq[d][0]), acc[f], 0, 0, 0);
+          acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(w1, __uint_as_float(xq[d][1]), acc[f], 0, 0, 0);
+          acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(w2, __uint_as_float(xq[d][2]), acc[f], 0, 0, 0);
+          acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(w3, __uint_as_float(xq[d][3]), acc[f], 0, 0, 0);
+        }
+      }
+    }
+    load_iq(s + 3, iq);
+    __syncthreads();
+  };
+  int s = 0;
+  for (; s + 2 < nsl; s += 3) {
+    slice(std::integral_constant<int, 0>{}, s);
+    slice(std::integral_constant<int, 1>{}, s + 1);
+    slice(std::integral_constant<int, 2>{}, s + 2);
+  }
+  if (s < nsl) slice(std::integral_constant<int, 0>{}, s);
+  if (s + 1 < nsl) slice(std::integral_constant<int, 1>{}, s + 1);
+
+  // ---- partial tiles in wave order; lane (g, l16), register r of fragment f:
+  // row 16 f + 4 g + r of the block, token l16
+  f32x4* part = reinterpret_cast<f32x4*>(smem);
+#pragma unroll
+  for (int f = 0; f < FN; ++f)
+    if (f < F) part[(wave * FMAX + f) * 64 + lane] = acc[f];
+  const int nrow = r1 - r0;
+  int64_t lo = 0, hi = 0;
+  if (a.nnz > 0 && F > 0) {
+    lo = lohi[0];
+    hi = lohi[1];
+  }
+  __syncthreads();
+  // thread o -> token o / (16 F), block row o % (16 F): consecutive threads store consecutive outputs
+  constexpr int OPT = FMAX * 16 * 16 / THREADS;
+  float out[OPT];
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) {
+    const int o = tid + THREADS * i, t = o / (16 * FMAX), j = o % (16 * FMAX);
+    float v = 0.f;
+    if (j < 16 * F) {
+      const int f = j >> 4, jr = j & 15, ln = t + 16 * (jr >> 2);
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) v += part[(w * FMAX + f) * 64 + ln][jr & 3];
+    }
+    out[i] = v;
+  }
+  // ---- sidecar terms delta * x[t][c], each output's in stored order, SCAP triplets a pass
+  float* tv = reinterpret_cast<float*>(smem + WAVES * FMAX * 64 * 16);
+  for (int64_t e0 = lo; e0 < hi; e0 += SCAP) {
+    const int cnt = (int)min<int64_t>(SCAP, hi - e0);
+    __syncthreads();
+    for (int i = tid; i < 16 * FMAX; i += THREADS) rsb[i] = rse[i] = 0;
+    __syncthreads();
+    // threads 0 .. SCAP - 1 take one triplet each; all loads of a pass are
+    // issued together (two dependent round trips: the column, then x)
+    if (tid < SCAP) {
+      const int64_t ee = e0 + min(tid, cnt - 1);
+      const int c = a.sc_cols[ee];
+      const float dl = a.sc_deltas[ee];
+      const int r = a.sc_rows[ee];
+      const int rp = a.sc_rows[ee > 0 ? ee - 1 : 0];
+      const int rn = a.sc_rows[ee + 1 < a.nnz ? ee + 1 : ee];
+      float xv[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int tm = min(t, M - 1);
+        xv[t] = XBF ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(ga.x)[(int64_t)tm * K + c] << 16)
+                    : static_cast<const float*>(ga.x)[(int64_t)tm * K + c];
+      }
+      if (tid < cnt) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) tv[tid * 16 + t] = dl * xv[t];
+        if (tid == 0 || rp != r) rsb[r - r0] = tid;
+        if (tid == cnt - 1 || rn != r) rse[r - r0] = tid + 1;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < OPT; ++i) {
+      const int o = tid + THREADS * i, t = o / (16 * FMAX), j = o % (16 * FMAX);
+      if (j < nrow)
+        for (int e = rsb[j]; e < rse[j]; ++e) out[i] += tv[e * 16 + t];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) {
+    const int o = tid + THREADS * i, t = o / (16 * FMAX), j = o % (16 * FMAX);
+    if (t < M && j < nrow) {
+      const int n = r0 + j;
+      a.y[(int64_t)t * N + n] = out[i] + (a.bias ? a.bias[n] : 0.f);
+    }
+  }
+}
+
+bool gemv_mfma_ok(const LayerArgs& a, bool pk12) {
+  if (pk12 || a.M < 1 || a.M > 16 || a.K < gmv::KC || a.K % gmv::KC != 0) return false;
+  if (reinterpret_cast<uintptr_t>(a.indices) % 16 != 0) return false;
+  if (reinterpret_cast<uintptr_t>(a.x) % (a.x_bf16 ? 8 : 16) != 0) return false;
+  return true;
+}
+
+template <bool XBF, int FN, int MX>
+static hipError_t launch_gemv_mfma_x(const GemvMArgs& g, int grid, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_mfma_u8<XBF, FN, MX>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, gmv::LDS_DYN);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gemv_mfma_u8<XBF, FN, MX>), dim3((unsigned)grid), dim3(gmv::THREADS), gmv::LDS_DYN, stream, g);
+  return hipGetLastError();
+}
+
+template <bool XBF, int MX>
+static hipError_t launch_gemv_mfma_f(const GemvMArgs& g, int fn, int grid, hipStream_t stream) {
+  switch (fn) {
+    case 1: return launch_gemv_mfma_x<XBF, 1, MX>(g, grid, stream);
+    case 2: return launch_gemv_mfma_x<XBF, 2, MX>(g, grid, stream);
+    case 3: return launch_gemv_mfma_x<XBF, 3, MX>(g, grid, stream);
+    default: return launch_gemv_mfma_x<XBF, 4, MX>(g, grid, stream);
+  }
+}
+
+// Workgroups per layer in proportion to its 16-row fragments, each layer at
+// least ceil(fragments / FMAX); false when the launch would need more
+// fragments per workgroup than the kernel takes.
+static bool gemv_mfma_plan(GemvMArgs& g, int& grid, int& fn) {
+  using namespace gmv;
+  const int cus = device_cu_count();
+  int64_t frags = 0;
+  for (int i = 0; i < g.nseg; ++i) frags += g.seg[i].nfrag;
+  int64_t want = frags < cus ? frags : cus;
+  int alloc[kMaxSegments];
+  int64_t tot = 0;
+  for (int i = 0; i < g.nseg; ++i) {
+    const int64_t need = (g.seg[i].nfrag + FMAX - 1) / FMAX;
+    int64_t share = want * g.seg[i].nfrag / frags;
+    if (share < need) share = need;
+    if (share < 1) share = 1;
+    if (share > g.seg[i].nfrag) share = g.seg[i].nfrag;
+    alloc[i] = (int)share;
+    tot += share;
+  }
+  if (tot > INT_MAX / 2) return false;
+  grid = 0;
+  fn = 1;
+  for (int i = 0; i < g.nseg; ++i) {
+    g.wg0[i] = grid;
+    grid += alloc[i];
+    const int f = (g.seg[i].nfrag + alloc[i] - 1) / alloc[i];
+    if (f > fn) fn = f;
+  }
+  for (int i = g.nseg; i < kMaxSegments; ++i) {
+    g.wg0[i] = INT_MAX;
+    g.seg[i] = g.seg[0];
+  }
+  return fn <= FMAX;
+}
+
+hipError_t launch_gemv_mfma_grouped(const GemvSeg* segs, int nseg, const void* x, bool xbf, int M, int K,
+                                    hipStream_t stream) {
+  if (nseg < 1 || nseg > kMaxSegments) return hipErrorInvalidValue;
+  GemvMArgs g;
+  g.x = x;
+  g.M = M;
+  g.K = K;
+  g.nseg = nseg;
+  for (int i = 0; i < nseg; ++i) {
+    g.seg[i] = segs[i];
+    g.seg[i].nfrag = (segs[i].N + 15) / 16;
+  }
+  int grid = 0, fn = 1;
+  if (!gemv_mfma_plan(g, grid, fn)) return hipErrorInvalidValue;
+  if (xbf) return M <= 8 ? launch_gemv_mfma_f<true, 8>(g, fn, grid, stream) : launch_gemv_mfma_f<true, 16>(g, fn, grid, stream);
+  return M <= 8 ? launch_gemv_mfma_f<false, 8>(g, fn, grid, stream) : launch_gemv_mfma_f<false, 16>(g, fn, grid, stream);
+}
+
+bool gemv_mfma_group_fits(const GemvSeg* segs, int nseg) {
+  if (nseg < 1 || nseg > kMaxSegments) return false;
+  GemvMArgs g;
+  g.nseg = nseg;
+  for (int i = 0; i < nseg; ++i) {
+    g.seg[i] = segs[i];
+    g.seg[i].nfrag = (segs[i].N + 15) / 16;
+  }
+  int grid = 0, fn = 1;
+  // one workgroup per CU at most: otherwise separate launches run better
+  return gemv_mfma_plan(g, grid, fn) && grid <= device_cu_count();
+}
+
+hipError_t launch_gemv_mfma(const LayerArgs& a, hipStream_t stream) {
+  const GemvSeg sg = {static_cast<const float*>(a.codebook), a.indices, a.sc_rows, a.sc_cols, a.sc_deltas, a.nnz,
+                      a.bias, a.y, a.N, 0};
+  return launch_gemv_mfma_grouped(&sg, 1, a.x, a.x_bf16, a.M, a.K, stream);
+}
+
+}  // namespace hxq
