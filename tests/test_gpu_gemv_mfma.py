@@ -1,5 +1,5 @@
-"""GPU parity of the matrix-core GEMV (5 <= M <= 16 tokens, u8, K % 64 == 0)
-against the CPU oracle, through the C ABI."""
+"""GPU parity of the matrix-core GEMV (5 <= M <= 16 tokens, u8 and pk12,
+K % 64 == 0) against the CPU oracle, through the C ABI."""
 
 import numpy as np
 import pytest
@@ -40,6 +40,20 @@ def test_gemv_mfma_matches_oracle(x_dtype, M, N, K):
     y = G.run(lay, d, G.dev_x(x_np, x_dtype))
     Y, B = G.oracle_fwd(lay, x_np, x_dtype)
     G.check(y, Y, B, G.TOL_FP32, "gemv mfma")
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M", [5, 9, 16])
+@pytest.mark.parametrize("N,K", [(300, 2048), (8512, 2048), (2048, 4096 + 64)])
+def test_gemv_mfma_pk12_matches_oracle(x_dtype, M, N, K):
+    # 2D pairs: 12-bit indices three bytes per pair of pairs, the 4096-pair table
+    G.say("gemv mfma pk12 %s M=%d N=%d K=%d" % (x_dtype, M, N, K))
+    lay = gen.random_layer(N + K + M + 1, N, K, "pk12", nnz=max(1, N * K // 2000), duplicates=True)
+    d = G.dev_layer(lay)
+    x_np = _x(M + K + 1, M, K, x_dtype)
+    y = G.run(lay, d, G.dev_x(x_np, x_dtype))
+    Y, B = G.oracle_fwd(lay, x_np, x_dtype)
+    G.check(y, Y, B, G.TOL_FP32, "gemv mfma pk12")
 
 
 def test_gemv_mfma_dense_sidecar():

@@ -165,6 +165,7 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
       const hxq_layer& l = layers[i];
       if (l.N == 0) continue;
       hxq::LayerArgs a = {};
+      a.codebook = l.codebook;
       a.indices = l.indices;
       a.x = x;
       a.x_bf16 = x_dtype == HXQ_BF16;
@@ -179,9 +180,9 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
       (void)hipGetLastError();
       const bool xbf = x_dtype == HXQ_BF16;
       if (hxq::gemv_mfma_group_fits(gs, ng))
-        return status_of(hxq::launch_gemv_mfma_grouped(gs, ng, x, xbf, (int)M, (int)K, stream));
+        return status_of(hxq::launch_gemv_mfma_grouped(gs, ng, pk12, x, xbf, (int)M, (int)K, stream));
       for (int i = 0; i < ng; ++i) {
-        const hipError_t err = hxq::launch_gemv_mfma_grouped(&gs[i], 1, x, xbf, (int)M, (int)K, stream);
+        const hipError_t err = hxq::launch_gemv_mfma_grouped(&gs[i], 1, pk12, x, xbf, (int)M, (int)K, stream);
         if (err != hipSuccess) return status_of(err);
       }
       return HXQ_OK;

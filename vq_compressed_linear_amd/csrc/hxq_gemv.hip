@@ -512,7 +512,7 @@ hipError_t launch_gemv_valu(const LayerArgs& a, bool pk12, hipStream_t stream) {
   DecodeSeg sg = {a.codebook, a.indices, a.sc_rows, a.sc_cols, a.sc_deltas, a.nnz, a.bias, a.y, a.N, 0, 0, 0.f};
   hipError_t err = hipSuccess;
   if (a.M <= 4 && launch_decode(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream, err)) return err;
-  if (gemv_mfma_ok(a, pk12)) return launch_gemv_mfma(a, stream);
+  if (gemv_mfma_ok(a, pk12)) return launch_gemv_mfma(a, pk12, stream);
   if (a.M > 4 && a.M <= kChunkMaxM && launch_decode_chunked(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream, err))
     return err;
   return pk12 ? launch_valu_fmt<true>(a, stream) : launch_valu_fmt<false>(a, stream);

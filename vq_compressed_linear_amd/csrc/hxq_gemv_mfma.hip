@@ -1,7 +1,9 @@
 // Matrix-core HelixLinear GEMV for up to 16 tokens (used from 5, and below
-// that where the decode kernel does not fit), u8 format, fp32 or bf16 x.
+// that where the decode kernel does not fit), u8 and pk12, fp32 or bf16 x.
 //
-// y[m][n] = sum_k (C[idx[n][k]] + S[n][k]) x[m][k] + b[n] with fp32 products
+// y[m][n] = sum_k (W[n][k] + S[n][k]) x[m][k] + b[n], W the codebook value of
+// the weight's index (u8) or component k % 2 of its pair's entry (pk12), with
+// fp32 products
 // and fp32 sums: the codebook values (fp32) and x (fp32, or bf16 upcast
 // exactly) go into v_mfma_f32_16x16x4_f32, so the arithmetic is the fp32
 // arithmetic of the vector paths, in another summation order.  (The model
@@ -14,8 +16,9 @@
 //
 // Work split: a workgroup owns whole fragments of 16 rows (at most FMAX) and
 // all of K; its eight waves split K, wave w taking the 64-deep chunk w of
-// every 512-deep slice.  Lane (g, l16) holds the 16 index bytes of row l16,
-// k = 16 g .. 16 g + 15 of its chunk; matrix-core step s sums k = 16 g + s
+// every 512-deep slice.  Lane (g, l16) holds the indices of row l16,
+// k = 16 g .. 16 g + 15 of its chunk (16 bytes u8, 12 bytes = 8 pairs pk12);
+// matrix-core step s sums k = 16 g + s
 // over g, with x read as the B operand for the same k.  x is staged per slice
 // in LDS (double-buffered, one barrier per slice) from registers loaded three
 // slices ahead.  The eight waves' partial
@@ -43,10 +46,11 @@ static_assert(WAVES * FMAX * 64 * 16 + SCAP * 16 * 4 <= 2 * XSL, "partials and s
 
 // FN: fragments per workgroup (the launch's largest; a workgroup may own one
 // fewer); MX: x rows staged per slice (8 or 16, at least M)
-template <bool XBF, int FN, int MX>
-__global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma_u8(GemvMArgs ga) {
+template <bool PK12, bool XBF, int FN, int MX>
+__global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
   using namespace gmv;
-  __shared__ __align__(16) unsigned char cbs[256 * 256];  // fp32 codebook, 64 copies per entry
+  // u8: fp32 codebook, 64 copies per entry; pk12: the 4096 fp32 pairs
+  __shared__ __align__(16) unsigned char cbs[PK12 ? 4096 * 8 : 256 * 256];
   extern __shared__ __align__(16) unsigned char smem[];
   int64_t* lohi = reinterpret_cast<int64_t*>(smem + OFF_MISC);
   int* rsb = reinterpret_cast<int*>(smem + OFF_MISC + 16);  // per row of the block: first, end term
@@ -78,12 +82,20 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma_u8(GemvMArgs ga) {
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
     const int row = min((f0 + min(f, max(F - 1, 0))) * 16 + l16, N - 1);
-    irow[f] = a.indices + (int64_t)row * K + 16 * g;
+    irow[f] = PK12 ? a.indices + (int64_t)row * (K / 4 * 3) + 12 * g : a.indices + (int64_t)row * K + 16 * g;
   }
+  typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
   auto load_iq = [&](int s, u32x4* d) {
     const int k0 = min(s * KS + wave * KC, K - KC);  // chunks past K read a valid one, unused
 #pragma unroll
-    for (int f = 0; f < FN; ++f) d[f] = *reinterpret_cast<const u32x4*>(irow[f] + k0);
+    for (int f = 0; f < FN; ++f) {
+      if (PK12) {
+        const u32x3 v = *reinterpret_cast<const u32x3*>(irow[f] + k0 / 4 * 3);
+        d[f] = u32x4{v[0], v[1], v[2], 0u};
+      } else {
+        d[f] = *reinterpret_cast<const u32x4*>(irow[f] + k0);
+      }
+    }
   };
   // ---- x slice: piece p = tid + 512 i covers token p / 128, k = 4 (p % 128) .. + 3 of
   // the slice; stored at ((k / 16) * 16 + token) * 64 + (k % 16) * 4.  Rows MX .. 15 of
@@ -122,15 +134,27 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma_u8(GemvMArgs ga) {
   // loads complete in order)
   u32x4 IQ[3][FN], XR[3][XPT];
   load_x(0, XR[0]);
-  const float cv = a.codebook[tid & 255];
+  constexpr int CBV = PK12 ? 4096 * 8 / 16 / THREADS : 1;  // 16-byte codebook pieces per thread
+  u32x4 cbv[CBV];
+  float cv = 0.f;
+  if (PK12) {
+#pragma unroll
+    for (int i = 0; i < CBV; ++i) cbv[i] = reinterpret_cast<const u32x4*>(a.codebook)[tid + i * THREADS];
+  } else {
+    cv = a.codebook[tid & 255];
+  }
   load_iq(0, IQ[0]);
   load_iq(1, IQ[1]);
   load_iq(2, IQ[2]);
   load_x(1, XR[1]);
   load_x(2, XR[2]);
 
-  // ---- codebook: entry e, copy j at byte e * 256 + 4 j; threads t, t + 256 write half each
-  {
+  // ---- codebook.  u8: entry e, copy j at byte e * 256 + 4 j; threads t, t + 256 write
+  // half each.  pk12: the table as stored, entry e at byte 8 e.
+  if (PK12) {
+#pragma unroll
+    for (int i = 0; i < CBV; ++i) reinterpret_cast<u32x4*>(cbs)[tid + i * THREADS] = cbv[i];
+  } else {
     const int e = tid & 255, h = tid >> 8;
     const float4 v4 = make_float4(cv, cv, cv, cv);
 #pragma unroll
@@ -170,11 +194,24 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma_u8(GemvMArgs ga) {
       if (f < F && live) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const uint32_t wd = iq[f][d];
-          const float w0 = lds_load<float>(byte_addr256<0>(wd, lane4), cbs);
-          const float w1 = lds_load<float>(byte_addr256<1>(wd, lane4), cbs);
-          const float w2 = lds_load<float>(byte_addr256<2>(wd, lane4), cbs);
-          const float w3 = lds_load<float>(byte_addr256<3>(wd, lane4), cbs);
+          float w0, w1, w2, w3;
+          if (PK12) {
+            // pair group d: 24 bits at byte 3 d of the lane's 12, indices (a, b) =
+            // (v & 0xfff, v >> 12) for weights 4 d, 4 d + 1 and 4 d + 2, 4 d + 3
+            const uint32_t v = d == 0 ? (iq[f][0] & 0xffffffu)
+                             : d == 1 ? (__builtin_amdgcn_alignbit(iq[f][1], iq[f][0], 24) & 0xffffffu)
+                             : d == 2 ? (__builtin_amdgcn_alignbit(iq[f][2], iq[f][1], 16) & 0xffffffu)
+                                      : (iq[f][2] >> 8);
+            const float2 p0 = lds_load<float2>((v & 0xfffu) << 3, cbs);
+            const float2 p1 = lds_load<float2>((v >> 12) << 3, cbs);
+            w0 = p0.x, w1 = p0.y, w2 = p1.x, w3 = p1.y;
+          } else {
+            const uint32_t wd = iq[f][d];
+            w0 = lds_load<float>(byte_addr256<0>(wd, lane4), cbs);
+            w1 = lds_load<float>(byte_addr256<1>(wd, lane4), cbs);
+            w2 = lds_load<float>(byte_addr256<2>(wd, lane4), cbs);
+            w3 = lds_load<float>(byte_addr256<3>(wd, lane4), cbs);
+          }
           acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(w0, __uint_as_float(xq[d][0]), acc[f], 0, 0, 0);
           acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(w1, __uint_as_float(xq[d][1]), acc[f], 0, 0, 0);
           acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(w2, __uint_as_float(xq[d][2]), acc[f], 0, 0, 0);
@@ -270,29 +307,39 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma_u8(GemvMArgs ga) {
 }
 
 bool gemv_mfma_ok(const LayerArgs& a, bool pk12) {
-  if (pk12 || a.M < 1 || a.M > 16 || a.K < gmv::KC || a.K % gmv::KC != 0) return false;
-  if (reinterpret_cast<uintptr_t>(a.indices) % 16 != 0) return false;
+  if (a.M < 1 || a.M > 16 || a.K < gmv::KC || a.K % gmv::KC != 0) return false;
+  if (reinterpret_cast<uintptr_t>(a.indices) % (pk12 ? 4 : 16) != 0) return false;
+  if (pk12 && reinterpret_cast<uintptr_t>(a.codebook) % 16 != 0) return false;
   if (reinterpret_cast<uintptr_t>(a.x) % (a.x_bf16 ? 8 : 16) != 0) return false;
   return true;
 }
 
-template <bool XBF, int FN, int MX>
+template <bool PK12, bool XBF, int FN, int MX>
 static hipError_t launch_gemv_mfma_x(const GemvMArgs& g, int grid, hipStream_t stream) {
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_mfma_u8<XBF, FN, MX>),
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_mfma<PK12, XBF, FN, MX>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, gmv::LDS_DYN);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemv_mfma_u8<XBF, FN, MX>), dim3((unsigned)grid), dim3(gmv::THREADS), gmv::LDS_DYN, stream, g);
+  hipLaunchKernelGGL((gemv_mfma<PK12, XBF, FN, MX>), dim3((unsigned)grid), dim3(gmv::THREADS), gmv::LDS_DYN, stream, g);
   return hipGetLastError();
 }
 
-template <bool XBF, int MX>
+template <bool PK12, bool XBF, int MX>
 static hipError_t launch_gemv_mfma_f(const GemvMArgs& g, int fn, int grid, hipStream_t stream) {
   switch (fn) {
-    case 1: return launch_gemv_mfma_x<XBF, 1, MX>(g, grid, stream);
-    case 2: return launch_gemv_mfma_x<XBF, 2, MX>(g, grid, stream);
-    case 3: return launch_gemv_mfma_x<XBF, 3, MX>(g, grid, stream);
-    default: return launch_gemv_mfma_x<XBF, 4, MX>(g, grid, stream);
+    case 1: return launch_gemv_mfma_x<PK12, XBF, 1, MX>(g, grid, stream);
+    case 2: return launch_gemv_mfma_x<PK12, XBF, 2, MX>(g, grid, stream);
+    case 3: return launch_gemv_mfma_x<PK12, XBF, 3, MX>(g, grid, stream);
+    default: return launch_gemv_mfma_x<PK12, XBF, 4, MX>(g, grid, stream);
   }
+}
+
+template <bool PK12>
+static hipError_t launch_gemv_mfma_p(const GemvMArgs& g, bool xbf, int fn, int grid, hipStream_t stream) {
+  if (xbf)
+    return g.M <= 8 ? launch_gemv_mfma_f<PK12, true, 8>(g, fn, grid, stream)
+                    : launch_gemv_mfma_f<PK12, true, 16>(g, fn, grid, stream);
+  return g.M <= 8 ? launch_gemv_mfma_f<PK12, false, 8>(g, fn, grid, stream)
+                  : launch_gemv_mfma_f<PK12, false, 16>(g, fn, grid, stream);
 }
 
 // Workgroups per layer in proportion to its 16-row fragments, each layer at
@@ -331,8 +378,8 @@ static bool gemv_mfma_plan(GemvMArgs& g, int& grid, int& fn) {
   return fn <= FMAX;
 }
 
-hipError_t launch_gemv_mfma_grouped(const GemvSeg* segs, int nseg, const void* x, bool xbf, int M, int K,
-                                    hipStream_t stream) {
+hipError_t launch_gemv_mfma_grouped(const GemvSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M,
+                                    int K, hipStream_t stream) {
   if (nseg < 1 || nseg > kMaxSegments) return hipErrorInvalidValue;
   GemvMArgs g;
   g.x = x;
@@ -345,8 +392,7 @@ hipError_t launch_gemv_mfma_grouped(const GemvSeg* segs, int nseg, const void* x
   }
   int grid = 0, fn = 1;
   if (!gemv_mfma_plan(g, grid, fn)) return hipErrorInvalidValue;
-  if (xbf) return M <= 8 ? launch_gemv_mfma_f<true, 8>(g, fn, grid, stream) : launch_gemv_mfma_f<true, 16>(g, fn, grid, stream);
-  return M <= 8 ? launch_gemv_mfma_f<false, 8>(g, fn, grid, stream) : launch_gemv_mfma_f<false, 16>(g, fn, grid, stream);
+  return pk12 ? launch_gemv_mfma_p<true>(g, xbf, fn, grid, stream) : launch_gemv_mfma_p<false>(g, xbf, fn, grid, stream);
 }
 
 bool gemv_mfma_group_fits(const GemvSeg* segs, int nseg) {
@@ -362,10 +408,10 @@ bool gemv_mfma_group_fits(const GemvSeg* segs, int nseg) {
   return gemv_mfma_plan(g, grid, fn) && grid <= device_cu_count();
 }
 
-hipError_t launch_gemv_mfma(const LayerArgs& a, hipStream_t stream) {
+hipError_t launch_gemv_mfma(const LayerArgs& a, bool pk12, hipStream_t stream) {
   const GemvSeg sg = {static_cast<const float*>(a.codebook), a.indices, a.sc_rows, a.sc_cols, a.sc_deltas, a.nnz,
                       a.bias, a.y, a.N, 0};
-  return launch_gemv_mfma_grouped(&sg, 1, a.x, a.x_bf16, a.M, a.K, stream);
+  return launch_gemv_mfma_grouped(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream);
 }
 
 }  // namespace hxq

@@ -64,7 +64,7 @@ struct DecodeArgs {
 bool launch_decode(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
                    hipStream_t stream, hipError_t& err);
 bool decode_fits(const DecodeSeg* segs, int nseg, bool pk12, bool xbf, int M, int K);
-// Matrix-core GEMV for M <= 16 (u8, K % 64 == 0): fp32 products on
+// Matrix-core GEMV for M <= 16 (u8 or pk12, K % 64 == 0): fp32 products on
 // v_mfma_f32_16x16x4_f32, one launch per layer.
 struct GemvSeg {
   const float* codebook;
@@ -86,13 +86,13 @@ struct GemvMArgs {
   GemvSeg seg[kMaxSegments];
 };
 bool gemv_mfma_ok(const LayerArgs& a, bool pk12);
-hipError_t launch_gemv_mfma(const LayerArgs& a, hipStream_t stream);
+hipError_t launch_gemv_mfma(const LayerArgs& a, bool pk12, hipStream_t stream);
 // Several layers sharing x in one launch (each must pass gemv_mfma_ok); the
 // fits check is false when the layers need more fragments per workgroup than
 // the kernel takes (then launch them one by one).
 bool gemv_mfma_group_fits(const GemvSeg* segs, int nseg);
-hipError_t launch_gemv_mfma_grouped(const GemvSeg* segs, int nseg, const void* x, bool xbf, int M, int K,
-                                    hipStream_t stream);
+hipError_t launch_gemv_mfma_grouped(const GemvSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M,
+                                    int K, hipStream_t stream);
 
 // M up to kChunkMaxM through the decode kernel in groups of up to four tokens
 // (indices streamed once per group); false when it does not fit.
