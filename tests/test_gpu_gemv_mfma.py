@@ -1,5 +1,6 @@
-"""GPU parity of the matrix-core GEMV (5 <= M <= 16 tokens, u8 and pk12,
-K % 64 == 0) against the CPU oracle, through the C ABI."""
+"""GPU parity of the matrix-core GEMV (5 <= M <= 64 tokens in one launch,
+more in launches of 64; u8 and pk12, K % 64 == 0) against the CPU oracle,
+through the C ABI."""
 
 import numpy as np
 import pytest
@@ -93,3 +94,58 @@ def test_gemv_mfma_constant_index_bit_exact():
     y = G.run(lay, G.dev_layer(lay), G.dev_x(x_np, "f32"), sidecar=False).cpu().numpy()
     want = (np.float32(0.375) * x_np.sum(1, dtype=np.float64)[:, None] + lay.bias[None, :]).astype(np.float32)
     assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
+@pytest.mark.parametrize("M", [17, 24, 32, 33, 40, 64])
+@pytest.mark.parametrize("N,K", [(300, 2048), (2048, 4096 + 64), (8512, 2048)])
+def test_gemv_mfma_token_groups(fmt, M, N, K):
+    # two and four 16-token groups per launch (teams of four and two waves,
+    # 256- and 128-deep slices), ragged last group, fp32 x
+    G.say("gemv mfma groups %s M=%d N=%d K=%d" % (fmt, M, N, K))
+    den = 1000 if fmt == "u8" else 2000
+    lay = gen.random_layer(N + K + 3 * M, N, K, fmt, nnz=max(1, N * K // den), duplicates=True)
+    d = G.dev_layer(lay)
+    x_np = _x(2 * M + K, M, K, "f32")
+    y = G.run(lay, d, G.dev_x(x_np, "f32"))
+    Y, B = G.oracle_fwd(lay, x_np, "f32")
+    G.check(y, Y, B, G.TOL_FP32, "gemv mfma %s M=%d" % (fmt, M))
+
+
+@pytest.mark.parametrize("fmt,x_dtype", [("u8", "f32"), ("pk12", "f32"), ("pk12", "bf16")])
+@pytest.mark.parametrize("M", [65, 130, 200])
+def test_gemv_mfma_chunks_past_64(fmt, x_dtype, M):
+    # launches of 64 tokens on offset x and y rows, ragged last launch
+    G.say("gemv mfma chunks %s %s M=%d" % (fmt, x_dtype, M))
+    N, K = 700, 1024
+    lay = gen.random_layer(M + 7, N, K, fmt, nnz=N * K // 500, duplicates=True)
+    d = G.dev_layer(lay)
+    x_np = _x(M + 8, M, K, x_dtype)
+    y = G.run(lay, d, G.dev_x(x_np, x_dtype))
+    Y, B = G.oracle_fwd(lay, x_np, x_dtype)
+    G.check(y, Y, B, G.TOL_FP32, "gemv mfma chunks %s M=%d" % (fmt, M))
+
+
+def test_gemv_mfma_dense_sidecar_token_groups():
+    # several epilogue passes (128 and 64 triplets each) with 32 and 64 staged tokens
+    lay = gen.random_layer(94, 40, 1024, "u8", nnz=40 * 1024 // 8, duplicates=True)
+    d = G.dev_layer(lay)
+    for M in (20, 64):
+        x_np = _x(M, M, 1024, "f32")
+        y = G.run(lay, d, G.dev_x(x_np, "f32"))
+        Y, B = G.oracle_fwd(lay, x_np, "f32")
+        G.check(y, Y, B, G.TOL_FP32, "gemv mfma dense sidecar M=%d" % M)
+
+
+def test_gemv_mfma_token_groups_constant_index_bit_exact():
+    N, K = 300, 4096
+    lay = gen.random_layer(95, N, K, "u8")
+    lay.codebook[5] = 0.375
+    lay.indices[:] = 5
+    lay.bias = (np.arange(N) % 5 - 2).astype(np.float32) / 8
+    rng = np.random.Generator(np.random.PCG64(6))
+    for M in (29, 64, 97):
+        x_np = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+        y = G.run(lay, G.dev_layer(lay), G.dev_x(x_np, "f32"), sidecar=False).cpu().numpy()
+        want = (np.float32(0.375) * x_np.sum(1, dtype=np.float64)[:, None] + lay.bias[None, :]).astype(np.float32)
+        assert np.array_equal(y, want), M

@@ -63,6 +63,23 @@ def test_grouped_matches_oracle_and_single_calls(fmt, x_dtype, M):
         assert G.torch().equal(y, y1), "grouped and single-layer results differ bitwise"
 
 
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
+@pytest.mark.parametrize("M", [20, 48, 64])
+def test_grouped_token_groups_match_single_calls(fmt, M):
+    # fp32 x past 16 tokens: the matrix-core GEMV with 32 / 64 staged tokens,
+    # one launch for the group, the single-layer kernel's arithmetic
+    G.say("grouped token groups %s M=%d" % (fmt, M))
+    K = 2048
+    lays, ds = _group(fmt, [1000, 96, 2500], K, seed=M + 100)
+    x_np = _x(M + 1, M, K, "f32")
+    xd = G.dev_x(x_np, "f32")
+    ys = _grouped(fmt, lays, ds, xd)
+    for lay, d, y in zip(lays, ds, ys):
+        Y, B = G.oracle_fwd(lay, x_np, "f32")
+        G.check(y, Y, B, G.TOL_FP32, "grouped %s N=%d" % (fmt, lay.N))
+        assert G.torch().equal(y, G.run(lay, d, xd)), "grouped and single-layer results differ bitwise"
+
+
 @pytest.mark.parametrize("M,K", [(17, 2048), (130, 2048), (300, 1024), (130, 96)])
 def test_grouped_prefill_gemm(M, K):
     # bf16 x past the decode sizes: one matrix-core launch over all layers

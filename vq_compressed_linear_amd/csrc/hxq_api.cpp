@@ -155,9 +155,12 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
     segs[nseg++] = {l.codebook, l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz, l.bias, l.y, (int)l.N, 0, 0, 0.f};
   }
   if (fast && nseg == 0) return HXQ_OK;
-  if (fast && M > 4) {
-    // the matrix-core GEMV when every layer takes it: one launch when the
-    // layers fit one workgroup per CU, else one launch per layer
+  // the matrix-core GEMV from 5 to 64 tokens when every layer takes it (and,
+  // for u8 with bf16 x past 16 tokens, where the bf16 GEMM does not take it
+  // instead): one launch when the layers fit one workgroup per CU, else one
+  // launch per layer; the same kernel a single-layer call would run
+  const bool bf16_gemm = !pk12 && x_dtype == HXQ_BF16 && M > 16;
+  if (K > 0 && M > 4 && M <= hxq::kGemvMfmaMaxM && !bf16_gemm) {
     hxq::GemvSeg gs[hxq::kMaxSegments];
     int ng = 0;
     bool mfma = true;
@@ -172,10 +175,11 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
       a.M = (int)M;
       a.N = (int)l.N;
       a.K = (int)K;
-      mfma = hxq::gemv_mfma_ok(a, pk12);
+      mfma = hxq::gemv_fast_path_ok(a, pk12) && hxq::gemv_mfma_ok(a, pk12);
       gs[ng++] = {static_cast<const float*>(l.codebook), l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz,
                   l.bias, l.y, (int)l.N, 0};
     }
+    if (mfma && ng == 0) return HXQ_OK;
     if (mfma) {
       (void)hipGetLastError();
       const bool xbf = x_dtype == HXQ_BF16;

@@ -88,15 +88,19 @@ __device__ __forceinline__ int wave_sum_dpp_i(int v) {
 
 // First sidecar entry with row >= target, searched by one wave in parallel:
 // each round the 64 lanes probe 64 evenly spaced positions of [lo, hi).
-// Every lane returns the same value.
+// Every lane returns the same value.  (Probes past the range load a clamped
+// position and are masked after the load: a load under a condition would make
+// each round wait for every load the wave has in flight.)
 __device__ __forceinline__ int64_t wave_lower_bound_rows(const int32_t* rows, int64_t nnz,
                                                          int32_t target) {
+  if (nnz <= 0) return 0;
   int64_t lo = 0, hi = nnz;
   const int lane = lane_id();
   while (hi - lo > kWave) {
     const int64_t step = (hi - lo + kWave - 1) / kWave;
     const int64_t p = lo + lane * step;
-    const bool below = (p < hi) && (rows[p] < target);
+    const int32_t v = rows[p < hi ? p : hi - 1];
+    const bool below = (p < hi) & (v < target);
     const uint64_t mask = __ballot(below);
     const int c = __popcll(mask);
     if (c == 0) return lo;
@@ -105,8 +109,10 @@ __device__ __forceinline__ int64_t wave_lower_bound_rows(const int32_t* rows, in
     lo = nlo;
     hi = nhi < hi ? nhi : hi;
   }
+  // hi > 0 here (nnz > 0, and every round leaves hi >= 1)
   const int64_t p = lo + lane;
-  const bool below = (p < hi) && (rows[p] < target);
+  const int32_t v = rows[p < hi ? p : hi - 1];
+  const bool below = (p < hi) & (v < target);
   return lo + __popcll(__ballot(below));
 }
 
@@ -118,15 +124,19 @@ __device__ __forceinline__ int64_t wave_lower_bound_rows(const int32_t* rows, in
 __device__ __forceinline__ int64_t wave_lower_bound_rows_near(const int32_t* rows, int64_t nnz,
                                                               int32_t target, int64_t guess) {
   constexpr int64_t WIN = 16 * kWave;
+  if (nnz <= 0) return 0;
   if (nnz <= WIN) {
-    // the whole array fits the window
+    // the whole array fits the window (clamped loads, masked after loading)
     const int lane = lane_id();
-    int c = 0;
+    int32_t v[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int64_t p = (int64_t)lane * 16 + j;
-      c += (p < nnz && rows[p] < target) ? 1 : 0;
+      v[j] = rows[p < nnz ? p : nnz - 1];
     }
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c += (int)((int64_t)lane * 16 + j < nnz) & (int)(v[j] < target);
     return wave_sum_dpp_i(c);
   }
   int64_t ws = guess - WIN / 2;
@@ -149,6 +159,46 @@ __device__ __forceinline__ int64_t wave_lower_bound_rows_near(const int32_t* row
   const bool lo_ok = total > 0 || ws == 0;
   const bool hi_ok = total < WIN || ws + WIN == nnz;
   if (lo_ok && hi_ok) return ws + total;
+  return wave_lower_bound_rows(rows, nnz, target);
+}
+
+// The same lower bound in two steps, so that the loads can go out long before
+// the answer is needed: row_window_load reads the 1024 rows around `guess`
+// (clamped to the array), lane l rows l, l + 64, ... of it (each load one
+// contiguous 256-byte piece); row_window_lower_bound
+// counts the rows below `target` there and falls back to the general search
+// when the answer is not strictly inside the window.  Needs nnz > 0.
+struct RowWindow {
+  int64_t ws;
+  int32_t v[16];
+};
+__device__ __forceinline__ void row_window_load(const int32_t* rows, int64_t nnz, int64_t guess, RowWindow& w) {
+  constexpr int64_t WIN = 16 * kWave;
+  int64_t ws = guess - WIN / 2;
+  if (ws > nnz - WIN) ws = nnz - WIN;
+  if (ws < 0) ws = 0;
+  w.ws = ws;
+  const int64_t p0 = ws + lane_id();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) w.v[j] = rows[p0 + kWave * j < nnz ? p0 + kWave * j : nnz - 1];
+}
+__device__ __forceinline__ int64_t row_window_lower_bound(const int32_t* rows, int64_t nnz, int32_t target,
+                                                          const RowWindow& w) {
+  constexpr int64_t WIN = 16 * kWave;
+  const int64_t p0 = w.ws + lane_id();
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    // (the empty asm pins the compare here: hoisted next to the loads, it would
+    // make the caller wait for them there)
+    int32_t v = w.v[j];
+    asm volatile("" : "+v"(v));
+    c += (int)(p0 + kWave * j < nnz) & (int)(v < target);
+  }
+  const int total = wave_sum_dpp_i(c);
+  const bool lo_ok = total > 0 || w.ws == 0;
+  const bool hi_ok = total < WIN || w.ws + WIN >= nnz;
+  if (lo_ok && hi_ok) return w.ws + total;
   return wave_lower_bound_rows(rows, nnz, target);
 }
 

@@ -1,4 +1,4 @@
-// Matrix-core HelixLinear GEMV for up to 16 tokens (used from 5, and below
+// Matrix-core HelixLinear GEMV for up to 64 tokens (used from 5, and below
 // that where the decode kernel does not fit), u8 and pk12, fp32 or bf16 x.
 //
 // y[m][n] = sum_k (W[n][k] + S[n][k]) x[m][k] + b[n], W the codebook value of
@@ -15,13 +15,16 @@
 // matrix-core step, and the index stream stays the bottleneck up to M = 16.
 //
 // Work split: a workgroup owns whole fragments of 16 rows (at most FMAX) and
-// all of K; its eight waves split K, wave w taking the 64-deep chunk w of
-// every 512-deep slice.  Lane (g, l16) holds the indices of row l16,
+// all of K.  Tokens come in TG groups of 16 (one group up to 16 tokens, two
+// up to 32, four up to 64); the eight waves are TG teams of 8 / TG, and wave
+// c of a team takes the 64-deep chunk c of every slice (512 / TG deep) for
+// the team's tokens, so every index byte is fetched by TG waves (the repeats
+// hit the caches).  Lane (g, l16) holds the indices of row l16,
 // k = 16 g .. 16 g + 15 of its chunk (16 bytes u8, 12 bytes = 8 pairs pk12);
 // matrix-core step s sums k = 16 g + s
 // over g, with x read as the B operand for the same k.  x is staged per slice
 // in LDS (double-buffered, one barrier per slice) from registers loaded three
-// slices ahead.  The eight waves' partial
+// slices ahead.  A team's partial
 // tiles are added in wave order at the end; sidecar terms delta * x are added
 // after them in stored order, then the bias.
 
@@ -35,20 +38,25 @@ namespace hxq {
 namespace gmv {
 constexpr int THREADS = 512, WAVES = THREADS / 64;
 constexpr int KC = 64;                 // k per wave chunk: 16 index bytes per lane
-constexpr int KS = KC * WAVES;         // k per slice: one chunk per wave
 constexpr int FMAX = 4;                // 16-row fragments per workgroup
-constexpr int XSL = 16 * KS * 4;       // one fp32 x slice for 16 tokens: 32 KB
-constexpr int SCAP = 256;              // sidecar triplets per epilogue pass
+constexpr int XSL = 16 * KC * WAVES * 4;  // one fp32 x slice (tokens x k): 32 KB
+constexpr int TV = 8192;               // sidecar terms (triplets x staged tokens) per epilogue pass
 constexpr int OFF_MISC = 2 * XSL;      // lo, hi (int64), row ranges
 constexpr int LDS_DYN = OFF_MISC + 16 + 2 * FMAX * 16 * 4;
-static_assert(WAVES * FMAX * 64 * 16 + SCAP * 16 * 4 <= 2 * XSL, "partials and sidecar terms fit the x buffers");
+static_assert(WAVES * FMAX * 64 * 16 + TV * 4 <= 2 * XSL, "partials and sidecar terms fit the x buffers");
 }  // namespace gmv
 
 // FN: fragments per workgroup (the launch's largest; a workgroup may own one
-// fewer); MX: x rows staged per slice (8 or 16, at least M)
+// fewer); MX: x rows staged per slice (8, 16, 32 or 64, at least M)
 template <bool PK12, bool XBF, int FN, int MX>
 __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
   using namespace gmv;
+  constexpr int TG = MX > 16 ? MX / 16 : 1;  // token groups of 16
+  constexpr int WPG = WAVES / TG;            // waves per team
+  constexpr int KS = KC * WPG;               // k per slice: one chunk per wave of a team
+  constexpr int MXR = 16 * TG;               // token slots of the result tile
+  constexpr int SCAP = TV / MXR;             // sidecar triplets per epilogue pass
+  static_assert(MX * KS * 4 <= XSL, "x slice fits its buffer");
   // u8: fp32 codebook, 64 copies per entry; pk12: the 4096 fp32 pairs
   __shared__ __align__(16) unsigned char cbs[PK12 ? 4096 * 8 : 256 * 256];
   extern __shared__ __align__(16) unsigned char smem[];
@@ -59,6 +67,7 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
+  const int team = wave / WPG, cw = wave % WPG;  // token group, chunk in the slice
   const uint32_t lane4 = (uint32_t)lane << 2;
   const int G = gridDim.x, bx = blockIdx.x;
   const int per = G / 8, full = per * 8;
@@ -86,7 +95,7 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
   }
   typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
   auto load_iq = [&](int s, u32x4* d) {
-    const int k0 = min(s * KS + wave * KC, K - KC);  // chunks past K read a valid one, unused
+    const int k0 = min(s * KS + cw * KC, K - KC);  // chunks past K read a valid one, unused
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
       if (PK12) {
@@ -97,15 +106,19 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
       }
     }
   };
-  // ---- x slice: piece p = tid + 512 i covers token p / 128, k = 4 (p % 128) .. + 3 of
-  // the slice; stored at ((k / 16) * 16 + token) * 64 + (k % 16) * 4.  Rows MX .. 15 of
-  // the LDS slice are never written: they only reach result columns that are not stored.
+  // ---- x slice: piece p = tid + 512 i covers token p / (KS / 4), k = 4 (p % (KS / 4))
+  // .. + 3 of the slice; token t = 16 q + t16 is stored at
+  // ((q * KS / 16 + k / 16) * 16 + t16) * 64 + (k % 16) * 4.  With MX = 8, rows 8 .. 15
+  // of the LDS slice are never written: they only reach result columns that are not
+  // stored.
   constexpr int XPT = MX * KS / 4 / THREADS;  // 4-wide pieces per thread
+  constexpr int PR = KS / 4;                  // pieces per token row
+  static_assert(XPT * THREADS == MX * PR, "pieces cover the slice");
   auto load_x = [&](int s, u32x4* XR) {
     const int sc = min(s, nsl - 1);
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int p = tid + THREADS * i, t = p >> 7, kq = p & 127;
+      const int p = tid + THREADS * i, t = p / PR, kq = p % PR;
       const int k = min(sc * KS + 4 * kq, K - 4);
       const int tm = min(t, M - 1);
       // (no zeroing: tokens past M repeat row M - 1 into result columns that are
@@ -123,8 +136,9 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
     unsigned char* buf = smem + (s & 1) * XSL;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int p = tid + THREADS * i, t = p >> 7, kq = p & 127;
-      *reinterpret_cast<u32x4*>(buf + (((kq >> 2) * 16 + t) << 6) + ((kq & 3) << 4)) = XR[i];
+      const int p = tid + THREADS * i, t = p / PR, kq = p % PR;
+      *reinterpret_cast<u32x4*>(buf + ((((t >> 4) * (KS / 16) + (kq >> 2)) * 16 + (t & 15)) << 6) +
+                                ((kq & 3) << 4)) = XR[i];
     }
   };
 
@@ -132,6 +146,13 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
   // slices ahead (a slice's own work is short next to a memory round trip)
   // (x of slice 0 and the codebook first: their LDS stores wait for them, and
   // loads complete in order)
+  // sidecar: waves 0 and 1 look up the first triplet of rows r0 and r1; their
+  // window loads go out before everything else, so the answer does not wait
+  // for the prefetch behind it
+  const bool srch = a.nnz > 0 && wave < 2 && F > 0;  // uniform
+  const int target = wave == 0 ? r0 : r1;
+  RowWindow win;
+  if (srch) row_window_load(a.sc_rows, a.nnz, (int64_t)((double)a.nnz * (double)target / (double)N), win);
   u32x4 IQ[3][FN], XR[3][XPT];
   load_x(0, XR[0]);
   constexpr int CBV = PK12 ? 4096 * 8 / 16 / THREADS : 1;  // 16-byte codebook pieces per thread
@@ -160,16 +181,36 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) *reinterpret_cast<float4*>(cbs + e * 256 + (((8 * h + q + e) & 15) << 4)) = v4;
   }
-  // ---- sidecar: the block's triplet range [lo, hi)
-  if (a.nnz > 0 && wave < 2 && F > 0) {
-    const int target = wave == 0 ? r0 : r1;
-    const int64_t guess = (int64_t)((double)a.nnz * (double)target / (double)N);
-    const int64_t v = wave_lower_bound_rows_near(a.sc_rows, a.nnz, target, guess);
+  // ---- sidecar: the block's triplet range [lo, hi) (kept below the prefetch: a
+  // compiler barrier stops the lookup, and its wait, from being hoisted above it)
+  asm volatile("" ::: "memory");
+  if (srch) {
+    const int64_t v = row_window_lower_bound(a.sc_rows, a.nnz, target, win);
     if (lane == 0) lohi[wave] = v;
   }
   store_x(0, XR[0]);
   load_x(3, XR[0]);
   __syncthreads();
+
+  // the block's triplet range, and the triplets of the first epilogue pass,
+  // requested now: they are older than every load the slices wait for
+  int64_t lo = 0, hi = 0;
+  if (a.nnz > 0 && F > 0) {
+    lo = lohi[0];
+    hi = lohi[1];
+  }
+  const int te = tid % SCAP, tq = tid / SCAP;  // epilogue: triplet, token group
+  int tc = 0, tr = 0, trp = 0, trn = 0;
+  float tdl = 0.f;
+  if (lo < hi && tid < SCAP * TG) {
+    const int cnt = (int)min<int64_t>(SCAP, hi - lo);
+    const int64_t ee = lo + min(te, cnt - 1);
+    tc = a.sc_cols[ee];
+    tdl = a.sc_deltas[ee];
+    tr = a.sc_rows[ee];
+    trp = a.sc_rows[ee > 0 ? ee - 1 : 0];
+    trn = a.sc_rows[ee + 1 < a.nnz ? ee + 1 : ee];
+  }
 
   f32x4 acc[FN];
 #pragma unroll
@@ -182,8 +223,8 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
     u32x4* iq = IQ[R];
     store_x(s + 1, XR[(R + 1) % 3]);
     load_x(s + 4, XR[(R + 1) % 3]);
-    const bool live = s * KS + wave * KC < K;  // uniform
-    const unsigned char* xb = smem + (s & 1) * XSL + (((4 * wave + g) * 16 + l16) << 6);
+    const bool live = s * KS + cw * KC < K;  // uniform
+    const unsigned char* xb = smem + (s & 1) * XSL + (((team * (KS / 16) + 4 * cw + g) * 16 + l16) << 6);
     const u32x4 xq0 = *reinterpret_cast<const u32x4*>(xb);
     const u32x4 xq1 = *reinterpret_cast<const u32x4*>(xb + 16);
     const u32x4 xq2 = *reinterpret_cast<const u32x4*>(xb + 32);
@@ -231,30 +272,26 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
   if (s < nsl) slice(std::integral_constant<int, 0>{}, s);
   if (s + 1 < nsl) slice(std::integral_constant<int, 1>{}, s + 1);
 
-  // ---- partial tiles in wave order; lane (g, l16), register r of fragment f:
-  // row 16 f + 4 g + r of the block, token l16
+  // ---- partial tiles, each team's in wave order; lane (g, l16), register r of
+  // fragment f: row 16 f + 4 g + r of the block, token 16 team + l16
   f32x4* part = reinterpret_cast<f32x4*>(smem);
 #pragma unroll
   for (int f = 0; f < FN; ++f)
     if (f < F) part[(wave * FMAX + f) * 64 + lane] = acc[f];
   const int nrow = r1 - r0;
-  int64_t lo = 0, hi = 0;
-  if (a.nnz > 0 && F > 0) {
-    lo = lohi[0];
-    hi = lohi[1];
-  }
   __syncthreads();
-  // thread o -> token o / (16 F), block row o % (16 F): consecutive threads store consecutive outputs
-  constexpr int OPT = FMAX * 16 * 16 / THREADS;
+  // thread o -> token o / (16 FMAX), block row o % (16 FMAX): consecutive threads store
+  // consecutive outputs
+  constexpr int OPT = FMAX * 16 * MXR / THREADS;
   float out[OPT];
 #pragma unroll
   for (int i = 0; i < OPT; ++i) {
     const int o = tid + THREADS * i, t = o / (16 * FMAX), j = o % (16 * FMAX);
     float v = 0.f;
     if (j < 16 * F) {
-      const int f = j >> 4, jr = j & 15, ln = t + 16 * (jr >> 2);
+      const int f = j >> 4, jr = j & 15, ln = (t & 15) + 16 * (jr >> 2), w0 = (t >> 4) * WPG;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) v += part[(w * FMAX + f) * 64 + ln][jr & 3];
+      for (int w = 0; w < WPG; ++w) v += part[((w0 + w) * FMAX + f) * 64 + ln][jr & 3];
     }
     out[i] = v;
   }
@@ -265,27 +302,32 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
     __syncthreads();
     for (int i = tid; i < 16 * FMAX; i += THREADS) rsb[i] = rse[i] = 0;
     __syncthreads();
-    // threads 0 .. SCAP - 1 take one triplet each; all loads of a pass are
-    // issued together (two dependent round trips: the column, then x)
-    if (tid < SCAP) {
-      const int64_t ee = e0 + min(tid, cnt - 1);
-      const int c = a.sc_cols[ee];
-      const float dl = a.sc_deltas[ee];
-      const int r = a.sc_rows[ee];
-      const int rp = a.sc_rows[ee > 0 ? ee - 1 : 0];
-      const int rn = a.sc_rows[ee + 1 < a.nnz ? ee + 1 : ee];
+    // thread e + SCAP q takes triplet e for tokens 16 q .. 16 q + 15; all loads of a
+    // pass are issued together (the first pass's triplets are already here)
+    if (tid < SCAP * TG) {
+      const int e = te, q = tq;
+      if (e0 != lo) {
+        const int64_t ee = e0 + min(e, cnt - 1);
+        tc = a.sc_cols[ee];
+        tdl = a.sc_deltas[ee];
+        tr = a.sc_rows[ee];
+        trp = a.sc_rows[ee > 0 ? ee - 1 : 0];
+        trn = a.sc_rows[ee + 1 < a.nnz ? ee + 1 : ee];
+      }
+      const int c = tc, r = tr, rp = trp, rn = trn;
+      const float dl = tdl;
       float xv[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const int tm = min(t, M - 1);
+        const int tm = min(16 * q + t, M - 1);
         xv[t] = XBF ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(ga.x)[(int64_t)tm * K + c] << 16)
                     : static_cast<const float*>(ga.x)[(int64_t)tm * K + c];
       }
-      if (tid < cnt) {
+      if (e < cnt) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) tv[tid * 16 + t] = dl * xv[t];
-        if (tid == 0 || rp != r) rsb[r - r0] = tid;
-        if (tid == cnt - 1 || rn != r) rse[r - r0] = tid + 1;
+        for (int t = 0; t < 16; ++t) tv[e * MXR + 16 * q + t] = dl * xv[t];
+        if (q == 0 && (e == 0 || rp != r)) rsb[r - r0] = e;
+        if (q == 0 && (e == cnt - 1 || rn != r)) rse[r - r0] = e + 1;
       }
     }
     __syncthreads();
@@ -293,7 +335,7 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
     for (int i = 0; i < OPT; ++i) {
       const int o = tid + THREADS * i, t = o / (16 * FMAX), j = o % (16 * FMAX);
       if (j < nrow)
-        for (int e = rsb[j]; e < rse[j]; ++e) out[i] += tv[e * 16 + t];
+        for (int e = rsb[j]; e < rse[j]; ++e) out[i] += tv[e * MXR + t];
     }
   }
 #pragma unroll
@@ -307,7 +349,7 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
 }
 
 bool gemv_mfma_ok(const LayerArgs& a, bool pk12) {
-  if (a.M < 1 || a.M > 16 || a.K < gmv::KC || a.K % gmv::KC != 0) return false;
+  if (a.M < 1 || a.M > kGemvMfmaMaxM || a.K < gmv::KC || a.K % gmv::KC != 0) return false;
   if (reinterpret_cast<uintptr_t>(a.indices) % (pk12 ? 4 : 16) != 0) return false;
   if (pk12 && reinterpret_cast<uintptr_t>(a.codebook) % 16 != 0) return false;
   if (reinterpret_cast<uintptr_t>(a.x) % (a.x_bf16 ? 8 : 16) != 0) return false;
@@ -335,11 +377,16 @@ static hipError_t launch_gemv_mfma_f(const GemvMArgs& g, int fn, int grid, hipSt
 
 template <bool PK12>
 static hipError_t launch_gemv_mfma_p(const GemvMArgs& g, bool xbf, int fn, int grid, hipStream_t stream) {
-  if (xbf)
-    return g.M <= 8 ? launch_gemv_mfma_f<PK12, true, 8>(g, fn, grid, stream)
-                    : launch_gemv_mfma_f<PK12, true, 16>(g, fn, grid, stream);
-  return g.M <= 8 ? launch_gemv_mfma_f<PK12, false, 8>(g, fn, grid, stream)
-                  : launch_gemv_mfma_f<PK12, false, 16>(g, fn, grid, stream);
+  if (xbf) {
+    if (g.M <= 8) return launch_gemv_mfma_f<PK12, true, 8>(g, fn, grid, stream);
+    if (g.M <= 16) return launch_gemv_mfma_f<PK12, true, 16>(g, fn, grid, stream);
+    if (g.M <= 32) return launch_gemv_mfma_f<PK12, true, 32>(g, fn, grid, stream);
+    return launch_gemv_mfma_f<PK12, true, 64>(g, fn, grid, stream);
+  }
+  if (g.M <= 8) return launch_gemv_mfma_f<PK12, false, 8>(g, fn, grid, stream);
+  if (g.M <= 16) return launch_gemv_mfma_f<PK12, false, 16>(g, fn, grid, stream);
+  if (g.M <= 32) return launch_gemv_mfma_f<PK12, false, 32>(g, fn, grid, stream);
+  return launch_gemv_mfma_f<PK12, false, 64>(g, fn, grid, stream);
 }
 
 // Workgroups per layer in proportion to its 16-row fragments, each layer at

@@ -64,8 +64,9 @@ struct DecodeArgs {
 bool launch_decode(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
                    hipStream_t stream, hipError_t& err);
 bool decode_fits(const DecodeSeg* segs, int nseg, bool pk12, bool xbf, int M, int K);
-// Matrix-core GEMV for M <= 16 (u8 or pk12, K % 64 == 0): fp32 products on
-// v_mfma_f32_16x16x4_f32, one launch per layer.
+// Matrix-core GEMV for M <= kGemvMfmaMaxM (u8 or pk12, K % 64 == 0): fp32
+// products on v_mfma_f32_16x16x4_f32, one launch per layer.
+constexpr int kGemvMfmaMaxM = 64;
 struct GemvSeg {
   const float* codebook;
   const uint8_t* indices;
