@@ -62,10 +62,15 @@ def group_bytes(layers, M, x_bytes):
     return sum(layer_bytes(l.fmt, l.N, l.K, l.nnz, M, x_bytes, with_x=(i == 0)) for i, l in enumerate(layers))
 
 
+# the decode kernel's source and the headers it includes: the counters in
+# profiles/traffic.json are that kernel's and stay valid while these are unchanged
+DECODE_SOURCES = ("hxq_decode.hip", "hxq_device.h", "hxq_launch.h")
+
+
 def source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "vq_compressed_linear_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in DECODE_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

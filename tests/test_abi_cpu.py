@@ -62,6 +62,9 @@ BAD = [
     (dict(nnz=1, cols=FAKE + 2), B.HXQ_ERR_ALIGN),
     (dict(variant=9), B.HXQ_ERR_UNSUPPORTED),
     (dict(variant=-1), B.HXQ_ERR_UNSUPPORTED),
+    # the fp32 matrix-core GEMV needs K % 64 == 0 (checked on the host)
+    (dict(variant=B.HXQ_VARIANT_GEMV_MFMA, K=16), B.HXQ_ERR_UNSUPPORTED),
+    (dict(variant=B.HXQ_VARIANT_GEMV_MFMA, K=96, M=100), B.HXQ_ERR_UNSUPPORTED),
 ]
 
 

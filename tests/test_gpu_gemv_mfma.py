@@ -149,3 +149,18 @@ def test_gemv_mfma_token_groups_constant_index_bit_exact():
         y = G.run(lay, G.dev_layer(lay), G.dev_x(x_np, "f32"), sidecar=False).cpu().numpy()
         want = (np.float32(0.375) * x_np.sum(1, dtype=np.float64)[:, None] + lay.bias[None, :]).astype(np.float32)
         assert np.array_equal(y, want), M
+
+
+@pytest.mark.parametrize("fmt,x_dtype", [("u8", "f32"), ("u8", "bf16"), ("pk12", "f32")])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 70])
+def test_gemv_mfma_forced(fmt, x_dtype, M):
+    # the kernel forced where the automatic choice takes another one (up to
+    # four tokens, and bf16 x past 16 tokens for u8)
+    G.say("gemv mfma forced %s %s M=%d" % (fmt, x_dtype, M))
+    N, K = 1000, 2048
+    lay = gen.random_layer(M + 50, N, K, fmt, nnz=N * K // 1000, duplicates=True)
+    d = G.dev_layer(lay)
+    x_np = _x(M + 51, M, K, x_dtype)
+    y = G.run(lay, d, G.dev_x(x_np, x_dtype), variant=hx.HXQ_VARIANT_GEMV_MFMA)
+    Y, B = G.oracle_fwd(lay, x_np, x_dtype)
+    G.check(y, Y, B, G.TOL_FP32, "gemv mfma forced %s M=%d" % (fmt, M))

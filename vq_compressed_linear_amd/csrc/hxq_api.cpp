@@ -76,6 +76,9 @@ int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32
     case HXQ_VARIANT_GEMV_VALU:
       if (!gemv_ok) return HXQ_ERR_UNSUPPORTED;
       return status_of(hxq::launch_gemv_valu(a, pk12, stream));
+    case HXQ_VARIANT_GEMV_MFMA:
+      if (!gemv_ok || !hxq::gemv_mfma_takes(a, pk12)) return HXQ_ERR_UNSUPPORTED;
+      return status_of(hxq::launch_gemv_mfma_tokens(a, pk12, stream));
     case HXQ_VARIANT_GEMM_BF16:
       if (!gemm_ok) return HXQ_ERR_UNSUPPORTED;
       if (hxq::gemm2_path_ok(a)) return status_of(hxq::launch_gemm2_bf16(a, stream));

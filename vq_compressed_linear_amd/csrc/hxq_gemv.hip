@@ -513,21 +513,7 @@ hipError_t launch_gemv_valu(const LayerArgs& a, bool pk12, hipStream_t stream) {
   DecodeSeg sg = {a.codebook, a.indices, a.sc_rows, a.sc_cols, a.sc_deltas, a.nnz, a.bias, a.y, a.N, 0, 0, 0.f};
   hipError_t err = hipSuccess;
   if (a.M <= 4 && launch_decode(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream, err)) return err;
-  if (gemv_mfma_ok(a, pk12)) return launch_gemv_mfma(a, pk12, stream);
-  LayerArgs c = a;
-  c.M = kGemvMfmaMaxM;
-  if (a.M > kGemvMfmaMaxM && gemv_mfma_ok(c, pk12)) {
-    // chunk offsets are multiples of 64 x rows of K % 64 == 0 elements: x stays aligned
-    const size_t xrow = (size_t)a.K * (a.x_bf16 ? 2 : 4);
-    for (int m0 = 0; m0 < a.M; m0 += kGemvMfmaMaxM) {
-      c.M = min(kGemvMfmaMaxM, a.M - m0);
-      c.x = static_cast<const unsigned char*>(a.x) + (size_t)m0 * xrow;
-      c.y = a.y + (size_t)m0 * a.N;
-      err = launch_gemv_mfma(c, pk12, stream);
-      if (err != hipSuccess) return err;
-    }
-    return hipSuccess;
-  }
+  if (gemv_mfma_takes(a, pk12)) return launch_gemv_mfma_tokens(a, pk12, stream);
   if (a.M > 4 && a.M <= kChunkMaxM && launch_decode_chunked(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream, err))
     return err;
   return pk12 ? launch_valu_fmt<true>(a, stream) : launch_valu_fmt<false>(a, stream);

@@ -461,4 +461,26 @@ hipError_t launch_gemv_mfma(const LayerArgs& a, bool pk12, hipStream_t stream) {
   return launch_gemv_mfma_grouped(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream);
 }
 
+bool gemv_mfma_takes(const LayerArgs& a, bool pk12) {
+  LayerArgs c = a;
+  c.M = min(a.M, kGemvMfmaMaxM);
+  return a.M >= 1 && gemv_mfma_ok(c, pk12);
+}
+
+hipError_t launch_gemv_mfma_tokens(const LayerArgs& a, bool pk12, hipStream_t stream) {
+  if (a.M <= kGemvMfmaMaxM) return launch_gemv_mfma(a, pk12, stream);
+  // launches of 64 tokens on offset x and y rows; the offsets are multiples of
+  // 64 rows of K % 64 == 0 elements, so x stays aligned
+  LayerArgs c = a;
+  const size_t xrow = (size_t)a.K * (a.x_bf16 ? 2 : 4);
+  for (int m0 = 0; m0 < a.M; m0 += kGemvMfmaMaxM) {
+    c.M = min(kGemvMfmaMaxM, a.M - m0);
+    c.x = static_cast<const unsigned char*>(a.x) + (size_t)m0 * xrow;
+    c.y = a.y + (size_t)m0 * a.N;
+    const hipError_t err = launch_gemv_mfma(c, pk12, stream);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
 }  // namespace hxq

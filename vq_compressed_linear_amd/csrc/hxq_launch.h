@@ -88,6 +88,10 @@ struct GemvMArgs {
 };
 bool gemv_mfma_ok(const LayerArgs& a, bool pk12);
 hipError_t launch_gemv_mfma(const LayerArgs& a, bool pk12, hipStream_t stream);
+// Any M >= 1: one launch up to kGemvMfmaMaxM tokens, launches of that many
+// tokens beyond (takes: the shape and alignment rules hold for such launches).
+bool gemv_mfma_takes(const LayerArgs& a, bool pk12);
+hipError_t launch_gemv_mfma_tokens(const LayerArgs& a, bool pk12, hipStream_t stream);
 // Several layers sharing x in one launch (each must pass gemv_mfma_ok); the
 // fits check is false when the layers need more fragments per workgroup than
 // the kernel takes (then launch them one by one).
