@@ -158,16 +158,17 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
     segs[nseg++] = {l.codebook, l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz, l.bias, l.y, (int)l.N, 0, 0, 0.f};
   }
   if (fast && nseg == 0) return HXQ_OK;
-  // the matrix-core GEMV from 5 to 64 tokens when every layer takes it (and,
-  // for u8 with bf16 x past 16 tokens, where the bf16 GEMM does not take it
-  // instead): one launch when the layers fit one workgroup per CU, else one
-  // launch per layer; the same kernel a single-layer call would run
+  // From 5 to 64 tokens the matrix-core GEMVs, with the kernel a single-layer
+  // call would pick for each layer (5 to 8 tokens: the 4x4-block GEMV where it
+  // takes the layer, else the 16x16 one; u8 with bf16 x past 16 tokens goes to
+  // the bf16 GEMM instead): one launch when every layer takes the same kernel
+  // and the group fits one workgroup per CU, one launch per layer when they
+  // take the same kernel but do not fit together, else the per-layer calls.
   const bool bf16_gemm = !pk12 && x_dtype == HXQ_BF16 && M > 16;
   if (K > 0 && M > 4 && M <= hxq::kGemvMfmaMaxM && !bf16_gemm) {
     hxq::GemvSeg gs[hxq::kMaxSegments];
-    int ng = 0;
-    bool mfma = true;
-    for (int i = 0; i < count && mfma; ++i) {
+    int ng = 0, n4 = 0, n16 = 0;
+    for (int i = 0; i < count; ++i) {
       const hxq_layer& l = layers[i];
       if (l.N == 0) continue;
       hxq::LayerArgs a = {};
@@ -178,14 +179,30 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
       a.M = (int)M;
       a.N = (int)l.N;
       a.K = (int)K;
-      mfma = hxq::gemv_fast_path_ok(a, pk12) && hxq::gemv_mfma_ok(a, pk12);
-      gs[ng++] = {static_cast<const float*>(l.codebook), l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz,
-                  l.bias, l.y, (int)l.N, 0};
+      gs[ng] = {static_cast<const float*>(l.codebook), l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz,
+                l.bias, l.y, (int)l.N, 0};
+      if (hxq::gemv_fast_path_ok(a, pk12)) {
+        if (M <= 8 && hxq::gemv_mfma4_ok(a, pk12) && hxq::gemv_mfma4_group_fits(&gs[ng], 1))
+          ++n4;
+        else if (hxq::gemv_mfma_ok(a, pk12))
+          ++n16;
+      }
+      ++ng;
     }
-    if (mfma && ng == 0) return HXQ_OK;
-    if (mfma) {
+    if (ng == 0) return HXQ_OK;
+    const bool xbf = x_dtype == HXQ_BF16;
+    if (n4 == ng) {
       (void)hipGetLastError();
-      const bool xbf = x_dtype == HXQ_BF16;
+      if (hxq::gemv_mfma4_group_fits(gs, ng))
+        return status_of(hxq::launch_gemv_mfma4_grouped(gs, ng, pk12, x, xbf, (int)M, (int)K, stream));
+      for (int i = 0; i < ng; ++i) {
+        const hipError_t err = hxq::launch_gemv_mfma4_grouped(&gs[i], 1, pk12, x, xbf, (int)M, (int)K, stream);
+        if (err != hipSuccess) return status_of(err);
+      }
+      return HXQ_OK;
+    }
+    if (n16 == ng) {
+      (void)hipGetLastError();
       if (hxq::gemv_mfma_group_fits(gs, ng))
         return status_of(hxq::launch_gemv_mfma_grouped(gs, ng, pk12, x, xbf, (int)M, (int)K, stream));
       for (int i = 0; i < ng; ++i) {
@@ -194,6 +211,7 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
       }
       return HXQ_OK;
     }
+    if (n4 + n16 > 0) fast = false;  // mixed kernels: the per-layer calls below
   }
   if (fast) {
     (void)hipGetLastError();

@@ -507,12 +507,18 @@ static hipError_t launch_valu_fmt(const LayerArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_gemv_valu(const LayerArgs& a, bool pk12, hipStream_t stream) {
-  // up to 4 tokens: the decode kernel; from 5 (or where it does not fit) to 64
-  // the matrix-core GEMV, past 64 in chunks of 64 tokens; where that kernel does
-  // not fit, token groups through the decode kernel, then the vector kernels
+  // up to 4 tokens: the decode kernel; 5 to 8 the 4x4-block matrix-core GEMV;
+  // then (or where those do not fit) the 16x16 matrix-core GEMV, past 64 tokens
+  // in launches of 64; where that does not fit either, token groups through
+  // the decode kernel, then the vector kernels
   DecodeSeg sg = {a.codebook, a.indices, a.sc_rows, a.sc_cols, a.sc_deltas, a.nnz, a.bias, a.y, a.N, 0, 0, 0.f};
   hipError_t err = hipSuccess;
   if (a.M <= 4 && launch_decode(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream, err)) return err;
+  if (a.M >= 5 && a.M <= 8 && gemv_mfma4_ok(a, pk12)) {
+    const GemvSeg gs = {static_cast<const float*>(a.codebook), a.indices, a.sc_rows, a.sc_cols, a.sc_deltas, a.nnz,
+                        a.bias, a.y, a.N, 0};
+    if (gemv_mfma4_group_fits(&gs, 1)) return launch_gemv_mfma4_grouped(&gs, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream);
+  }
   if (gemv_mfma_takes(a, pk12)) return launch_gemv_mfma_tokens(a, pk12, stream);
   if (a.M > 4 && a.M <= kChunkMaxM && launch_decode_chunked(&sg, 1, pk12, a.x, a.x_bf16, a.M, a.K, stream, err))
     return err;

@@ -88,6 +88,14 @@ struct GemvMArgs {
 };
 bool gemv_mfma_ok(const LayerArgs& a, bool pk12);
 hipError_t launch_gemv_mfma(const LayerArgs& a, bool pk12, hipStream_t stream);
+// Matrix-core GEMV on 4x4 fp32 blocks for up to 8 tokens (u8 or pk12,
+// K % 256 == 0, x 16-byte aligned): 4-row fragments, one workgroup per CU.
+// The group check is false when the layers need more than one workgroup per
+// CU at the kernel's fragment limit.
+bool gemv_mfma4_ok(const LayerArgs& a, bool pk12);
+bool gemv_mfma4_group_fits(const GemvSeg* segs, int nseg);
+hipError_t launch_gemv_mfma4_grouped(const GemvSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M,
+                                     int K, hipStream_t stream);
 // Any M >= 1: one launch up to kGemvMfmaMaxM tokens, launches of that many
 // tokens beyond (takes: the shape and alignment rules hold for such launches).
 bool gemv_mfma_takes(const LayerArgs& a, bool pk12);
