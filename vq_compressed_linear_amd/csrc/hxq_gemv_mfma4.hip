@@ -74,7 +74,7 @@ __device__ __forceinline__ float reduce_blocks(f32x4 v) {
 }
 
 // TG: groups of 4 tokens (1 up to 4 tokens, 2 up to 8); FG: fragments per
-// accumulator group (1, 2 or 4, no more than a workgroup owns); X1: K <= 2048,
+// accumulator group (1 to 4, no more than a workgroup owns); X1: K <= 2048,
 // so a wave has at most one chunk and loads its x once
 template <bool PK12, bool XBF, int TG, int FG, bool X1>
 __global__ __launch_bounds__(gm4::THREADS, 1) void gemv_mfma4(GemvMArgs ga) {
@@ -336,6 +336,17 @@ __global__ __launch_bounds__(gm4::THREADS, 1) void gemv_mfma4(GemvMArgs ga) {
   }
   if (t < T) step(std::integral_constant<int, 0>{}, t);
   if (t + 1 < T) step(std::integral_constant<int, 1>{}, t + 1);
+  // x at the first epilogue pass's sidecar columns, requested before the
+  // partial sums are added (its triplets arrived long ago)
+  float xv[MXR];
+  if (lo < hi && tid < SCAP) {
+#pragma unroll
+    for (int u = 0; u < MXR; ++u) {
+      const int tm = min(u, M - 1);
+      xv[u] = XBF ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(ga.x)[(int64_t)tm * K + tc] << 16)
+                  : static_cast<const float*>(ga.x)[(int64_t)tm * K + tc];
+    }
+  }
   __syncthreads();
 
   // ---- epilogue: thread o -> token o / (4 FMAX), block row o % (4 FMAX)
@@ -367,12 +378,13 @@ __global__ __launch_bounds__(gm4::THREADS, 1) void gemv_mfma4(GemvMArgs ga) {
         trp = a.sc_rows[ee > 0 ? ee - 1 : 0];
         trn = a.sc_rows[ee + 1 < a.nnz ? ee + 1 : ee];
       }
-      float xv[MXR];
+      if (e0 != lo) {
 #pragma unroll
-      for (int u = 0; u < MXR; ++u) {
-        const int tm = min(u, M - 1);
-        xv[u] = XBF ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(ga.x)[(int64_t)tm * K + tc] << 16)
-                    : static_cast<const float*>(ga.x)[(int64_t)tm * K + tc];
+        for (int u = 0; u < MXR; ++u) {
+          const int tm = min(u, M - 1);
+          xv[u] = XBF ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(ga.x)[(int64_t)tm * K + tc] << 16)
+                      : static_cast<const float*>(ga.x)[(int64_t)tm * K + tc];
+        }
       }
       if (tid < cnt) {
 #pragma unroll
@@ -480,6 +492,7 @@ template <bool PK12, bool XBF, int TG>
 static hipError_t launch_gemv_mfma4_f(const GemvMArgs& g, int fmax, int grid, hipStream_t stream) {
   if (fmax <= 1) return launch_gemv_mfma4_k<PK12, XBF, TG, 1>(g, grid, stream);
   if (fmax <= 2) return launch_gemv_mfma4_k<PK12, XBF, TG, 2>(g, grid, stream);
+  if (fmax <= 3) return launch_gemv_mfma4_k<PK12, XBF, TG, 3>(g, grid, stream);
   return launch_gemv_mfma4_k<PK12, XBF, TG, 4>(g, grid, stream);
 }
 
