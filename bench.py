@@ -125,8 +125,8 @@ class GroupCall:
 class LayerCall:
     """One pre-marshalled single-layer call."""
 
-    def __init__(self, L, B, d, y, x, M, N, K, stream):
-        self.fn = L.hxq_linear_fwd_u8
+    def __init__(self, L, B, d, y, x, M, N, K, stream, pk12=False):
+        self.fn = L.hxq_linear_fwd_pk12 if pk12 else L.hxq_linear_fwd_u8
         xdt = B.HXQ_BF16 if x.element_size() == 2 else B.HXQ_F32
         self.args = (d["codebook"].data_ptr(), d["indices"].data_ptr(), d["rows"].data_ptr(), d["cols"].data_ptr(),
                      d["deltas"].data_ptr(), d["rows"].numel(), x.data_ptr(), xdt, d["bias"].data_ptr(),
@@ -135,7 +135,7 @@ class LayerCall:
     def __call__(self):
         st = self.fn(*self.args)
         if st != 0:
-            raise RuntimeError("hxq_linear_fwd_u8 failed with status %d" % st)
+            raise RuntimeError("HelixLinear forward failed with status %d" % st)
 
 
 def hold_gpu(torch, ms):

@@ -37,10 +37,10 @@
  *   - Arithmetic: fp32 activations are multiplied in fp32 with fp32
  *     accumulation (vector FMAs up to 4 tokens, fp32 matrix-core products
  *     beyond, which are exact fp32 products summed in fp32); bf16 activations
- *     are upcast exactly and take the same fp32 path, except with M > 16 in
- *     the u8 format, which runs on bf16 matrix cores with fp32 accumulation,
- *     the codebook value (plus any sidecar delta at that position, added in
- *     fp32) rounded once to bf16.
+ *     are upcast exactly and take the same fp32 path, except with M > 16
+ *     (and K % 64 == 0 for pk12), which runs on bf16 matrix cores with fp32
+ *     accumulation, the codebook value (plus any sidecar delta at that
+ *     position, added in fp32) rounded once to bf16.
  *   - Errors are returned as a negative hxq_status before anything is
  *     launched; HXQ_ERR_HIP reports a failed launch.
  */
@@ -117,7 +117,8 @@ int hxq_sidecar_add(const int32_t* sc_rows, const int32_t* sc_cols,
  * hxq_linear_fwd_u8 / hxq_linear_fwd_pk12 would compute for it, within the
  * same tolerance (bitwise the same where the single-layer call would run the
  * same kernel); the layers normally run in a single launch (up to 64 tokens,
- * and for u8 with bf16 x at any M), otherwise one after another on `stream`.
+ * and with bf16 x at any M where K % 64 == 0), otherwise one after another on
+ * `stream`.
  *   fmt     HXQ_FMT_U8 or HXQ_FMT_PK12.
  *   layers  host array of `count` descriptors, 1 <= count <= HXQ_MAX_GROUP,
  *           read during the call only.  Each field means what the argument of
@@ -167,7 +168,7 @@ enum hxq_variant {
   HXQ_VARIANT_AUTO = 0,
   HXQ_VARIANT_GEMV_VALU = 1,  /* fp32 GEMV family: vector FMAs up to 4 tokens, fp32 matrix cores beyond */
   HXQ_VARIANT_GEMV_MFMA = 2,  /* fp32 matrix-core GEMV (16x16x4 fp32 MFMA) at any M; needs K % 64 == 0 */
-  HXQ_VARIANT_GEMM_BF16 = 3,  /* bf16 matrix-core GEMM (u8, bf16 x only) */
+  HXQ_VARIANT_GEMM_BF16 = 3,  /* bf16 matrix-core GEMM (bf16 x only; pk12 needs K % 64 == 0) */
   HXQ_VARIANT_GENERIC = 4     /* any shape or alignment, one wave per output row */
 };
 

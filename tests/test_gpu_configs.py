@@ -48,7 +48,7 @@ def _run_cfg(cfg, i, Ms, xdt, m_rows_for=None):
         y = G.run(lay, d, G.dev_x(x_np, xdt))
         rows = m_rows_for(M) if m_rows_for else None
         Y, B = G.oracle_fwd(lay, x_np, xdt, m_rows=rows)
-        tol = G.TOL_BF16 if (lay.fmt == "u8" and xdt == "bf16" and M > 16) else G.TOL_FP32
+        tol = G.TOL_BF16 if (xdt == "bf16" and M > 16) else G.TOL_FP32
         ratios[M] = G.check(y, Y, B, tol, "cfg%d %s M=%d" % (cfg, lay.name, M), m_rows=rows)
     return ratios
 

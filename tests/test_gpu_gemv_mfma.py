@@ -121,7 +121,7 @@ def test_gemv_mfma_chunks_past_64(fmt, x_dtype, M):
     lay = gen.random_layer(M + 7, N, K, fmt, nnz=N * K // 500, duplicates=True)
     d = G.dev_layer(lay)
     x_np = _x(M + 8, M, K, x_dtype)
-    y = G.run(lay, d, G.dev_x(x_np, x_dtype))
+    y = G.run(lay, d, G.dev_x(x_np, x_dtype), variant=hx.HXQ_VARIANT_GEMV_MFMA)
     Y, B = G.oracle_fwd(lay, x_np, x_dtype)
     G.check(y, Y, B, G.TOL_FP32, "gemv mfma chunks %s M=%d" % (fmt, M))
 

@@ -67,8 +67,10 @@ def test_pk12_gemv_valu(N, K, M):
 
 @pytest.mark.parametrize("M", [1, 16, 40])
 def test_pk12_bf16_x(M):
+    # up to 16 tokens the fp32 path, beyond it the bf16 matrix-core GEMM
     lay = gen.random_layer(4, 400, 1024, "pk12", nnz=300)
-    _case(lay, M, "bf16", hx.HXQ_VARIANT_AUTO, G.TOL_FP32, seed=M, what="pk12 bf16")
+    tol = G.TOL_BF16 if M > 16 else G.TOL_FP32
+    _case(lay, M, "bf16", hx.HXQ_VARIANT_AUTO, tol, seed=M, what="pk12 bf16")
 
 
 # ------------------------------------------------------------------ generic
@@ -92,6 +94,22 @@ def test_u8_gemm_bf16(N, K, M):
     G.say("u8 gemm N=%d K=%d M=%d" % (N, K, M))
     lay = gen.random_layer(N + K + 5, N, K, "u8", nnz=max(1, N * K // 1000), duplicates=True)
     _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=M, what="gemm")
+
+
+@pytest.mark.parametrize("N,K", [(1000, 2048), (300, 64), (2048, 4096 + 64), (11008, 2048)])
+@pytest.mark.parametrize("M", [17, 130, 300])
+def test_pk12_gemm_bf16(N, K, M):
+    # 2D pairs on the matrix cores: 12-byte index groups, the bf16 pair table
+    G.say("pk12 gemm N=%d K=%d M=%d" % (N, K, M))
+    lay = gen.random_layer(N + K + 9, N, K, "pk12", nnz=max(1, N * K // 2000), duplicates=True)
+    _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=M, what="pk12 gemm")
+
+
+@pytest.mark.parametrize("N,K,nnz,M", [(64, 1024, 8192, 150), (96, 33024, 3000, 130)])
+def test_pk12_gemm_sidecar_paths(N, K, nnz, M):
+    G.say("pk12 gemm sidecar paths N=%d K=%d nnz=%d" % (N, K, nnz))
+    lay = gen.random_layer(N + K + 1, N, K, "pk12", nnz=nnz, duplicates=True)
+    _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=M, what="pk12 gemm sidecar paths")
 
 
 @pytest.mark.parametrize("M", [1, 5, 16])
@@ -269,11 +287,12 @@ def test_one_hot_dequant_bit_exact(fmt, variant):
     _one_hot_case(fmt, variant, 260, 96, 200)
 
 
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
 @pytest.mark.parametrize("N,K,nnz", [(260, 128, 300), (40, 256, 6000)])
-def test_one_hot_gemm_k64(N, K, nnz):
+def test_one_hot_gemm_k64(fmt, N, K, nnz):
     """The same probe on the K % 64 == 0 matrix-core kernel: sidecar patches
     (few triplets) and the per-row walk (more triplets than the patch area)."""
-    _one_hot_case("u8", hx.HXQ_VARIANT_GEMM_BF16, N, K, nnz)
+    _one_hot_case(fmt, hx.HXQ_VARIANT_GEMM_BF16, N, K, nnz)
 
 
 def _one_hot_case(fmt, variant, N, K, nnz):

@@ -37,7 +37,7 @@ int validate_forward(const void* codebook, const uint8_t* indices, const int32_t
 
 int select(bool pk12, bool x_bf16, int64_t M, int64_t K, bool gemv_ok, bool gemm_ok) {
   if (K == 0) return HXQ_VARIANT_GENERIC;
-  if (!pk12 && x_bf16 && M > 16 && gemm_ok) return HXQ_VARIANT_GEMM_BF16;
+  if (x_bf16 && M > 16 && gemm_ok) return HXQ_VARIANT_GEMM_BF16;
   if (gemv_ok) return HXQ_VARIANT_GEMV_VALU;
   return HXQ_VARIANT_GENERIC;
 }
@@ -68,7 +68,7 @@ int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32
   a.N = (int)N;
   a.K = (int)K;
   const bool gemv_ok = K > 0 && hxq::gemv_fast_path_ok(a, pk12);
-  const bool gemm_ok = K > 0 && !pk12 && hxq::gemm_path_ok(a);
+  const bool gemm_ok = K > 0 && (pk12 ? hxq::gemm2_path_ok(a, true) : hxq::gemm_path_ok(a));
   int v = variant;
   if (v == HXQ_VARIANT_AUTO) v = select(pk12, a.x_bf16, M, K, gemv_ok, gemm_ok);
   (void)hipGetLastError();  // start from a clean error state
@@ -81,8 +81,8 @@ int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32
       return status_of(hxq::launch_gemv_mfma_tokens(a, pk12, stream));
     case HXQ_VARIANT_GEMM_BF16:
       if (!gemm_ok) return HXQ_ERR_UNSUPPORTED;
-      if (hxq::gemm2_path_ok(a)) return status_of(hxq::launch_gemm2_bf16(a, stream));
-      return status_of(hxq::launch_gemm_bf16(a, stream));
+      if (hxq::gemm2_path_ok(a, pk12)) return status_of(hxq::launch_gemm2_bf16(a, pk12, stream));
+      return status_of(hxq::launch_gemm_bf16(a, stream));  // u8 only (pk12 passed the check above)
     case HXQ_VARIANT_GENERIC:
       return status_of(hxq::launch_generic(a, pk12, stream));
     default:
@@ -164,7 +164,7 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
   // the bf16 GEMM instead): one launch when every layer takes the same kernel
   // and the group fits one workgroup per CU, one launch per layer when they
   // take the same kernel but do not fit together, else the per-layer calls.
-  const bool bf16_gemm = !pk12 && x_dtype == HXQ_BF16 && M > 16;
+  const bool bf16_gemm = x_dtype == HXQ_BF16 && M > 16;
   if (K > 0 && M > 4 && M <= hxq::kGemvMfmaMaxM && !bf16_gemm) {
     hxq::GemvSeg gs[hxq::kMaxSegments];
     int ng = 0, n4 = 0, n16 = 0;
@@ -223,7 +223,7 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
     if (done) return status_of(err);
   }
   // one matrix-core launch for bf16 x past the decode sizes when every layer takes it
-  if (!pk12 && x_dtype == HXQ_BF16 && M > 16 && K > 0) {
+  if (x_dtype == HXQ_BF16 && M > 16 && K > 0) {
     hxq::GemmSeg gs[hxq::kMaxSegments];
     int ng = 0;
     bool ok = true;
@@ -239,14 +239,14 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
       a.M = (int)M;
       a.N = (int)l.N;
       a.K = (int)K;
-      ok = hxq::gemm2_path_ok(a);
+      ok = hxq::gemm2_path_ok(a, pk12);
       gs[ng++] = {static_cast<const float*>(l.codebook), l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz,
                   l.bias, l.y, (int)l.N, 0};
     }
     if (ok && ng == 0) return HXQ_OK;
     if (ok) {
       (void)hipGetLastError();
-      return status_of(hxq::launch_gemm_grouped(gs, ng, x, (int)M, (int)K, stream));
+      return status_of(hxq::launch_gemm_grouped(gs, ng, pk12, x, (int)M, (int)K, stream));
     }
   }
   for (int i = 0; i < count; ++i) {
@@ -300,7 +300,7 @@ int hxq_select_variant(int fmt_pk12, int x_dtype, int64_t M, int64_t N, int64_t 
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return HXQ_ERR_SHAPE;
   if (fmt_pk12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
   const bool gemv_ok = K > 0 && K % 16 == 0;
-  const bool gemm_ok = !fmt_pk12 && x_dtype == HXQ_BF16 && K > 0 && K % 32 == 0;
+  const bool gemm_ok = x_dtype == HXQ_BF16 && K > 0 && K % (fmt_pk12 ? 64 : 32) == 0;
   return select(fmt_pk12 != 0, x_dtype == HXQ_BF16, M, K, gemv_ok, gemm_ok);
 }
 

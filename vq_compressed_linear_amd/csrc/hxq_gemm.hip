@@ -271,13 +271,18 @@ static_assert(MAXBINS % THREADS == 0, "bin prefix: whole bins per thread");
 static_assert(CAP <= ATILE, "head flags overlay an x tile");
 }  // namespace gemm3
 
-template <int FN>
-__global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(GemmArgs ga) {
+// PK12: 2D-VQ layers (HXQ whitepaper, "2D vector quantization"): 12-bit pair
+// indices, three bytes per two pairs, the 4096-pair codebook as bf16 pairs in
+// LDS (one gather gives the operand word of two k-adjacent weights)
+template <int FN, bool PK12>
+__global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_bf16(GemmArgs ga) {
   using namespace gemm3;
   constexpr int BN = 16 * WAVES * FN;
   typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
   typedef u32x8 vecB[FN];  // operands of one stage: fragment j, words 0-3 sub-step 0, 4-7 sub-step 1
-  __shared__ __align__(16) unsigned char cbs[256 * 256];  // 64 copies per entry, bf16 in the upper half
+  // u8: 64 copies per entry, bf16 in the upper half; pk12: entry e at byte 4 e,
+  // bf16 of component 0 (even k) in the low half, component 1 in the high half
+  __shared__ __align__(16) unsigned char cbs[PK12 ? 4096 * 4 : 256 * 256];
   extern __shared__ __align__(16) unsigned char smem[];
   float* cbf = reinterpret_cast<float*>(smem + OFF_CBF);
   int* bins = reinterpret_cast<int*>(smem + OFF_BINS);  // bin b spans patch[bins[b] .. bins[b + 1])
@@ -333,9 +338,12 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(GemmArgs ga) 
     xst[i] = ((r >> 4) * 2 + (c & 1)) * 1024 + (((c >> 1) * 16 + ((r & 15) ^ c)) << 4);
   }
   // index bytes of fragment j: output n0 + nw + 16 j + l16, k = 16 g .. 16 g + 15 of the stage
+  // (u8: 16 bytes; pk12: 12 bytes, the 8 pairs (k, k + 1) of those 16 k)
+  constexpr int IB = PK12 ? 12 : 16;
+  const int64_t row_bytes = PK12 ? (int64_t)(K / 4) * 3 : (int64_t)K;
   const uint8_t* irow[FN];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) irow[j] = a.indices + (int64_t)min(n0 + nw + 16 * j + l16, N - 1) * K + 16 * g;
+  for (int j = 0; j < FN; ++j) irow[j] = a.indices + (int64_t)min(n0 + nw + 16 * j + l16, N - 1) * row_bytes + IB * g;
   // A operand of token block i, sub-step u: block 2 i + u
   const int aoff0 = (g * 16 + (l16 ^ (2 * g))) * 16, aoff1 = 1024 + (g * 16 + (l16 ^ (2 * g + 1))) * 16;
 
@@ -350,18 +358,35 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(GemmArgs ga) 
 #pragma unroll
     for (int i = 0; i < XPT; ++i) *reinterpret_cast<u32x4*>(t + xst[i]) = d[i];
   };
+  typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
   auto load_iq = [&](int st, u32x4* d) {
-    const int kn = min(st, nk - 1) * BK;
+    const int kn = min(st, nk - 1) * (BK / 16 * IB);  // index bytes per stage and row
 #pragma unroll
-    for (int j = 0; j < FN; ++j) d[j] = *reinterpret_cast<const u32x4*>(irow[j] + kn);
+    for (int j = 0; j < FN; ++j) {
+      if (PK12) {
+        const u32x3 v = *reinterpret_cast<const u32x3*>(irow[j] + kn);
+        d[j] = u32x4{v[0], v[1], v[2], 0u};
+      } else {
+        d[j] = *reinterpret_cast<const u32x4*>(irow[j] + kn);
+      }
+    }
   };
   load_x(0, XA);
   load_x(1, XB);
   load_iq(0, IQ);
 
-  // ---- codebook: threads t and t + 256 stage half of entry t's 64 bf16
-  // copies each (pieces rotated against bank conflicts); fp32 values too
-  {
+  // ---- codebook.  u8: threads t and t + 256 stage half of entry t's 64 bf16
+  // copies each (pieces rotated against bank conflicts); fp32 values too.
+  // pk12: thread t packs pairs t, t + 512, ... (each component rounded to
+  // nearest even on its own)
+  if (PK12) {
+#pragma unroll
+    for (int i = 0; i < 4096 / THREADS; ++i) {
+      const int e = tid + THREADS * i;
+      const float2 c = reinterpret_cast<const float2*>(a.codebook)[e];
+      reinterpret_cast<uint32_t*>(cbs)[e] = f32_to_bf16_rne(c.x) | (f32_to_bf16_rne(c.y) << 16);
+    }
+  } else {
     const int e = tid & 255, h = tid >> 8;
     const float cv = static_cast<const float*>(a.codebook)[e];
     const float vb = __uint_as_float(f32_to_bf16_rne(cv) << 16);
@@ -411,7 +436,13 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(GemmArgs ga) 
     for (int q = 0; q < QMAX; ++q) {
       const int64_t e = lo + tid + (int64_t)THREADS * q;
       head[q] = e < hi && (e == lo || pr[q] != tr[q] || pc[q] != tc[q]);
-      tb[q] = a.indices[(int64_t)tr[q] * K + tc[q]];
+      if (PK12) {
+        // the 24-bit group holding the pair of column tc (the pair is tc / 2)
+        const uint8_t* pb = a.indices + (int64_t)tr[q] * row_bytes + (tc[q] >> 2) * 3;
+        tb[q] = (uint32_t)pb[0] | ((uint32_t)pb[1] << 8) | ((uint32_t)pb[2] << 16);
+      } else {
+        tb[q] = a.indices[(int64_t)tr[q] * K + tc[q]];
+      }
       if (e < hi) hflag[e - lo] = head[q] ? 1 : 0;
       if (head[q]) atomicAdd(&bins[1 + (tc[q] / BK) * WAVES + (tr[q] - n0) / (16 * FN)], 1);
     }
@@ -448,7 +479,13 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(GemmArgs ga) 
     for (int q = 0; q < QMAX; ++q) {
       if (!head[q]) continue;
       const int64_t e = lo + tid + (int64_t)THREADS * q;
-      float v = cbf[tb[q]] + td[q];
+      float v = td[q];
+      if (PK12) {
+        const uint32_t pi = ((tc[q] >> 1) & 1) ? (tb[q] >> 12) : (tb[q] & 0xfffu);
+        v += static_cast<const float*>(a.codebook)[2 * pi + (tc[q] & 1)];
+      } else {
+        v += cbf[tb[q]];
+      }
       for (int64_t e2 = e + 1; e2 < hi && !hflag[e2 - lo]; ++e2) v += a.sc_deltas[e2];
       // patch word: lane (bits 0-5), column in the lane's 16 (bits 6-9), fragment (10-11), bf16 (16-31)
       const int rl = tr[q] - n0, cl = tc[q] % BK;
@@ -477,12 +514,23 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(GemmArgs ga) 
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // operands of one stage from its index bytes: 16 gathers and 8 packs per fragment
+  // operands of one stage from its index bytes: u8 16 gathers and 8 packs per
+  // fragment; pk12 8 gathers (24-bit group d holds pairs 2 d, 2 d + 1 as
+  // v & 0xfff, v >> 12; operand word e is the pair of k = 2 e, 2 e + 1)
   auto build = [&](const u32x4* iq, vecB& out) {
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
+        if (PK12) {
+          const uint32_t v = d == 0 ? (iq[j][0] & 0xffffffu)
+                           : d == 1 ? (__builtin_amdgcn_alignbit(iq[j][1], iq[j][0], 24) & 0xffffffu)
+                           : d == 2 ? (__builtin_amdgcn_alignbit(iq[j][2], iq[j][1], 16) & 0xffffffu)
+                                    : (iq[j][2] >> 8);
+          out[j][2 * d] = lds_load<uint32_t>((v & 0xfffu) << 2, cbs);
+          out[j][2 * d + 1] = lds_load<uint32_t>((v >> 12) << 2, cbs);
+          continue;
+        }
         const uint32_t wd = iq[j][d];
         const uint32_t f0 = lds_load<uint32_t>(byte_addr256<0>(wd, lane4), cbs);
         const uint32_t f1 = lds_load<uint32_t>(byte_addr256<1>(wd, lane4), cbs);
@@ -546,8 +594,20 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(GemmArgs ga) 
         const int c = snc[j];
         if (c >= c0) {
           const int p = c - c0;
-          const uint32_t word = iq[j][p >> 2];
-          float val = cbf[(word >> ((p & 3) * 8)) & 0xffu] + a.sc_deltas[scur[j]];
+          float val = a.sc_deltas[scur[j]];
+          if (PK12) {
+            // pair p / 2 of the lane's 8: group p / 4 of the 12 bytes
+            const int d = p >> 2;
+            const uint32_t v = d == 0 ? (iq[j][0] & 0xffffffu)
+                             : d == 1 ? (__builtin_amdgcn_alignbit(iq[j][1], iq[j][0], 24) & 0xffffffu)
+                             : d == 2 ? (__builtin_amdgcn_alignbit(iq[j][2], iq[j][1], 16) & 0xffffffu)
+                                      : (iq[j][2] >> 8);
+            const uint32_t pi = ((p >> 1) & 1) ? (v >> 12) : (v & 0xfffu);
+            val += static_cast<const float*>(a.codebook)[2 * pi + (p & 1)];
+          } else {
+            const uint32_t word = iq[j][p >> 2];
+            val += cbf[(word >> ((p & 3) * 8)) & 0xffu];
+          }
           while (scur[j] + 1 < send[j] && a.sc_cols[scur[j] + 1] == c) {
             ++scur[j];
             val += a.sc_deltas[scur[j]];
@@ -669,10 +729,10 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_u8_bf16(GemmArgs ga) 
   }
 }
 
-template <int FN>
+template <int FN, bool PK12>
 static hipError_t launch_gemm3(GemmArgs& ga, hipStream_t stream) {
   using namespace gemm3;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm3_u8_bf16<FN>),
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm3_bf16<FN, PK12>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS_DYN);
   if (attr != hipSuccess) return attr;
   int64_t tiles = 0;
@@ -681,19 +741,25 @@ static hipError_t launch_gemm3(GemmArgs& ga, hipStream_t stream) {
     tiles += (int64_t)ga.tiles_m * ((ga.seg[i].N + 16 * WAVES * FN - 1) / (16 * WAVES * FN));
     if (tiles > INT_MAX) return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((gemm3_u8_bf16<FN>), dim3((unsigned)tiles), dim3(THREADS), LDS_DYN, stream, ga);
+  hipLaunchKernelGGL((gemm3_bf16<FN, PK12>), dim3((unsigned)tiles), dim3(THREADS), LDS_DYN, stream, ga);
   return hipGetLastError();
 }
 
-bool gemm2_path_ok(const LayerArgs& a) {
-  if (!gemm_path_ok(a) || a.K % gemm3::BK != 0 || a.K < gemm3::BK) return false;
+bool gemm2_path_ok(const LayerArgs& a, bool pk12) {
+  if (!a.x_bf16 || a.K % gemm3::BK != 0 || a.K < gemm3::BK) return false;
+  if (reinterpret_cast<uintptr_t>(a.indices) % (pk12 ? 4 : 16) != 0) return false;
+  if (pk12 && reinterpret_cast<uintptr_t>(a.codebook) % 8 != 0) return false;
+  if (reinterpret_cast<uintptr_t>(a.x) % 16 != 0) return false;
+  const int64_t tiles = (((int64_t)a.M + gemm3::BM - 1) / gemm3::BM) * (((int64_t)a.N + 127) / 128);
+  if (tiles > INT_MAX) return false;
   // x offsets are 32-bit
   return (int64_t)a.M * a.K * 2 < ((int64_t)1 << 32);
 }
 
 // Output tile width by how many tiles the launch has: 256 outputs when that
 // still gives every CU a tile, else 128.
-hipError_t launch_gemm_grouped(const GemmSeg* segs, int nseg, const void* x, int M, int K, hipStream_t stream) {
+hipError_t launch_gemm_grouped(const GemmSeg* segs, int nseg, bool pk12, const void* x, int M, int K,
+                               hipStream_t stream) {
   if (nseg < 1 || nseg > kMaxSegments) return hipErrorInvalidValue;
   GemmArgs ga;
   ga.x = x;
@@ -707,14 +773,14 @@ hipError_t launch_gemm_grouped(const GemmSeg* segs, int nseg, const void* x, int
     wide += (int64_t)ga.tiles_m * ((segs[i].N + 255) / 256);
   }
   for (int i = nseg; i < kMaxSegments; ++i) ga.seg[i] = segs[0];
-  if (wide >= device_cu_count()) return launch_gemm3<2>(ga, stream);
-  return launch_gemm3<1>(ga, stream);
+  if (pk12) return wide >= device_cu_count() ? launch_gemm3<2, true>(ga, stream) : launch_gemm3<1, true>(ga, stream);
+  return wide >= device_cu_count() ? launch_gemm3<2, false>(ga, stream) : launch_gemm3<1, false>(ga, stream);
 }
 
-hipError_t launch_gemm2_bf16(const LayerArgs& a, hipStream_t stream) {
+hipError_t launch_gemm2_bf16(const LayerArgs& a, bool pk12, hipStream_t stream) {
   const GemmSeg sg = {static_cast<const float*>(a.codebook), a.indices, a.sc_rows, a.sc_cols, a.sc_deltas,
                       a.nnz, a.bias, a.y, a.N, 0};
-  return launch_gemm_grouped(&sg, 1, a.x, a.M, a.K, stream);
+  return launch_gemm_grouped(&sg, 1, pk12, a.x, a.M, a.K, stream);
 }
 
 }  // namespace hxq

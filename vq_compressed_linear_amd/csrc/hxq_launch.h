@@ -120,13 +120,13 @@ hipError_t launch_generic(const LayerArgs& a, bool pk12, hipStream_t stream);
 // aligned index and x rows.
 hipError_t launch_gemm_bf16(const LayerArgs& a, hipStream_t stream);
 bool gemm_path_ok(const LayerArgs& a);
-// The same product with per-wave weight operands built in registers; needs
-// K % 64 == 0 as well.
-hipError_t launch_gemm2_bf16(const LayerArgs& a, hipStream_t stream);
-bool gemm2_path_ok(const LayerArgs& a);
+// The same product with per-wave weight operands built in registers, u8 or
+// pk12; needs K % 64 == 0, index rows 16-byte (u8) or 4-byte (pk12) aligned.
+hipError_t launch_gemm2_bf16(const LayerArgs& a, bool pk12, hipStream_t stream);
+bool gemm2_path_ok(const LayerArgs& a, bool pk12);
 
-// Several u8 layers sharing bf16 x in one launch of that kernel (each must
-// pass gemm2_path_ok); tile0 is filled in by the launcher.
+// Several layers of one format sharing bf16 x in one launch of that kernel
+// (each must pass gemm2_path_ok); tile0 is filled in by the launcher.
 struct GemmSeg {
   const float* codebook;
   const uint8_t* indices;
@@ -146,7 +146,8 @@ struct GemmArgs {
   int nseg;
   GemmSeg seg[kMaxSegments];
 };
-hipError_t launch_gemm_grouped(const GemmSeg* segs, int nseg, const void* x, int M, int K, hipStream_t stream);
+hipError_t launch_gemm_grouped(const GemmSeg* segs, int nseg, bool pk12, const void* x, int M, int K,
+                               hipStream_t stream);
 
 // y += S x.
 hipError_t launch_sidecar_add(const LayerArgs& a, hipStream_t stream);
