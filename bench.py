@@ -15,7 +15,7 @@ value: algorithmic GB/s of the step (the compressed bytes the method must
 move: indices, codebooks, sidecar triplets, x once per launch, bias, y) over
 the GPU time of the timed steps.  Also reported: the same step issued as seven
 single-layer calls, the M = 8 step, the bf16 prefill GEMM at M = 2048
-(TFLOP/s), the read bandwidth of a plain streaming kernel over the same
+(TFLOP/s; u8 layer set and two pk12 layers), the read bandwidth of a plain streaming kernel over the same
 rotated buffers, the roofline of the dominant launch (gate|up) and the CPU
 oracle baseline.
 
@@ -230,6 +230,31 @@ def stream_ceiling(torch, L, sets, steps):
                 avg_us=round(avg * 1e3, 3), gbs=round(nbytes / (avg * 1e-3) / 1e9, 1))
 
 
+def prefill_pk12(torch, L, B, stream, M, steps):
+    """The bf16 matrix-core GEMM on 2D-VQ (pk12) layers of the pk12
+    configuration's shapes (seeded random pair indices and codebook, 0.05%
+    sidecar: the kernel's speed does not depend on how the codebook was fit),
+    one single-layer call per layer at M tokens of bf16 x."""
+    import numpy as np
+
+    from hxq_synth import gen
+
+    rows = []
+    for i, (name, N, K) in enumerate(gen.CONFIGS[3]["layers"]):
+        lay = gen.random_layer(9000 + i, N, K, "pk12", nnz=N * K // 2000)
+        d = to_dev(lay, torch)
+        xf = gen.synth_x(3, i, M, K)
+        x = torch.from_numpy(gen.to_bf16_bits(xf).view(np.int16)).cuda().view(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        call = LayerCall(L, B, d, y, x, M, N, K, stream, pk12=True)
+        t = time_steps(torch, [[call]], steps, 1) / steps
+        rows.append(dict(layer=name, N=N, K=K, avg_us=round(t * 1e3, 2),
+                         tflops=round(2.0 * M * N * K / (t * 1e-3) / 1e12, 1)))
+        del d, x, y
+    return dict(workload="2D-VQ (pk12) gate/down-shaped layers (11008x2048, 2048x11008), prefill M=%d, "
+                         "bf16 x, one call per layer" % M, M=M, layers=rows)
+
+
 def cpu_baseline(layers, M, budget_s=15.0):
     """The CPU oracle over the same layer set, as many whole steps as fit in
     about `budget_s` seconds (at least one)."""
@@ -389,6 +414,9 @@ def main(argv=None):
         log("prefill M=2048 step %.1f us, %.1f TFLOP/s" % (total_p / steps * 1e3, tfs))
         del sp
         torch.cuda.empty_cache()
+        extras["prefill_pk12"] = prefill_pk12(torch, L, B, stream, M, steps)
+        log("pk12 prefill M=2048: %s" % ", ".join("%s %.1f us" % (r["layer"], r["avg_us"])
+                                                  for r in extras["prefill_pk12"]["layers"]))
 
     out = {
         "metric": "HelixLinear decode GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak)",
