@@ -101,11 +101,14 @@ def test_sidecar_add_rejects(L):
 
 def test_variant_selection(L):
     sel = L.hxq_select_variant
-    # u8: bf16 x with M > 16 goes to the matrix-core GEMM, everything else to a GEMV
+    # bf16 x with M > 16 goes to the matrix-core GEMM (pk12: K % 64 == 0), everything else to a GEMV
     assert sel(0, B.HXQ_BF16, 2048, 11008, 2048) == B.HXQ_VARIANT_GEMM_BF16
     assert sel(0, B.HXQ_BF16, 16, 11008, 2048) != B.HXQ_VARIANT_GEMM_BF16
     assert sel(0, B.HXQ_F32, 64, 8512, 2048) != B.HXQ_VARIANT_GEMM_BF16
-    assert sel(1, B.HXQ_BF16, 2048, 11008, 2048) != B.HXQ_VARIANT_GEMM_BF16
+    assert sel(1, B.HXQ_BF16, 2048, 11008, 2048) == B.HXQ_VARIANT_GEMM_BF16
+    assert sel(1, B.HXQ_BF16, 2048, 11008, 96) != B.HXQ_VARIANT_GEMM_BF16
+    assert sel(0, B.HXQ_BF16, 2048, 11008, 96) == B.HXQ_VARIANT_GEMM_BF16
+    assert sel(1, B.HXQ_F32, 2048, 11008, 2048) != B.HXQ_VARIANT_GEMM_BF16
     # shapes the fast kernels do not take go to the generic kernel
     assert sel(0, B.HXQ_F32, 1, 100, 100) == B.HXQ_VARIANT_GENERIC
     assert sel(1, B.HXQ_F32, 1, 100, 6) == B.HXQ_VARIANT_GENERIC
