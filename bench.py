@@ -255,6 +255,54 @@ def prefill_pk12(torch, L, B, stream, M, steps):
                          "bf16 x, one call per layer" % M, M=M, layers=rows)
 
 
+def buffered_baseline(torch, L, B, layers, stream, M, steps, fused_step_us):
+    """The buffered design the pages describe, for comparison only (the
+    library never forms the weight): per layer, the dense bf16 weight into
+    one shared buffer sized to the largest layer (hxq_dequant_bf16), then the
+    library bf16 matmul (torch.mm, hipBLASLt), bias added; bf16 x at M tokens."""
+    import numpy as np
+
+    from hxq_synth import gen
+
+    devs = [to_dev(l, torch) for l in layers]
+    big = max(l.N * l.K for l in layers)
+    wbuf = torch.empty(big, dtype=torch.bfloat16, device="cuda")
+    xs = [torch.from_numpy(gen.to_bf16_bits(gen.synth_x(4, i, M, l.K)).view(np.int16)).cuda().view(torch.bfloat16)
+          for i, l in enumerate(layers)]
+    deq_args = []
+    for d, l in zip(devs, layers):
+        deq_args.append((B.HXQ_FMT_U8, d["codebook"].data_ptr(), d["indices"].data_ptr(), d["rows"].data_ptr(),
+                         d["cols"].data_ptr(), d["deltas"].data_ptr(), d["rows"].numel(), wbuf.data_ptr(), l.N, l.K,
+                         stream))
+    biases = [d["bias"].to(torch.bfloat16) for d in devs]
+
+    def deq(i):
+        def f():
+            st = L.hxq_dequant_bf16(*deq_args[i])
+            if st != 0:
+                raise RuntimeError("hxq_dequant_bf16 failed with status %d" % st)
+        return f
+
+    def mm(i):
+        w = wbuf[: layers[i].N * layers[i].K].view(layers[i].N, layers[i].K)
+
+        def f():
+            torch.addmm(biases[i], xs[i], w.t())
+        return f
+
+    per = []
+    for i, l in enumerate(layers):
+        td = time_steps(torch, [[deq(i)]], steps, 1) / steps
+        tm = time_steps(torch, [[mm(i)]], steps, 1) / steps
+        per.append(dict(layer=l.name, dequant_us=round(td * 1e3, 2), matmul_us=round(tm * 1e3, 2)))
+    step = time_steps(torch, [[f for i in range(len(layers)) for f in (deq(i), mm(i))]], steps, 1) / steps
+    flops = sum(2.0 * M * l.N * l.K for l in layers)
+    return dict(workload="the same u8 layer set at M=%d, bf16 x: per layer the bf16 weight into one shared buffer, "
+                         "then torch.addmm (hipBLASLt, bf16 output)" % M,
+                step_us=round(step * 1e3, 2), tflops=round(flops / (step * 1e-3) / 1e12, 1),
+                fused_step_us=fused_step_us, layers=per)
+
+
 def cpu_baseline(layers, M, budget_s=15.0):
     """The CPU oracle over the same layer set, as many whole steps as fit in
     about `budget_s` seconds (at least one)."""
@@ -415,6 +463,10 @@ def main(argv=None):
         del sp
         torch.cuda.empty_cache()
         extras["prefill_pk12"] = prefill_pk12(torch, L, B, stream, M, steps)
+        extras["buffered_baseline"] = buffered_baseline(torch, L, B, layers, stream, M, steps,
+                                                        extras["prefill"]["step_us"])
+        log("buffered (dequant + library matmul) M=2048 step %.1f us"
+            % extras["buffered_baseline"]["step_us"])
         log("pk12 prefill M=2048: %s" % ", ".join("%s %.1f us" % (r["layer"], r["avg_us"])
                                                   for r in extras["prefill_pk12"]["layers"]))
 

@@ -150,8 +150,9 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count,
 
 /* Measurement helper, not part of the forward pass: reads `bytes` bytes of
  * device memory at `src` once, with the decode kernels' grid shape (one
- * 512-thread workgroup per CU, 16-byte loads, each wave a contiguous stretch),
- * and writes one 32-bit digest of what it read per workgroup into `sink`
+ * 512-thread workgroup per CU, 16-byte loads, the whole grid sweeping the
+ * buffer in order, four loads in flight per thread), and writes a 32-bit
+ * digest of what it read per workgroup into `sink`
  * (device memory, `sink_words` entries; the launch uses at most that many
  * workgroups).  Its duration is the attainable read bandwidth that the decode
  * GEMV's HBM fraction is compared against.
@@ -160,6 +161,27 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count,
  * 16-byte aligned or sink not 4-byte aligned. */
 int hxq_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words,
                     hipStream_t stream);
+
+/* Measurement helper, not part of the forward pass: the dense bf16 weight of
+ * one layer, for timing the buffered design the HXQ whitepaper's inference
+ * paragraph describes (gather the weight into a shared bf16 buffer, then a
+ * library matmul) against the fused kernels, which never form it.
+ *   w[n][k] = bf16(C[idx[n][k]] + the sidecar deltas at (n, k)), the deltas
+ *   added in fp32 in stored order and the sum rounded once to nearest even
+ *   (the value the bf16 matrix-core GEMM uses).
+ *   fmt      HXQ_FMT_U8 or HXQ_FMT_PK12; codebook, indices and sidecar as for
+ *            the forward entry points (sidecar sorted by (row, col)).
+ *   w        [N][K] bf16 bit patterns, caller-owned device memory, 16-byte
+ *            aligned, overwritten.
+ * Work is two launches on `stream`.  Errors: HXQ_ERR_SHAPE for an unknown fmt,
+ * negative or oversized N, K, nnz, or odd K with pk12; HXQ_ERR_NULL;
+ * HXQ_ERR_ALIGN (indices 16-byte (u8) or 4-byte (pk12), codebook 4 / 8-byte,
+ * w 16-byte, sidecar 4-byte); HXQ_ERR_UNSUPPORTED if K % 16 != 0; N == 0 or
+ * K == 0 is a no-op. */
+int hxq_dequant_bf16(int fmt, const float* codebook, const uint8_t* indices,
+                     const int32_t* sc_rows, const int32_t* sc_cols,
+                     const float* sc_deltas, int64_t nnz, uint16_t* w,
+                     int64_t N, int64_t K, hipStream_t stream);
 
 /* Kernel selection, for tests and measurement.  HXQ_VARIANT_AUTO is what the
  * entry points above use; the others force one kernel family and return

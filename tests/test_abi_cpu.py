@@ -188,3 +188,28 @@ def test_stream_read_rejects(L):
     assert f(FAKE + 4, 16, FAKE, 4, None) == B.HXQ_ERR_ALIGN
     assert f(FAKE, 16, FAKE + 2, 4, None) == B.HXQ_ERR_ALIGN
     assert f(None, 0, None, 4, None) == B.HXQ_OK
+
+
+def test_dequant_rejects(L):
+    f = L.hxq_dequant_bf16
+    U8, PK = B.HXQ_FMT_U8, B.HXQ_FMT_PK12
+
+    def call(fmt=U8, cb=FAKE, idx=FAKE, r=FAKE, c=FAKE, d=FAKE, nnz=0, w=FAKE, N=4, K=32):
+        return f(fmt, cb, idx, r, c, d, nnz, w, N, K, None)
+
+    assert call(fmt=7) == B.HXQ_ERR_SHAPE
+    assert call(N=-1) == B.HXQ_ERR_SHAPE
+    assert call(K=-16) == B.HXQ_ERR_SHAPE
+    assert call(nnz=-1) == B.HXQ_ERR_SHAPE
+    assert call(fmt=PK, K=33) == B.HXQ_ERR_SHAPE
+    assert call(w=None) == B.HXQ_ERR_NULL
+    assert call(idx=None) == B.HXQ_ERR_NULL
+    assert call(nnz=2, r=None) == B.HXQ_ERR_NULL
+    assert call(idx=FAKE + 4) == B.HXQ_ERR_ALIGN
+    assert call(fmt=PK, idx=FAKE + 2) == B.HXQ_ERR_ALIGN
+    assert call(fmt=PK, cb=FAKE + 4) == B.HXQ_ERR_ALIGN
+    assert call(w=FAKE + 8) == B.HXQ_ERR_ALIGN
+    assert call(K=24) == B.HXQ_ERR_UNSUPPORTED
+    # empty weights launch nothing
+    assert call(N=0, cb=None, idx=None, w=None) == B.HXQ_OK
+    assert call(K=0, cb=None, idx=None, w=None) == B.HXQ_OK

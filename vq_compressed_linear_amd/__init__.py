@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     VARIANT_NAMES,
     HxqError,
     HxqLayer,
+    hxq_dequant_bf16,
     hxq_linear_fwd_grouped,
     hxq_linear_fwd_pk12,
     hxq_linear_fwd_u8,

@@ -77,6 +77,7 @@ SIGNATURES = {
     "hxq_sidecar_add": (_INT, [_P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P]),
     "hxq_linear_fwd_grouped": (_INT, [_INT, ctypes.POINTER(HxqLayer), _INT, _P, _INT, _I64, _I64, _P]),
     "hxq_stream_read": (_INT, [_P, _I64, _P, _INT, _P]),
+    "hxq_dequant_bf16": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _I64, _I64, _P]),
     "hxq_select_variant": (_INT, [_INT, _INT, _I64, _I64, _I64]),
     "hxq_status_str": (ctypes.c_char_p, [_INT]),
     "hxq_version": (_INT, []),
@@ -218,6 +219,28 @@ def hxq_sidecar_add(sc_rows, sc_cols, sc_deltas, x, y, stream=None) -> None:
                                _x_dtype(x), _ptr(y), M, N, K, _stream(stream))
     if st != HXQ_OK:
         raise HxqError(st, "hxq_sidecar_add")
+
+
+def hxq_dequant_bf16(fmt: int, codebook, indices, sc_rows, sc_cols, sc_deltas, w, stream=None) -> None:
+    """w <- bf16(C[indices] + S) on the device: the dense weight, for timing
+    the buffered design only (the forward entry points never form it).  w is
+    a contiguous [N, K] bfloat16 (or int16 / uint16 bit pattern) tensor."""
+    torch = _torch()
+    if w.dim() != 2 or w.element_size() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [N, K] tensor of 16-bit elements")
+    N, K = w.shape
+    if indices.dtype != torch.uint8 or indices.dim() != 2 or not indices.is_contiguous() or indices.shape[0] != N:
+        raise ValueError("indices must be a contiguous uint8 [N, row bytes] tensor")
+    row = K if fmt == HXQ_FMT_U8 else 3 * ((K + 3) // 4)
+    if indices.shape[1] != row:
+        raise ValueError("index rows hold %d bytes, expected %d" % (indices.shape[1], row))
+    if codebook.dtype != torch.float32 or codebook.numel() != (256 if fmt == HXQ_FMT_U8 else 8192):
+        raise ValueError("wrong codebook size or dtype")
+    nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
+    st = lib().hxq_dequant_bf16(fmt, _ptr(codebook), _ptr(indices), _ptr(sc_rows), _ptr(sc_cols),
+                                _ptr(sc_deltas), nnz, _ptr(w), N, K, _stream(stream))
+    if st != HXQ_OK:
+        raise HxqError(st, "hxq_dequant_bf16")
 
 
 def grouped_layers(fmt: int, layers, M: int, K: int):

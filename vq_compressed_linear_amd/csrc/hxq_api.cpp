@@ -267,6 +267,25 @@ int hxq_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_wor
   return status_of(hxq::launch_stream_read(src, bytes, sink, sink_words, stream));
 }
 
+int hxq_dequant_bf16(int fmt, const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
+                     const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, uint16_t* w, int64_t N,
+                     int64_t K, hipStream_t stream) {
+  if (fmt != HXQ_FMT_U8 && fmt != HXQ_FMT_PK12) return HXQ_ERR_SHAPE;
+  const bool pk12 = fmt == HXQ_FMT_PK12;
+  if (N < 0 || K < 0 || nnz < 0 || N > kMaxDim || K > kMaxDim || nnz > kMaxDim) return HXQ_ERR_SHAPE;
+  if (pk12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
+  if (N == 0 || K == 0) return HXQ_OK;
+  if (!codebook || !indices || !w) return HXQ_ERR_NULL;
+  if (nnz > 0 && (!sc_rows || !sc_cols || !sc_deltas)) return HXQ_ERR_NULL;
+  if (misaligned(indices, pk12 ? 4 : 16) || misaligned(codebook, pk12 ? 8 : 4) || misaligned(w, 16) ||
+      misaligned(sc_rows, 4) || misaligned(sc_cols, 4) || misaligned(sc_deltas, 4))
+    return HXQ_ERR_ALIGN;
+  if (K % 16 != 0) return HXQ_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return status_of(hxq::launch_dequant_bf16(pk12, codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, w, N, K,
+                                            stream));
+}
+
 int hxq_sidecar_add(const int32_t* sc_rows, const int32_t* sc_cols, const float* sc_deltas,
                     int64_t nnz, const void* x, int x_dtype, float* y, int64_t M, int64_t N,
                     int64_t K, hipStream_t stream) {

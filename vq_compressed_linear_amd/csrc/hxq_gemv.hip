@@ -567,21 +567,23 @@ namespace hxq {
 
 __global__ __launch_bounds__(512) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                            uint32_t* __restrict__ sink) {
-  constexpr int P = 8;
+  // the grid sweeps the buffer in order: each round every thread requests P
+  // pieces, round r of the grid covering one contiguous window of
+  // P * threads pieces (faster than one stretch per wave: the requests in
+  // flight stay close together)
+  constexpr int P = 4;
   const int lane = threadIdx.x & 63;
-  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t per = (n16 + waves - 1) / waves;  // 16-byte pieces per wave
-  const int64_t b = w * per, e = b + per < n16 ? b + per : n16;
+  const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   uint32_t acc = 0;
-  for (int64_t i0 = b; i0 < e; i0 += (int64_t)P * kWave) {
+  for (int64_t i0 = 0; i0 < n16; i0 += P * nthr) {
     u32x4 v[P];
     uint32_t keep[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int64_t i = i0 + p * kWave + lane;
-      keep[p] = i < e ? 0xffffffffu : 0u;  // a lane past the end re-reads a valid piece and drops it
-      v[p] = src[i < e ? i : (e > b ? e - 1 : 0)];
+      const int64_t i = i0 + p * nthr + t;
+      keep[p] = i < n16 ? 0xffffffffu : 0u;  // a thread past the end re-reads a valid piece and drops it
+      v[p] = src[i < n16 ? i : n16 - 1];
     }
 #pragma unroll
     for (int p = 0; p < P; ++p) acc ^= (v[p].x ^ v[p].y ^ v[p].z ^ v[p].w) & keep[p];

@@ -113,6 +113,11 @@ constexpr int kChunkMaxM = 16;
 bool launch_decode_chunked(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
                            hipStream_t stream, hipError_t& err);
 
+// Measurement helper: the dense bf16 weight (K % 16 == 0), two launches.
+hipError_t launch_dequant_bf16(bool pk12, const float* codebook, const uint8_t* indices, const int32_t* rows,
+                               const int32_t* cols, const float* deltas, int64_t nnz, uint16_t* w, int64_t N,
+                               int64_t K, hipStream_t stream);
+
 // Any shape and alignment: one wave per output row.
 hipError_t launch_generic(const LayerArgs& a, bool pk12, hipStream_t stream);
 
