@@ -674,8 +674,46 @@ bool plan(const DecodeSeg* segs, int nseg, bool pk12, bool xbf, int M, int K, in
 
 }  // namespace
 
+static bool launch_decode_plan(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
+                               hipStream_t stream, hipError_t& err);
+
+// One token row with K <= 4096 goes to the lean kernel (hxq_decode1.hip)
+// layer by layer as a single-layer call would: one launch when every layer
+// takes it and they fit together, else one launch per layer.
 bool launch_decode(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
                    hipStream_t stream, hipError_t& err) {
+  if (M == 1 && nseg >= 1 && nseg <= kMaxSegments) {
+    int n1 = 0;
+    for (int i = 0; i < nseg; ++i) n1 += decode1_takes(segs[i], pk12, xbf, M, K, x) ? 1 : 0;
+    if (n1 == nseg) {
+      if (launch_decode1(segs, nseg, pk12, x, xbf, M, K, stream, err)) return true;
+      for (int i = 0; i < nseg; ++i) {
+        if (!launch_decode1(&segs[i], 1, pk12, x, xbf, M, K, stream, err)) return false;
+        if (err != hipSuccess) return true;
+      }
+      return true;
+    }
+    if (n1 > 0) {
+      // mixed: every layer on its own kernel, checked before anything is launched
+      DecodeArgs a;
+      Plan p;
+      for (int i = 0; i < nseg; ++i)
+        if (!decode1_takes(segs[i], pk12, xbf, M, K, x) && !plan(&segs[i], 1, pk12, xbf, M, K, device_cu_count(), a, p))
+          return false;
+      for (int i = 0; i < nseg; ++i) {
+        const bool ok = decode1_takes(segs[i], pk12, xbf, M, K, x)
+                            ? launch_decode1(&segs[i], 1, pk12, x, xbf, M, K, stream, err)
+                            : launch_decode_plan(&segs[i], 1, pk12, x, xbf, M, K, stream, err);
+        if (!ok || err != hipSuccess) return true;
+      }
+      return true;
+    }
+  }
+  return launch_decode_plan(segs, nseg, pk12, x, xbf, M, K, stream, err);
+}
+
+static bool launch_decode_plan(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
+                               hipStream_t stream, hipError_t& err) {
   DecodeArgs a;
   Plan p;
   if (!plan(segs, nseg, pk12, xbf, M, K, device_cu_count(), a, p)) return false;

@@ -64,6 +64,12 @@ struct DecodeArgs {
 bool launch_decode(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
                    hipStream_t stream, hipError_t& err);
 bool decode_fits(const DecodeSeg* segs, int nseg, bool pk12, bool xbf, int M, int K);
+// The lean decode kernel for one token row and K <= 4096 (K % 1024 == 0):
+// takes = it runs this layer in a single-layer call; launch returns false
+// without launching when the layers do not fit one launch.
+bool decode1_takes(const DecodeSeg& s, bool pk12, bool xbf, int M, int K, const void* x);
+bool launch_decode1(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
+                    hipStream_t stream, hipError_t& err);
 // Matrix-core GEMV for M <= kGemvMfmaMaxM (u8 or pk12, K % 64 == 0): fp32
 // products on v_mfma_f32_16x16x4_f32, one launch per layer.
 constexpr int kGemvMfmaMaxM = 64;
