@@ -29,12 +29,19 @@ constexpr int THREADS = 512, WAVES = THREADS / 64;
 constexpr int RMAX = 96;      // rows per workgroup
 constexpr int SCAP = 512;     // sidecar triplets per epilogue pass
 constexpr int KMAX = 4096;
-constexpr int OFF_X = 0;                    // x as fp32, KMAX
+constexpr int OFF_X = 0;                    // x as fp32, KMAX, in lane order (xoff)
 constexpr int OFF_PART = OFF_X + KMAX * 4;  // row sums
 constexpr int OFF_TV = OFF_PART + RMAX * 4; // sidecar terms of a pass
 constexpr int OFF_MISC = OFF_TV + SCAP * 4; // lo, hi (int64), row ranges
 constexpr int LDS_DYN = OFF_MISC + 16 + 2 * RMAX * 4;
 }  // namespace dc1
+
+// Where x[k] sits in LDS (floats): element e of 16-byte piece h of lane l's
+// chunk c (k = 16 (64 c + l) + 4 h + e) at ((4 c + h) 64 + l) 4 + e, so the
+// lanes' reads of piece h are consecutive 16-byte pieces (no bank conflicts).
+__device__ __forceinline__ int xoff(int k) {
+  return ((((k >> 10) << 2) + ((k >> 2) & 3)) * 64 + ((k >> 4) & 63)) * 4 + (k & 3);
+}
 
 // CH: chunks of 16 weights per lane and row (K = 1024 CH)
 template <bool PK12, bool XBF, int CH>
@@ -69,8 +76,30 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
   constexpr int CB = PK12 ? 12 : 16;                                   // index bytes per chunk
   const int64_t row_bytes = (int64_t)K / 16 * CB;
 
-  // sidecar: waves 0 and 1 look up the first triplet of rows r0 and r1 (window
-  // loads first)
+  // ---- prologue.  Requests in the order they are waited for: the bias (used
+  // last, but one small load), the codebook and x (the barrier waits for
+  // their LDS copies), the sidecar window (waves 0 and 1), then the index
+  // bytes of the wave's first rows.
+  float bias_v = 0.f;
+  if (a.bias) bias_v = a.bias[min(r0 + tid, N - 1)];
+  constexpr int CBV = PK12 ? 4096 * 8 / 16 / THREADS : 1;
+  u32x4 cbv[CBV];
+  float cv = 0.f;
+  if (PK12) {
+#pragma unroll
+    for (int i = 0; i < CBV; ++i) cbv[i] = reinterpret_cast<const u32x4*>(a.codebook)[tid + i * THREADS];
+  } else {
+    cv = a.codebook[tid & 255];
+  }
+  // x: 16-byte pieces, thread t the pieces t, t + 512, ... (clamped: a thread
+  // past the end loads and stores the last piece again, so neither the load
+  // nor the store sits under a condition); one copy per workgroup in LDS
+  constexpr int XE = XBF ? 8 : 4;  // elements per piece
+  constexpr int XPT = (CH * 1024 / XE + THREADS - 1) / THREADS;
+  const int xpieces = K / XE;
+  u32x4 xv[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) xv[i] = reinterpret_cast<const u32x4*>(ga.x)[min(tid + THREADS * i, xpieces - 1)];
   const bool srch = a.nnz > 0 && wave < 2 && nrow > 0;
   const int target = wave == 0 ? r0 : r1;
   RowWindow win;
@@ -93,28 +122,6 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
   };
   u32x4 IQ[3][CH];
   load_row(0, IQ[0]);
-  // codebook and x into registers, then LDS
-  constexpr int CBV = PK12 ? 4096 * 8 / 16 / THREADS : 1;
-  u32x4 cbv[CBV];
-  float cv = 0.f;
-  if (PK12) {
-#pragma unroll
-    for (int i = 0; i < CBV; ++i) cbv[i] = reinterpret_cast<const u32x4*>(a.codebook)[tid + i * THREADS];
-  } else {
-    cv = a.codebook[tid & 255];
-  }
-  // x: 16-byte pieces, thread t the pieces t, t + 512, ... (clamped: a thread
-  // past the end loads and stores the last piece again, so neither the load
-  // nor the store sits under a condition)
-  constexpr int XE = XBF ? 8 : 4;  // elements per piece
-  constexpr int XPT = (CH * 1024 / XE + THREADS - 1) / THREADS;
-  const int xpieces = K / XE;
-  u32x4 xv[XPT];
-#pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const int q = min(tid + THREADS * i, xpieces - 1);
-    xv[i] = reinterpret_cast<const u32x4*>(ga.x)[q];
-  }
   load_row(1, IQ[1]);
   load_row(2, IQ[2]);
   if (PK12) {
@@ -129,18 +136,16 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const int q = min(tid + THREADS * i, xpieces - 1);
-    {
-      if (XBF) {
-        const u32x4 w = xv[i];
-        *reinterpret_cast<float4*>(xs + 8 * q) = make_float4(
-            __uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
-            __uint_as_float(w[1] & 0xffff0000u));
-        *reinterpret_cast<float4*>(xs + 8 * q + 4) = make_float4(
-            __uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u), __uint_as_float(w[3] << 16),
-            __uint_as_float(w[3] & 0xffff0000u));
-      } else {
-        *reinterpret_cast<u32x4*>(xs + 4 * q) = xv[i];
-      }
+    if (XBF) {
+      const u32x4 w = xv[i];
+      *reinterpret_cast<float4*>(xs + xoff(8 * q)) = make_float4(
+          __uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+          __uint_as_float(w[1] & 0xffff0000u));
+      *reinterpret_cast<float4*>(xs + xoff(8 * q + 4)) = make_float4(
+          __uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u), __uint_as_float(w[3] << 16),
+          __uint_as_float(w[3] & 0xffff0000u));
+    } else {
+      *reinterpret_cast<u32x4*>(xs + xoff(4 * q)) = xv[i];
     }
   }
   asm volatile("" ::: "memory");  // the lookup (and its wait) stays below the loads
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
   for (int c = 0; c < CH; ++c)
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float4 v = *reinterpret_cast<const float4*>(xs + 16 * (64 * c + lane) + 4 * h);
+      const float4 v = *reinterpret_cast<const float4*>(xs + ((4 * c + h) * 64 + lane) * 4);
       xr[c][4 * h] = v.x, xr[c][4 * h + 1] = v.y, xr[c][4 * h + 2] = v.z, xr[c][4 * h + 3] = v.w;
     }
   // the block's triplet range and the first epilogue pass's triplets
@@ -236,7 +241,7 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
         trn = a.sc_rows[ee + 1 < a.nnz ? ee + 1 : ee];
       }
       if (tid < cnt) {
-        tv[tid] = tdl * xs[tc];
+        tv[tid] = tdl * xs[xoff(tc)];
         if (tid == 0 || trp != tr) rsb[tr - r0] = tid;
         if (tid == cnt - 1 || trn != tr) rse[tr - r0] = tid + 1;
       }
@@ -245,10 +250,7 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
     if (tid < nrow)
       for (int e = rsb[tid]; e < rse[tid]; ++e) out += tv[e];
   }
-  if (tid < nrow) {
-    const int n = r0 + tid;
-    a.y[n] = out + (a.bias ? a.bias[n] : 0.f);
-  }
+  if (tid < nrow) a.y[r0 + tid] = out + bias_v;
 }
 
 bool decode1_ok(const DecodeSeg& s, bool pk12, bool xbf, int M, int K, const void* x) {
