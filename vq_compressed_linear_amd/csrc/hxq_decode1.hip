@@ -1,5 +1,5 @@
-// Decode GEMV for one token row with K <= 4096 (K % 1024 == 0), u8 and pk12,
-// one or several layers per launch: the lean variant of the decode kernel.
+// Decode GEMV for one token row (K % 16 == 0, K <= 12288), u8 and pk12, one
+// or several layers per launch: the lean variant of the decode kernel.
 //
 // y[n] = sum_k (C[idx[n][k]] + S[n][k]) x[k] + b[n]  (model cards, "What is
 // HelixCode?"; HXQ whitepaper, "Method" and "2D vector quantization"; the
@@ -8,7 +8,9 @@
 // A workgroup (one per CU) owns a contiguous run of rows of one layer; wave w
 // takes rows w, w + 8, ... of the run, a whole row at a time: lane l holds the
 // weights k = 16 (64 c + l) .. + 15 of chunk c (16 index bytes u8, 12 bytes =
-// 8 pairs pk12) and the matching x, read once from LDS into registers.  Per
+// 8 pairs pk12) and the matching x, read once from LDS into registers when
+// K <= 4096, else read from LDS chunk by chunk (x zero-padded to whole
+// chunks; index loads past the row end re-read its last piece).  Per
 // row: the codebook gather (LDS, 64 copies per entry for u8 so every lane has
 // its own bank; the 4096 pairs for pk12), fp32 FMAs into four partial sums,
 // a DPP reduction, one LDS word.  Index bytes are loaded three rows ahead;
@@ -28,7 +30,7 @@ namespace dc1 {
 constexpr int THREADS = 512, WAVES = THREADS / 64;
 constexpr int RMAX = 96;      // rows per workgroup
 constexpr int SCAP = 512;     // sidecar triplets per epilogue pass
-constexpr int KMAX = 4096;
+constexpr int KMAX = 12288;
 constexpr int OFF_X = 0;                    // x as fp32, KMAX, in lane order (xoff)
 constexpr int OFF_PART = OFF_X + KMAX * 4;  // row sums
 constexpr int OFF_TV = OFF_PART + RMAX * 4; // sidecar terms of a pass
@@ -43,8 +45,9 @@ __device__ __forceinline__ int xoff(int k) {
   return ((((k >> 10) << 2) + ((k >> 2) & 3)) * 64 + ((k >> 4) & 63)) * 4 + (k & 3);
 }
 
-// CH: chunks of 16 weights per lane and row (K = 1024 CH)
-template <bool PK12, bool XBF, int CH>
+// CH: chunks of 16 weights per lane and row (K <= 1024 CH); XL: x read from
+// LDS per chunk (else held in registers, K == 1024 CH)
+template <bool PK12, bool XBF, int CH, bool XL>
 __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
   using namespace dc1;
   __shared__ __align__(16) unsigned char cbs[PK12 ? 4096 * 8 : 256 * 256];
@@ -107,16 +110,18 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
 
   // ---- index bytes of the wave's row j (past its last row: a valid stand-in, unused)
   typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
+  const int kch = K / 16;  // chunks of 16 in a row
   auto load_row = [&](int j, u32x4 (&iq)[CH]) {
     const int row = min(r0 + wave + WAVES * min(j, max(nj - 1, 0)), N - 1);
-    const uint8_t* p = a.indices + (int64_t)row * row_bytes + CB * lane;
+    const uint8_t* p = a.indices + (int64_t)row * row_bytes;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
+      const int cc = XL ? min(64 * c + lane, kch - 1) : 64 * c + lane;
       if (PK12) {
-        const u32x3 v = *reinterpret_cast<const u32x3*>(p + CB * 64 * c);
+        const u32x3 v = *reinterpret_cast<const u32x3*>(p + CB * cc);
         iq[c] = u32x4{v[0], v[1], v[2], 0u};
       } else {
-        iq[c] = *reinterpret_cast<const u32x4*>(p + CB * 64 * c);
+        iq[c] = *reinterpret_cast<const u32x4*>(p + CB * cc);
       }
     }
   };
@@ -148,6 +153,9 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
       *reinterpret_cast<u32x4*>(xs + xoff(4 * q)) = xv[i];
     }
   }
+  if (XL)  // zeros from K up to whole chunks of every lane
+    for (int k = K + 4 * tid; k < 1024 * CH; k += 4 * THREADS)
+      *reinterpret_cast<float4*>(xs + xoff(k)) = make_float4(0.f, 0.f, 0.f, 0.f);
   asm volatile("" ::: "memory");  // the lookup (and its wait) stays below the loads
   if (srch) {
     const int64_t v = row_window_lower_bound(a.sc_rows, a.nnz, target, win);
@@ -156,14 +164,18 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
   __syncthreads();
 
   // the lane's x: k = 16 (64 c + lane) + i
-  float xr[CH][16];
-#pragma unroll
-  for (int c = 0; c < CH; ++c)
+  constexpr int XRC = XL ? 1 : CH;
+  float xr[XRC][16];
+  auto read_x = [&](int c, float (&d)[16]) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const float4 v = *reinterpret_cast<const float4*>(xs + ((4 * c + h) * 64 + lane) * 4);
-      xr[c][4 * h] = v.x, xr[c][4 * h + 1] = v.y, xr[c][4 * h + 2] = v.z, xr[c][4 * h + 3] = v.w;
+      d[4 * h] = v.x, d[4 * h + 1] = v.y, d[4 * h + 2] = v.z, d[4 * h + 3] = v.w;
     }
+  };
+  if (!XL)
+#pragma unroll
+    for (int c = 0; c < XRC; ++c) read_x(c, xr[c]);
   // the block's triplet range and the first epilogue pass's triplets
   int64_t lo = 0, hi = 0;
   if (a.nnz > 0 && nrow > 0) {
@@ -187,7 +199,10 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
     constexpr int R = decltype(r_c)::value;
     float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < CH; ++c)
+    for (int c = 0; c < CH; ++c) {
+      float xl[16];
+      if (XL) read_x(c, xl);
+      const float(&xc)[16] = XL ? xl : xr[XL ? 0 : c];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         float w[4];
@@ -208,8 +223,9 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
           w[3] = lds_load<float>(byte_addr256<3>(wd, lane4), cbs);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] = fmaf(w[e], xr[c][4 * d + e], s[e]);
+        for (int e = 0; e < 4; ++e) s[e] = fmaf(w[e], xc[4 * d + e], s[e]);
       }
+    }
     const float t = wave_sum_dpp((s[0] + s[1]) + (s[2] + s[3]));
     if (lane == 0) part[wave + WAVES * j] = t;
     load_row(j + 3, IQ[R]);
@@ -254,7 +270,7 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
 }
 
 bool decode1_ok(const DecodeSeg& s, bool pk12, bool xbf, int M, int K, const void* x) {
-  if (M != 1 || K < 1024 || K > dc1::KMAX || K % 1024 != 0) return false;
+  if (M != 1 || K < 16 || K > dc1::KMAX || K % 16 != 0) return false;
   if (reinterpret_cast<uintptr_t>(s.indices) % (pk12 ? 4 : 16) != 0) return false;
   if (pk12 && reinterpret_cast<uintptr_t>(s.codebook) % 16 != 0) return false;
   (void)xbf;
@@ -297,24 +313,36 @@ static bool decode1_plan(GemvMArgs& g, int& grid) {
   return true;
 }
 
-template <bool PK12, bool XBF, int CH>
+template <bool PK12, bool XBF, int CH, bool XL>
 static hipError_t launch_decode1_x(const GemvMArgs& g, int grid, hipStream_t stream) {
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode1_gemv<PK12, XBF, CH>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, dc1::LDS_DYN);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&decode1_gemv<PK12, XBF, CH, XL>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      dc1::LDS_DYN);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((decode1_gemv<PK12, XBF, CH>), dim3((unsigned)grid), dim3(dc1::THREADS), dc1::LDS_DYN, stream,
-                     g);
+  hipLaunchKernelGGL((decode1_gemv<PK12, XBF, CH, XL>), dim3((unsigned)grid), dim3(dc1::THREADS), dc1::LDS_DYN,
+                     stream, g);
   return hipGetLastError();
 }
 
+// K a multiple of 1024 up to 4096: x in registers; otherwise x from LDS with
+// the smallest instantiated chunk count that covers K
 template <bool PK12, bool XBF>
 static hipError_t launch_decode1_k(const GemvMArgs& g, int grid, hipStream_t stream) {
-  switch (g.K / 1024) {
-    case 1: return launch_decode1_x<PK12, XBF, 1>(g, grid, stream);
-    case 2: return launch_decode1_x<PK12, XBF, 2>(g, grid, stream);
-    case 3: return launch_decode1_x<PK12, XBF, 3>(g, grid, stream);
-    default: return launch_decode1_x<PK12, XBF, 4>(g, grid, stream);
+  if (g.K % 1024 == 0 && g.K <= 4096) {
+    switch (g.K / 1024) {
+      case 1: return launch_decode1_x<PK12, XBF, 1, false>(g, grid, stream);
+      case 2: return launch_decode1_x<PK12, XBF, 2, false>(g, grid, stream);
+      case 3: return launch_decode1_x<PK12, XBF, 3, false>(g, grid, stream);
+      default: return launch_decode1_x<PK12, XBF, 4, false>(g, grid, stream);
+    }
   }
+  const int ch = (g.K + 1023) / 1024;
+  if (ch <= 2) return launch_decode1_x<PK12, XBF, 2, true>(g, grid, stream);
+  if (ch <= 4) return launch_decode1_x<PK12, XBF, 4, true>(g, grid, stream);
+  if (ch <= 6) return launch_decode1_x<PK12, XBF, 6, true>(g, grid, stream);
+  if (ch <= 8) return launch_decode1_x<PK12, XBF, 8, true>(g, grid, stream);
+  if (ch <= 11) return launch_decode1_x<PK12, XBF, 11, true>(g, grid, stream);
+  return launch_decode1_x<PK12, XBF, 12, true>(g, grid, stream);
 }
 
 bool launch_decode1(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
