@@ -64,7 +64,7 @@ def group_bytes(layers, M, x_bytes):
 
 # the decode kernel's source and the headers it includes: the counters in
 # profiles/traffic.json are that kernel's and stay valid while these are unchanged
-DECODE_SOURCES = ("hxq_decode.hip", "hxq_device.h", "hxq_launch.h")
+DECODE_SOURCES = ("hxq_decode1.hip", "hxq_decode.hip", "hxq_device.h", "hxq_launch.h")
 
 
 def source_digest():
@@ -487,7 +487,7 @@ def main(argv=None):
                                "u8 1D VQ + 0.1% sidecar, decode M=1, fp32 x; launches q|k|v, o, gate|up, down",
                    "M": 1, "layers": len(layers), "launches_per_step": len(GROUPS),
                    "bytes_per_step": bytes_step, "rotating_copies": copies},
-        "roofline": {"bound": "hbm", "kernel": "decode_gemv (gate|up launch)",
+        "roofline": {"bound": "hbm", "kernel": "decode1_gemv (gate|up launch)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic("decode_gemv_gate_up_m1"),
