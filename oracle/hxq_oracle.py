@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle of the HelixLinear forward pass.
+"""Plain fp64 CPU oracle of the HelixLinear forward pass and of its product
+with the transposed weight (the gradient with respect to the input).
 
 TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or run this module; the GPU
@@ -20,6 +21,14 @@ definition written out:
     Y = X @ W^T + bias                                   (M x N, fp64)
     B = |X| @ |W|^T                                      (tolerance scale)
 
+The model cards ("Good to Know") keep the compressed weights frozen while
+LoRA adapters train through each HelixLinear (via HelixLinearSTE).  Training
+through a frozen layer needs the gradient of its output with respect to its
+input, which for y = x W^T + b is the product with the untransposed weight:
+
+    dX = dY @ W                                          (M x K, fp64)
+    B  = |dY| @ |W|                                      (tolerance scale)
+
 Readings of points the pages leave open (each also listed in the design notes):
   * orientation: W has nn.Linear's layout [out N, in K]; y = x W^T + b;
   * the sidecar is additive, W = C[idx] + delta, duplicate coordinates sum;
@@ -27,13 +36,18 @@ Readings of points the pages leave open (each also listed in the design notes):
     components 0 and 1 of the codebook pair;
   * 12-bit layout: triplet t of a row holds indices (a, b) = (2t, 2t+1) as the
     little-endian 24-bit word v = a | b << 12; a row has 3*ceil(K/4) bytes;
-  * bf16 activations are given as bit patterns and upcast exactly.
+  * bf16 activations are given as bit patterns and upcast exactly;
+  * the input gradient uses the same dequantised W, sidecar included (the
+    weights are frozen, so no gradient flows to codebook, indices or deltas).
 
 Pins (tests marked "not gpu"): brute-force fsum products on tiny non-square
 inputs with repeated sidecar coordinates, the constant-index closed form, the
 empty-sidecar difference, exhaustive 12-bit round trip and printed golden
 bytes, one-hot column reconstruction, the u8/pk12 cross-format special case,
-and bf16 rounding against the library cast.  No function here is unpinned.
+and bf16 rounding against the library cast.  The input gradient is pinned by
+its own brute force, a hand-computed example, the constant-index closed form,
+one-hot rows, and the adjoint identity sum(dY * (Y - b)) = sum(dX * X) that
+ties it to the pinned forward.  No function here is unpinned.
 """
 
 from __future__ import annotations
@@ -54,6 +68,10 @@ __all__ = [
     "hxq_linear_fwd_u8",
     "hxq_linear_fwd_pk12",
     "hxq_sidecar_add",
+    "linear_backward_x",
+    "error_bound_bwd",
+    "hxq_linear_bwd_x_u8",
+    "hxq_linear_bwd_x_pk12",
     "max_err_ratio",
 ]
 
@@ -198,6 +216,37 @@ def hxq_sidecar_add(rows, cols, deltas, x, x_dtype, N):
         Z[:, r[i]] += d[i] * X[:, c[i]]
         B[:, r[i]] += abs(d[i]) * np.abs(X[:, c[i]])
     return Z, B
+
+
+# ------------------------------------------------ product with W (input gradient)
+
+def linear_backward_x(W: np.ndarray, DY: np.ndarray) -> np.ndarray:
+    """dX = dY @ W, fp64: the gradient of y = x W^T + b with respect to x, for
+    a frozen W (model cards, "Good to Know": LoRA on frozen HelixLinear)."""
+    return DY @ W
+
+
+def error_bound_bwd(W: np.ndarray, DY: np.ndarray) -> np.ndarray:
+    """B = |dY| @ |W|, the elementwise scale of the tolerance."""
+    return np.abs(DY) @ np.abs(W)
+
+
+def hxq_linear_bwd_x_u8(codebook, indices, rows, cols, deltas, dy, dy_dtype,
+                        m_rows=None, want_bound=True):
+    """Oracle of the u8 input gradient.  dy is [M, N] (fp32, or bf16 bit
+    patterns); returns (dX, B) for all rows of dy or the rows in ``m_rows``."""
+    W = apply_sidecar(dequant_u8(codebook, unpack_u8(indices)), rows, cols, deltas)
+    DY = _rows(activations_f64(dy, dy_dtype), m_rows)
+    return linear_backward_x(W, DY), (error_bound_bwd(W, DY) if want_bound else None)
+
+
+def hxq_linear_bwd_x_pk12(codebook2, packed, rows, cols, deltas, dy, dy_dtype,
+                          N, K, m_rows=None, want_bound=True):
+    """Oracle of the pk12 input gradient (2D VQ, 12-bit packed indices)."""
+    W = dequant_pk12(codebook2, unpack_pk12(packed, N, K), K)
+    W = apply_sidecar(W, rows, cols, deltas)
+    DY = _rows(activations_f64(dy, dy_dtype), m_rows)
+    return linear_backward_x(W, DY), (error_bound_bwd(W, DY) if want_bound else None)
 
 
 def max_err_ratio(y, Y, B) -> float:

@@ -22,6 +22,13 @@ PINS = [
     P.test_cross_format_special_case,
     P.test_pk12_golden_bytes,
     P.test_bf16_round_matches_library_cast,
+    lambda: P.test_bwd_u8_matches_bruteforce(7, 12, 3),
+    lambda: P.test_bwd_pk12_matches_bruteforce(6, 16, 3),
+    P.test_bwd_golden_hand_example,
+    P.test_bwd_constant_index_closed_form,
+    P.test_bwd_one_hot_rows_give_weight_rows,
+    lambda: P.test_bwd_adjoint_of_forward("u8"),
+    lambda: P.test_bwd_adjoint_of_forward("pk12"),
 ]
 
 
@@ -78,6 +85,23 @@ def _bf16_bits_low_half(bits):
     return np.asarray(bits, np.uint16).astype(np.float32).astype(np.float64)
 
 
+def _bwd_rows_reversed(W, DY):
+    return DY @ W[::-1]
+
+
+def _bwd_forward_orientation(W, DY):
+    # the forward's operand order: only defined when W is square
+    return DY @ W.T
+
+
+def _bwd_columns_shifted(W, DY):
+    return np.roll(DY @ W, 1, axis=1)
+
+
+def _bwd_sign_lost(W, DY):
+    return DY @ np.abs(W)
+
+
 MUTATIONS = {
     "transposed_weight": ("linear_forward", _transposed_forward),
     "dropped_bias": ("linear_forward", _no_bias_forward),
@@ -87,6 +111,10 @@ MUTATIONS = {
     "pk12_pair_components_swapped": ("dequant_pk12", _dequant_pk12_components_swapped),
     "bf16_truncation": ("bf16_round_f32", _bf16_truncate),
     "bf16_upcast_wrong": ("bf16_bits_to_f64", _bf16_bits_low_half),
+    "bwd_rows_reversed": ("linear_backward_x", _bwd_rows_reversed),
+    "bwd_forward_orientation": ("linear_backward_x", _bwd_forward_orientation),
+    "bwd_columns_shifted": ("linear_backward_x", _bwd_columns_shifted),
+    "bwd_sign_lost": ("linear_backward_x", _bwd_sign_lost),
 }
 
 

@@ -363,3 +363,131 @@ def test_page_byte_counts():
                     pc["pk12_saving_vs_uint16_percent"] * (2 * N * K // 2)
         assert lay.compressed_bytes() == expect
         assert pc["sidecar_fields_per_entry"] * 4 == 12
+
+
+# ------------------------------------------- input gradient dX = dY @ W
+
+def _brute_bwd_from_W(W, rows, cols, deltas, DY):
+    """dX[m][k] = fsum over n of dy[m][n] * (W[n][k] + deltas at (n, k))."""
+    M, N, K = len(DY), len(W), len(W[0])
+    extra = {}
+    for r, c, d in zip(rows, cols, deltas):
+        extra.setdefault((int(r), int(c)), []).append(float(d))
+    out = np.zeros((M, K))
+    for m in range(M):
+        for k in range(K):
+            terms = []
+            for n in range(N):
+                g = float(DY[m][n])
+                terms.append(g * W[n][k])
+                terms += [g * d for d in extra.get((n, k), [])]
+            out[m, k] = math.fsum(terms)
+    return out
+
+
+@pytest.mark.parametrize("N,K,M", [(7, 12, 3), (5, 33, 2), (16, 8, 4)])
+def test_bwd_u8_matches_bruteforce(N, K, M):
+    rng = _rng(3000 + N * K + M)
+    cb = (0.05 * rng.standard_normal(256)).astype(np.float32)
+    idx = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    rows, cols, deltas = _tiny_sidecar(rng, N, K, 9)
+    DY = rng.standard_normal((M, N)).astype(np.float32)
+    dX, B = oracle.hxq_linear_bwd_x_u8(cb, idx, rows, cols, deltas, DY, "f32")
+    W = [[float(cb[int(i)]) for i in r] for r in idx.tolist()]
+    ref = _brute_bwd_from_W(W, rows, cols, deltas, DY.tolist())
+    assert dX.shape == (M, K)
+    assert np.all(np.abs(dX - ref) <= (N + 4) * 2.0 ** -52 * B)
+
+
+@pytest.mark.parametrize("N,K,M", [(6, 16, 3), (3, 10, 2), (9, 4, 5)])
+def test_bwd_pk12_matches_bruteforce(N, K, M):
+    rng = _rng(4000 + N * K + M)
+    cb2 = (0.05 * rng.standard_normal((4096, 2))).astype(np.float32)
+    idx2 = rng.integers(0, 4096, size=(N, K // 2))
+    packed = gen.pack12_rows(idx2)
+    rows, cols, deltas = _tiny_sidecar(rng, N, K, 7)
+    DY = rng.standard_normal((M, N)).astype(np.float32)
+    dX, B = oracle.hxq_linear_bwd_x_pk12(cb2, packed, rows, cols, deltas, DY, "f32", N, K)
+    W = _brute_pk12_weights(cb2, packed.tolist(), N, K)
+    ref = _brute_bwd_from_W(W, rows, cols, deltas, DY.tolist())
+    assert dX.shape == (M, K)
+    assert np.all(np.abs(dX - ref) <= (N + 4) * 2.0 ** -52 * B)
+
+
+def _golden_bwd():
+    vals = {}
+    with open(os.path.join(GOLDEN, "bwd_x_tiny.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                name, *rest = line.split()
+                vals[name] = rest
+    return vals
+
+
+def test_bwd_golden_hand_example():
+    g = _golden_bwd()
+    cb = np.full(256, 0.5, np.float32)
+    cb[:4] = [0.0, 1.0, 2.0, -1.0]
+    idx = np.array([int(v) for v in g["indices"]], np.uint8).reshape(2, 3)
+    rows = np.array([int(v) for v in g["sc_rows"]], np.int32)
+    cols = np.array([int(v) for v in g["sc_cols"]], np.int32)
+    deltas = np.array([float(v) for v in g["sc_deltas"]], np.float32)
+    DY = np.array([float(v) for v in g["dy"]], np.float32).reshape(2, 2)
+    want = np.array([float(v) for v in g["dx"]]).reshape(2, 3)
+    dX, _ = oracle.hxq_linear_bwd_x_u8(cb, idx, rows, cols, deltas, DY, "f32")
+    assert np.array_equal(dX, want)
+
+
+def test_bwd_constant_index_closed_form():
+    # every index e, no sidecar: W = C[e] everywhere, dX[m][k] = C[e] * sum_n dy[m][n]
+    rng = _rng(31)
+    N, K, M = 13, 10, 3
+    cb = (0.05 * rng.standard_normal(256)).astype(np.float32)
+    idx = np.full((N, K), 77, np.uint8)
+    DY = rng.standard_normal((M, N)).astype(np.float32)
+    dX, _ = oracle.hxq_linear_bwd_x_u8(cb, idx, [], [], [], DY, "f32")
+    want = float(cb[77]) * np.array([math.fsum(map(float, r)) for r in DY])
+    assert np.allclose(dX, np.repeat(want[:, None], K, axis=1), rtol=0, atol=1e-14)
+
+
+def test_bwd_one_hot_rows_give_weight_rows():
+    # dy row m = unit vector at n  ->  dX row m = W[n] (pk12 weights built from bytes)
+    rng = _rng(32)
+    N, K = 5, 12
+    cb2 = (0.05 * rng.standard_normal((4096, 2))).astype(np.float32)
+    idx2 = rng.integers(0, 4096, size=(N, K // 2))
+    packed = gen.pack12_rows(idx2)
+    rows, cols, deltas = _tiny_sidecar(rng, N, K, 5)
+    DY = np.eye(N, dtype=np.float32)[[3, 0, 4]]
+    dX, _ = oracle.hxq_linear_bwd_x_pk12(cb2, packed, rows, cols, deltas, DY, "f32", N, K)
+    W = np.array(_brute_pk12_weights(cb2, packed.tolist(), N, K))
+    for r, c, d in zip(rows, cols, deltas):
+        W[int(r), int(c)] += float(d)
+    assert np.array_equal(dX, W[[3, 0, 4]])
+
+
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
+def test_bwd_adjoint_of_forward(fmt):
+    # <dY, X W^T> = <dY W, X>: the input gradient is the adjoint of the pinned
+    # forward (bias subtracted), for non-square W and M > 1
+    rng = _rng(33 if fmt == "u8" else 34)
+    N, K, M = 11, 14, 4
+    rows, cols, deltas = _tiny_sidecar(rng, N, K, 8)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    DY = rng.standard_normal((M, N)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    if fmt == "u8":
+        cb = (0.05 * rng.standard_normal(256)).astype(np.float32)
+        idx = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+        Y, _ = oracle.hxq_linear_fwd_u8(cb, idx, rows, cols, deltas, X, "f32", bias)
+        dX, _ = oracle.hxq_linear_bwd_x_u8(cb, idx, rows, cols, deltas, DY, "f32")
+    else:
+        cb2 = (0.05 * rng.standard_normal((4096, 2))).astype(np.float32)
+        packed = gen.pack12_rows(rng.integers(0, 4096, size=(N, K // 2)))
+        Y, _ = oracle.hxq_linear_fwd_pk12(cb2, packed, rows, cols, deltas, X, "f32", bias, N, K)
+        dX, _ = oracle.hxq_linear_bwd_x_pk12(cb2, packed, rows, cols, deltas, DY, "f32", N, K)
+    lhs = math.fsum((DY.astype(np.float64) * (Y - bias.astype(np.float64)[None, :])).ravel())
+    rhs = math.fsum((dX * X.astype(np.float64)).ravel())
+    scale = math.fsum((np.abs(dX) * np.abs(X.astype(np.float64))).ravel()) + 1.0
+    assert abs(lhs - rhs) <= 1e-12 * scale
