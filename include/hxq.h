@@ -183,6 +183,60 @@ int hxq_dequant_bf16(int fmt, const float* codebook, const uint8_t* indices,
                      const float* sc_deltas, int64_t nnz, uint16_t* w,
                      int64_t N, int64_t K, hipStream_t stream);
 
+/* Input gradient of a frozen layer: the product with W itself (not W^T),
+ *
+ *     dx[m][k] = sum_n dy[m][n] * (C[idx[n][k]] + S[n][k])     (m < M, k < K)
+ *
+ * which is the gradient of the forward's y with respect to x.  The model cards
+ * ("Good to Know") keep the compressed weights frozen while LoRA adapters
+ * train through each HelixLinear (via HelixLinearSTE), so training needs this
+ * product and no gradient for the codebook, indices or sidecar.  There is no
+ * bias term.
+ *   fmt        HXQ_FMT_U8 or HXQ_FMT_PK12.
+ *   codebook, indices, sc_*  as for the forward entry points of that format
+ *              (the layer's N x K weight; pk12 needs even K).
+ *   dy         [M][N] float32 or bf16 bit patterns (dy_dtype), row-major.
+ *   dx         [M][K] float32, overwritten; must not overlap any input.
+ *   workspace  device memory for the partial sums when the sum over n is split
+ *              over several workgroups to fill the GPU, workspace_bytes long
+ *              (hxq_linear_bwd_x_workspace gives the size the call would use;
+ *              with less, or NULL, it splits less, down to not at all, which
+ *              is slower for small M).  Caller-owned, 4-byte aligned, contents
+ *              on entry ignored and on return unspecified; two calls in flight
+ *              at once need separate workspaces.
+ * Arithmetic: fp32 products with fp32 accumulation (bf16 dy upcast exactly).
+ * The splits are added in a fixed order; sidecar terms that land in the same
+ * column of one workgroup's tile are added in no fixed order.
+ * N == 0 sets dx to zero; M == 0 or K == 0 does nothing.  Work is one or two
+ * launches on `stream`.
+ * Errors: HXQ_ERR_SHAPE for an unknown fmt, negative or oversized M, N, K, nnz,
+ * negative workspace_bytes, or odd K with pk12; HXQ_ERR_DTYPE for an unknown
+ * dy_dtype; HXQ_ERR_NULL; HXQ_ERR_ALIGN (dy to its element size, dx, codebook,
+ * workspace and sidecar 4-byte); nothing is launched when an error is
+ * returned. */
+int hxq_linear_bwd_x(int fmt, const float* codebook, const uint8_t* indices,
+                     const int32_t* sc_rows, const int32_t* sc_cols,
+                     const float* sc_deltas, int64_t nnz,
+                     const void* dy, int dy_dtype, float* dx,
+                     int64_t M, int64_t N, int64_t K,
+                     void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace hxq_linear_bwd_x uses for these sizes on the current
+ * device (0 when it does not split), or a negative hxq_status for arguments
+ * it would reject with HXQ_ERR_SHAPE.  Host only. */
+int64_t hxq_linear_bwd_x_workspace(int fmt, int64_t M, int64_t N, int64_t K);
+
+/* The same with the kernel family forced: HXQ_VARIANT_AUTO, or
+ * HXQ_VARIANT_GEMV_VALU (the vector-FMA kernel, any shape); any other value
+ * returns HXQ_ERR_UNSUPPORTED. */
+int hxq_linear_bwd_x_ex(int fmt, const float* codebook, const uint8_t* indices,
+                        const int32_t* sc_rows, const int32_t* sc_cols,
+                        const float* sc_deltas, int64_t nnz,
+                        const void* dy, int dy_dtype, float* dx,
+                        int64_t M, int64_t N, int64_t K,
+                        void* workspace, int64_t workspace_bytes, hipStream_t stream,
+                        int variant);
+
 /* Kernel selection, for tests and measurement.  HXQ_VARIANT_AUTO is what the
  * entry points above use; the others force one kernel family and return
  * HXQ_ERR_UNSUPPORTED when it cannot take the call. */

@@ -213,3 +213,50 @@ def test_dequant_rejects(L):
     # empty weights launch nothing
     assert call(N=0, cb=None, idx=None, w=None) == B.HXQ_OK
     assert call(K=0, cb=None, idx=None, w=None) == B.HXQ_OK
+
+
+def test_bwd_x_rejects(L):
+    f = L.hxq_linear_bwd_x_ex
+    U8, PK = B.HXQ_FMT_U8, B.HXQ_FMT_PK12
+
+    def call(fmt=U8, cb=FAKE, idx=FAKE, r=FAKE, c=FAKE, d=FAKE, nnz=0, dy=FAKE, dt=0, dx=FAKE,
+             M=2, N=4, K=32, ws=None, wsb=0, variant=0):
+        return f(fmt, cb, idx, r, c, d, nnz, dy, dt, dx, M, N, K, ws, wsb, None, variant)
+
+    assert call(fmt=5) == B.HXQ_ERR_SHAPE
+    assert call(dt=3) == B.HXQ_ERR_DTYPE
+    assert call(M=-1) == B.HXQ_ERR_SHAPE
+    assert call(N=-1) == B.HXQ_ERR_SHAPE
+    assert call(K=-2) == B.HXQ_ERR_SHAPE
+    assert call(nnz=-1) == B.HXQ_ERR_SHAPE
+    assert call(K=2 ** 31) == B.HXQ_ERR_SHAPE
+    assert call(fmt=PK, K=31) == B.HXQ_ERR_SHAPE
+    assert call(variant=B.HXQ_VARIANT_GENERIC) == B.HXQ_ERR_UNSUPPORTED
+    assert call(variant=99) == B.HXQ_ERR_UNSUPPORTED
+    assert call(dx=None) == B.HXQ_ERR_NULL
+    assert call(dy=None) == B.HXQ_ERR_NULL
+    assert call(idx=None) == B.HXQ_ERR_NULL
+    assert call(cb=None) == B.HXQ_ERR_NULL
+    assert call(nnz=3, c=None) == B.HXQ_ERR_NULL
+    assert call(dx=FAKE + 2) == B.HXQ_ERR_ALIGN
+    assert call(dy=FAKE + 2) == B.HXQ_ERR_ALIGN
+    assert call(dy=FAKE + 1, dt=1) == B.HXQ_ERR_ALIGN
+    assert call(cb=FAKE + 2) == B.HXQ_ERR_ALIGN
+    assert call(nnz=1, d=FAKE + 1) == B.HXQ_ERR_ALIGN
+    assert call(ws=FAKE + 2, wsb=64) == B.HXQ_ERR_ALIGN
+    assert call(wsb=-1) == B.HXQ_ERR_SHAPE
+    # nothing to compute: no launch, no pointer needed
+    assert call(M=0, cb=None, idx=None, dy=None, dx=None) == B.HXQ_OK
+    assert call(K=0, cb=None, idx=None, dy=None, dx=None) == B.HXQ_OK
+
+
+def test_bwd_x_workspace_query(L):
+    q = L.hxq_linear_bwd_x_workspace
+    assert q(9, 1, 8, 8) == B.HXQ_ERR_SHAPE
+    assert q(B.HXQ_FMT_PK12, 1, 8, 7) == B.HXQ_ERR_SHAPE
+    assert q(B.HXQ_FMT_U8, -1, 8, 8) == B.HXQ_ERR_SHAPE
+    assert q(B.HXQ_FMT_U8, 0, 8, 8) == 0
+    # a split workspace holds whole [M][K] fp32 partial sums
+    for M, N, K in ((1, 11008, 2048), (3, 2048, 11008), (64, 4096, 4096)):
+        n = q(B.HXQ_FMT_U8, M, N, K)
+        assert n >= 0 and n % (M * K * 4) == 0

@@ -21,6 +21,8 @@ from ._binding import (  # noqa: F401
     HxqError,
     HxqLayer,
     hxq_dequant_bf16,
+    hxq_linear_bwd_x,
+    hxq_linear_bwd_x_workspace,
     hxq_linear_fwd_grouped,
     hxq_linear_fwd_pk12,
     hxq_linear_fwd_u8,

@@ -78,6 +78,10 @@ SIGNATURES = {
     "hxq_linear_fwd_grouped": (_INT, [_INT, ctypes.POINTER(HxqLayer), _INT, _P, _INT, _I64, _I64, _P]),
     "hxq_stream_read": (_INT, [_P, _I64, _P, _INT, _P]),
     "hxq_dequant_bf16": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _I64, _I64, _P]),
+    "hxq_linear_bwd_x": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P, _I64, _P]),
+    "hxq_linear_bwd_x_ex": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P, _I64, _P,
+                                   _INT]),
+    "hxq_linear_bwd_x_workspace": (_I64, [_INT, _I64, _I64, _I64]),
     "hxq_select_variant": (_INT, [_INT, _INT, _I64, _I64, _I64]),
     "hxq_status_str": (ctypes.c_char_p, [_INT]),
     "hxq_version": (_INT, []),
@@ -243,6 +247,45 @@ def hxq_dequant_bf16(fmt: int, codebook, indices, sc_rows, sc_cols, sc_deltas, w
         raise HxqError(st, "hxq_dequant_bf16")
 
 
+def hxq_linear_bwd_x(fmt: int, codebook, indices, sc_rows, sc_cols, sc_deltas, dy, dx, K: int,
+                     stream=None, variant: int = HXQ_VARIANT_AUTO, workspace=None) -> None:
+    """dx <- dy (C[indices] + S) on the device: the input gradient of a frozen
+    layer.  dy is a contiguous float32 or bfloat16 [M, N] tensor, dx a
+    contiguous float32 [M, K] tensor; K is the layer's input width (pk12 rows
+    hold 3*ceil(K/4) bytes).  ``workspace`` (a device tensor) holds the partial
+    sums of split rows; when None, one of the size the library asks for is
+    taken from torch's caching allocator; an empty tensor means none."""
+    torch = _torch()
+    if codebook.dtype != torch.float32 or codebook.numel() != (256 if fmt == HXQ_FMT_U8 else 8192):
+        raise ValueError("wrong codebook size or dtype")
+    if indices.dtype != torch.uint8 or indices.dim() != 2 or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous uint8 matrix")
+    N = indices.shape[0]
+    row = K if fmt == HXQ_FMT_U8 else 3 * ((K + 3) // 4)
+    if indices.shape[1] != row:
+        raise ValueError("index rows hold %d bytes, expected %d" % (indices.shape[1], row))
+    if dy.dim() != 2 or not dy.is_contiguous() or dy.shape[1] != N:
+        raise ValueError("dy must be a contiguous [M, N] tensor")
+    M = dy.shape[0]
+    if dx.dtype != torch.float32 or tuple(dx.shape) != (M, K) or not dx.is_contiguous():
+        raise ValueError("dx must be a contiguous float32 [M, K] tensor")
+    nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
+    if workspace is None:
+        need = lib().hxq_linear_bwd_x_workspace(fmt, M, N, K)
+        if need < 0:
+            raise HxqError(int(need), "hxq_linear_bwd_x_workspace")
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dx.device) if need > 0 else None
+    if workspace is None or workspace.numel() == 0:
+        wptr, wbytes = None, 0
+    else:
+        wptr, wbytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = lib().hxq_linear_bwd_x_ex(fmt, _ptr(codebook), _ptr(indices), _ptr(sc_rows), _ptr(sc_cols),
+                                   _ptr(sc_deltas), nnz, _ptr(dy), _x_dtype(dy), _ptr(dx), M, N, K,
+                                   wptr, wbytes, _stream(stream), variant)
+    if st != HXQ_OK:
+        raise HxqError(st, "hxq_linear_bwd_x")
+
+
 def grouped_layers(fmt: int, layers, M: int, K: int):
     """HxqLayer array for hxq_linear_fwd_grouped from dicts holding the
     tensors codebook, indices, sc_rows, sc_cols, sc_deltas, bias (or None) and
@@ -280,6 +323,14 @@ def hxq_linear_fwd_grouped(fmt: int, layers, x, stream=None) -> None:
     st = lib().hxq_linear_fwd_grouped(fmt, arr, len(layers), _ptr(x), _x_dtype(x), M, K, _stream(stream))
     if st != HXQ_OK:
         raise HxqError(st, "hxq_linear_fwd_grouped")
+
+
+def hxq_linear_bwd_x_workspace(fmt: int, M: int, N: int, K: int) -> int:
+    """Bytes of workspace hxq_linear_bwd_x uses for these sizes."""
+    n = lib().hxq_linear_bwd_x_workspace(fmt, M, N, K)
+    if n < 0:
+        raise HxqError(int(n), "hxq_linear_bwd_x_workspace")
+    return int(n)
 
 
 def hxq_select_variant(fmt_pk12: bool, x_dtype: int, M: int, N: int, K: int) -> int:

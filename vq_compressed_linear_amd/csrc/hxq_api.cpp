@@ -90,9 +90,71 @@ int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32
   }
 }
 
+int backward_x(int fmt, const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
+               const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* dy, int dy_dtype,
+               float* dx, int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+               hipStream_t stream, int variant) {
+  if (fmt != HXQ_FMT_U8 && fmt != HXQ_FMT_PK12) return HXQ_ERR_SHAPE;
+  const bool pk12 = fmt == HXQ_FMT_PK12;
+  if (dy_dtype != HXQ_F32 && dy_dtype != HXQ_BF16) return HXQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || nnz < 0 || workspace_bytes < 0) return HXQ_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim || nnz > kMaxDim) return HXQ_ERR_SHAPE;
+  if (pk12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
+  if (variant != HXQ_VARIANT_AUTO && variant != HXQ_VARIANT_GEMV_VALU) return HXQ_ERR_UNSUPPORTED;
+  if (M == 0 || K == 0) return HXQ_OK;
+  if (!dx) return HXQ_ERR_NULL;
+  if (N > 0 && (!dy || !indices || !codebook)) return HXQ_ERR_NULL;
+  if (nnz > 0 && (!sc_rows || !sc_cols || !sc_deltas)) return HXQ_ERR_NULL;
+  const uintptr_t ds = dy_dtype == HXQ_BF16 ? 2 : 4;
+  if (misaligned(dy, ds) || misaligned(dx, 4) || misaligned(codebook, 4) || misaligned(sc_rows, 4) ||
+      misaligned(sc_cols, 4) || misaligned(sc_deltas, 4) || misaligned(workspace, 4))
+    return HXQ_ERR_ALIGN;
+  (void)hipGetLastError();
+  if (N == 0) return status_of(hxq::launch_fill_zero(dx, M * K, stream));
+  hxq::BwdArgs a = {};
+  a.codebook = codebook;
+  a.indices = indices;
+  a.sc_rows = sc_rows;
+  a.sc_cols = sc_cols;
+  a.sc_deltas = sc_deltas;
+  a.nnz = nnz;
+  a.dy = dy;
+  a.dy_bf16 = dy_dtype == HXQ_BF16;
+  a.dx = dx;
+  a.ws = workspace ? static_cast<float*>(workspace) : nullptr;
+  a.ws_bytes = workspace ? workspace_bytes : 0;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  return status_of(hxq::launch_bwdx_valu(a, pk12, stream));
+}
+
 }  // namespace
 
 extern "C" {
+
+int hxq_linear_bwd_x(int fmt, const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
+                     const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* dy, int dy_dtype,
+                     float* dx, int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                     hipStream_t stream) {
+  return backward_x(fmt, codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, dy, dy_dtype, dx, M, N, K, workspace,
+                    workspace_bytes, stream, HXQ_VARIANT_AUTO);
+}
+
+int64_t hxq_linear_bwd_x_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (fmt != HXQ_FMT_U8 && fmt != HXQ_FMT_PK12) return HXQ_ERR_SHAPE;
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return HXQ_ERR_SHAPE;
+  if (fmt == HXQ_FMT_PK12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
+  return hxq::bwdx_workspace_bytes((int)M, (int)N, (int)K);
+}
+
+int hxq_linear_bwd_x_ex(int fmt, const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
+                        const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* dy, int dy_dtype,
+                        float* dx, int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                        hipStream_t stream, int variant) {
+  return backward_x(fmt, codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, dy, dy_dtype, dx, M, N, K, workspace,
+                    workspace_bytes, stream, variant);
+}
 
 int hxq_linear_fwd_u8_ex(const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
                          const int32_t* sc_cols, const float* sc_deltas, int64_t nnz,

@@ -167,4 +167,31 @@ hipError_t launch_sidecar_add(const LayerArgs& a, hipStream_t stream);
 // sink (at most sink_words workgroups).
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream);
 
+// ---- input gradient dx = dy W (hxq_bwd.hip, hxq_bwd_mfma.hip)
+struct BwdArgs {
+  const float* codebook;     // u8: float[256]; pk12: float[4096][2]
+  const uint8_t* indices;    // u8: [N][K]; pk12: [N][3*ceil(K/4)]
+  const int32_t* sc_rows;
+  const int32_t* sc_cols;
+  const float* sc_deltas;
+  int64_t nnz;
+  const void* dy;            // [M][N] fp32 or bf16 bits
+  bool dy_bf16;
+  float* dx;                 // [M][K]
+  int M, N, K;
+  float* ws;                 // workspace for the partial sums of row splits, or nullptr
+  int64_t ws_bytes;
+  int CT, S, R;              // set by the launcher: column tiles, row splits, rows per split
+};
+
+struct BwdPlan {
+  int mt, lpr, mtiles, ct, S;
+};
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+bool bwdx_vec_ok(const BwdArgs& a, bool pk12);
+BwdPlan bwdx_plan(int M, int N, int K);
+int64_t bwdx_workspace_bytes(int M, int N, int K);
+hipError_t launch_bwdx_valu(const BwdArgs& a, bool pk12, hipStream_t stream);
+
 }  // namespace hxq
