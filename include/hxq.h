@@ -204,8 +204,13 @@ int hxq_dequant_bf16(int fmt, const float* codebook, const uint8_t* indices,
  *              is slower for small M).  Caller-owned, 4-byte aligned, contents
  *              on entry ignored and on return unspecified; two calls in flight
  *              at once need separate workspaces.
- * Arithmetic: fp32 products with fp32 accumulation (bf16 dy upcast exactly).
- * The splits are added in a fixed order; sidecar terms that land in the same
+ * Arithmetic: fp32 products with fp32 accumulation (bf16 dy upcast exactly);
+ * with bf16 dy from 16 tokens, on shapes and pointers the bf16 matrix-core
+ * kernel takes (see hxq_linear_bwd_x_ex) and with its workspace, bf16
+ * products with fp32 accumulation, the weight value being the codebook value
+ * plus the sidecar deltas at that position (added in fp32 in stored order)
+ * rounded once to bf16, as in the forward bf16 GEMM.  Row splits are added in
+ * a fixed order; on the vector path, sidecar terms that land in the same
  * column of one workgroup's tile are added in no fixed order.
  * N == 0 sets dx to zero; M == 0 or K == 0 does nothing.  Work is one or two
  * launches on `stream`.
@@ -221,14 +226,20 @@ int hxq_linear_bwd_x(int fmt, const float* codebook, const uint8_t* indices,
                      int64_t M, int64_t N, int64_t K,
                      void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace hxq_linear_bwd_x uses for these sizes on the current
- * device (0 when it does not split), or a negative hxq_status for arguments
- * it would reject with HXQ_ERR_SHAPE.  Host only. */
-int64_t hxq_linear_bwd_x_workspace(int fmt, int64_t M, int64_t N, int64_t K);
+/* Bytes of workspace hxq_linear_bwd_x uses on the current device for these
+ * sizes with pointers aligned to 16 bytes (0 when it needs none), or a
+ * negative hxq_status for arguments it would reject (HXQ_ERR_SHAPE,
+ * HXQ_ERR_DTYPE).  Host only. */
+int64_t hxq_linear_bwd_x_workspace(int fmt, int dy_dtype, int64_t M, int64_t N,
+                                   int64_t K, int64_t nnz);
 
-/* The same with the kernel family forced: HXQ_VARIANT_AUTO, or
- * HXQ_VARIANT_GEMV_VALU (the vector-FMA kernel, any shape); any other value
- * returns HXQ_ERR_UNSUPPORTED. */
+/* The same with the kernel family forced: HXQ_VARIANT_AUTO;
+ * HXQ_VARIANT_GEMV_VALU, the vector-FMA kernel (any shape); or
+ * HXQ_VARIANT_GEMM_BF16, the bf16 matrix-core kernel (bf16 dy, N % 32 == 0,
+ * K % 128 == 0, K <= 16384, dy and dx 16-byte and indices 8-byte (u8) or
+ * 4-byte (pk12) aligned, and the workspace the query gives), which returns
+ * HXQ_ERR_UNSUPPORTED when it cannot take the call; any other value returns
+ * HXQ_ERR_UNSUPPORTED. */
 int hxq_linear_bwd_x_ex(int fmt, const float* codebook, const uint8_t* indices,
                         const int32_t* sc_rows, const int32_t* sc_cols,
                         const float* sc_deltas, int64_t nnz,

@@ -252,11 +252,16 @@ def test_bwd_x_rejects(L):
 
 def test_bwd_x_workspace_query(L):
     q = L.hxq_linear_bwd_x_workspace
-    assert q(9, 1, 8, 8) == B.HXQ_ERR_SHAPE
-    assert q(B.HXQ_FMT_PK12, 1, 8, 7) == B.HXQ_ERR_SHAPE
-    assert q(B.HXQ_FMT_U8, -1, 8, 8) == B.HXQ_ERR_SHAPE
-    assert q(B.HXQ_FMT_U8, 0, 8, 8) == 0
-    # a split workspace holds whole [M][K] fp32 partial sums
+    F32, BF = B.HXQ_F32, B.HXQ_BF16
+    assert q(9, F32, 1, 8, 8, 0) == B.HXQ_ERR_SHAPE
+    assert q(B.HXQ_FMT_U8, 5, 1, 8, 8, 0) == B.HXQ_ERR_DTYPE
+    assert q(B.HXQ_FMT_PK12, F32, 1, 8, 7, 0) == B.HXQ_ERR_SHAPE
+    assert q(B.HXQ_FMT_U8, F32, -1, 8, 8, 0) == B.HXQ_ERR_SHAPE
+    assert q(B.HXQ_FMT_U8, F32, 1, 8, 8, -1) == B.HXQ_ERR_SHAPE
+    assert q(B.HXQ_FMT_U8, F32, 0, 8, 8, 0) == 0
+    # the vector path's workspace holds whole [M][K] fp32 partial sums
     for M, N, K in ((1, 11008, 2048), (3, 2048, 11008), (64, 4096, 4096)):
-        n = q(B.HXQ_FMT_U8, M, N, K)
+        n = q(B.HXQ_FMT_U8, F32, M, N, K, 0)
         assert n >= 0 and n % (M * K * 4) == 0
+    # the matrix-core path also keeps the sidecar bins there
+    assert q(B.HXQ_FMT_U8, BF, 256, 2048, 2048, 4096) > q(B.HXQ_FMT_U8, BF, 256, 2048, 2048, 0)

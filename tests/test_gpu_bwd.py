@@ -5,7 +5,11 @@ Shapes cover M = 1 at the full attention and MLP widths of the Qwen2.5-3B
 workload (K and N of 2048 and 11008), ragged column tails (K not a multiple
 of the 512-column tile), the byte-load path (u8 K % 8 != 0, pk12 K % 16 != 0),
 token tails past the 8-token tile, a launch with a single row split (plain
-stores) and the empty cases.  Tolerance: 1e-5 * (|dY| |W|) for the fp32 path.
+stores) and the empty cases.  Tolerance: 1e-5 * (|dY| |W|) for the fp32 path,
+8e-3 * (|dY| |W|) for the bf16 matrix-core kernel (bf16 dy from 16 tokens),
+which is also run forced on its own shapes: the MLP widths, K not a multiple
+of its 512-column workgroup tile, token tails, the smallest and largest K, and
+sidecar bins longer than a wave.
 """
 
 import numpy as np
@@ -87,7 +91,9 @@ def test_bwd_x_matches_oracle(fmt, dtype, N, K, M):
     dx = _run(lay, d, G.dev_x(dy_np, dtype))
     G.torch().cuda.synchronize()
     Y, B = _oracle(lay, dy_np, dtype)
-    G.check(dx, Y, B, G.TOL_FP32, "bwd_x %s %s N=%d K=%d M=%d" % (fmt, dtype, N, K, M))
+    # bf16 dy from 16 tokens may take the bf16 matrix-core kernel
+    tol = G.TOL_BF16 if dtype == "bf16" and M >= 16 else G.TOL_FP32
+    G.check(dx, Y, B, tol, "bwd_x %s %s N=%d K=%d M=%d" % (fmt, dtype, N, K, M))
 
 
 @pytest.mark.parametrize("fmt", ["u8", "pk12"])
@@ -170,10 +176,62 @@ def test_bwd_x_workspace_sizes(fmt, share):
     lay = gen.random_layer(98, N, K, fmt, nnz=N * K // 1000, duplicates=True)
     d = G.dev_layer(lay)
     dy_np = _dy(99, M, N, "f32")
-    need = hx.hxq_linear_bwd_x_workspace(_fmt(lay), M, N, K)
+    need = hx.hxq_linear_bwd_x_workspace(_fmt(lay), hx.HXQ_F32, M, N, K, len(lay.rows))
     assert need >= 2 * M * K * 4  # this shape splits its rows
     nbytes = 0 if share is None else max(4, int(need * share) // 4 * 4)
     ws = t.full((nbytes // 4,), float("nan"), dtype=t.float32, device="cuda")
     dx = _run(lay, d, G.dev_x(dy_np, "f32"), workspace=ws)
     Y, B = _oracle(lay, dy_np, "f32")
     G.check(dx, Y, B, G.TOL_FP32, "bwd_x %s workspace %s" % (fmt, share))
+
+
+MFMA_CASES = [
+    # (N, K, M)
+    (2048, 2048, 64),
+    (11008, 2048, 128),
+    (2048, 11008, 96),
+    (256, 512, 16),
+    (64, 128, 200),
+    (32, 16384, 20),
+]
+
+
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
+@pytest.mark.parametrize("N,K,M", MFMA_CASES)
+def test_bwd_x_mfma_matches_oracle(fmt, N, K, M):
+    G.say("bwd_x mfma %s N=%d K=%d M=%d" % (fmt, N, K, M))
+    lay = gen.random_layer(7000 + N + 3 * K + 7 * M, N, K, fmt, nnz=max(1, N * K // 1000), duplicates=True)
+    d = G.dev_layer(lay)
+    dy_np = _dy(8000 + N + K + M, M, N, "bf16")
+    dx = _run(lay, d, G.dev_x(dy_np, "bf16"), variant=hx.HXQ_VARIANT_GEMM_BF16)
+    G.torch().cuda.synchronize()
+    Y, B = _oracle(lay, dy_np, "bf16")
+    G.check(dx, Y, B, G.TOL_BF16, "bwd_x mfma %s N=%d K=%d M=%d" % (fmt, N, K, M))
+
+
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
+def test_bwd_x_mfma_dense_sidecar(fmt):
+    # bins of several hundred triplets (past the 64 a wave prefetches) with
+    # repeated coordinates; and the same layer without its sidecar
+    N, K, M = 64, 1024, 48
+    G.say("bwd_x mfma %s dense sidecar" % fmt)
+    lay = gen.random_layer(101, N, K, fmt, nnz=N * K // 8, duplicates=True)
+    d = G.dev_layer(lay)
+    dy_np = _dy(102, M, N, "bf16")
+    for sidecar in (True, False):
+        dx = _run(lay, d, G.dev_x(dy_np, "bf16"), sidecar=sidecar, variant=hx.HXQ_VARIANT_GEMM_BF16)
+        Y, B = _oracle(lay, dy_np, "bf16", sidecar=sidecar)
+        G.check(dx, Y, B, G.TOL_BF16, "bwd_x mfma %s dense sidecar=%s" % (fmt, sidecar))
+
+
+def test_bwd_x_mfma_needs_its_workspace():
+    # forced onto the matrix cores with too little workspace: refused, nothing launched
+    t = G.torch()
+    N, K, M = 2048, 2048, 64
+    lay = gen.random_layer(103, N, K, "u8", nnz=N * K // 1000)
+    d = G.dev_layer(lay)
+    dy = G.dev_x(_dy(104, M, N, "bf16"), "bf16")
+    dx = t.zeros((M, K), dtype=t.float32, device="cuda")
+    with pytest.raises(hx.HxqError):
+        hx.hxq_linear_bwd_x(hx.HXQ_FMT_U8, d["codebook"], d["indices"], d["rows"], d["cols"], d["deltas"], dy, dx,
+                            K, variant=hx.HXQ_VARIANT_GEMM_BF16, workspace=t.zeros(4, dtype=t.uint8, device="cuda"))

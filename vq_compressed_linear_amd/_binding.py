@@ -81,7 +81,7 @@ SIGNATURES = {
     "hxq_linear_bwd_x": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "hxq_linear_bwd_x_ex": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P, _I64, _P,
                                    _INT]),
-    "hxq_linear_bwd_x_workspace": (_I64, [_INT, _I64, _I64, _I64]),
+    "hxq_linear_bwd_x_workspace": (_I64, [_INT, _INT, _I64, _I64, _I64, _I64]),
     "hxq_select_variant": (_INT, [_INT, _INT, _I64, _I64, _I64]),
     "hxq_status_str": (ctypes.c_char_p, [_INT]),
     "hxq_version": (_INT, []),
@@ -271,7 +271,7 @@ def hxq_linear_bwd_x(fmt: int, codebook, indices, sc_rows, sc_cols, sc_deltas, d
         raise ValueError("dx must be a contiguous float32 [M, K] tensor")
     nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
     if workspace is None:
-        need = lib().hxq_linear_bwd_x_workspace(fmt, M, N, K)
+        need = lib().hxq_linear_bwd_x_workspace(fmt, _x_dtype(dy), M, N, K, nnz)
         if need < 0:
             raise HxqError(int(need), "hxq_linear_bwd_x_workspace")
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dx.device) if need > 0 else None
@@ -325,9 +325,9 @@ def hxq_linear_fwd_grouped(fmt: int, layers, x, stream=None) -> None:
         raise HxqError(st, "hxq_linear_fwd_grouped")
 
 
-def hxq_linear_bwd_x_workspace(fmt: int, M: int, N: int, K: int) -> int:
+def hxq_linear_bwd_x_workspace(fmt: int, dy_dtype: int, M: int, N: int, K: int, nnz: int) -> int:
     """Bytes of workspace hxq_linear_bwd_x uses for these sizes."""
-    n = lib().hxq_linear_bwd_x_workspace(fmt, M, N, K)
+    n = lib().hxq_linear_bwd_x_workspace(fmt, dy_dtype, M, N, K, nnz)
     if n < 0:
         raise HxqError(int(n), "hxq_linear_bwd_x_workspace")
     return int(n)

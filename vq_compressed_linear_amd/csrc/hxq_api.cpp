@@ -12,6 +12,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)INT32_MAX - 65536;  // room for tile rounding in int32
+constexpr int64_t kBwdMfmaMinM = 16;                       // input gradient: matrix cores from here
 
 bool misaligned(const void* p, uintptr_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
@@ -100,7 +101,8 @@ int backward_x(int fmt, const float* codebook, const uint8_t* indices, const int
   if (M < 0 || N < 0 || K < 0 || nnz < 0 || workspace_bytes < 0) return HXQ_ERR_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim || nnz > kMaxDim) return HXQ_ERR_SHAPE;
   if (pk12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
-  if (variant != HXQ_VARIANT_AUTO && variant != HXQ_VARIANT_GEMV_VALU) return HXQ_ERR_UNSUPPORTED;
+  if (variant != HXQ_VARIANT_AUTO && variant != HXQ_VARIANT_GEMV_VALU && variant != HXQ_VARIANT_GEMM_BF16)
+    return HXQ_ERR_UNSUPPORTED;
   if (M == 0 || K == 0) return HXQ_OK;
   if (!dx) return HXQ_ERR_NULL;
   if (N > 0 && (!dy || !indices || !codebook)) return HXQ_ERR_NULL;
@@ -126,6 +128,17 @@ int backward_x(int fmt, const float* codebook, const uint8_t* indices, const int
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
+  // the bf16 matrix-core kernel past 16 tokens, when the shape, the pointers
+  // and the workspace (row splits and sidecar bins) allow it
+  bool mfma = hxq::bwdx_mfma_ok(a, pk12);
+  if (mfma) {
+    const hxq::BwdMPlan p = hxq::bwdx_mfma_plan(a.M, a.N, a.K, nnz);
+    const int64_t need = p.split_bytes + p.bin_bytes;
+    mfma = need == 0 || (workspace && workspace_bytes >= need);
+  }
+  if (variant == HXQ_VARIANT_GEMM_BF16 && !mfma) return HXQ_ERR_UNSUPPORTED;
+  if (variant == HXQ_VARIANT_GEMM_BF16 || (variant == HXQ_VARIANT_AUTO && mfma && M >= kBwdMfmaMinM))
+    return status_of(hxq::launch_bwdx_mfma(a, pk12, stream));
   return status_of(hxq::launch_bwdx_valu(a, pk12, stream));
 }
 
@@ -141,10 +154,26 @@ int hxq_linear_bwd_x(int fmt, const float* codebook, const uint8_t* indices, con
                     workspace_bytes, stream, HXQ_VARIANT_AUTO);
 }
 
-int64_t hxq_linear_bwd_x_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
+int64_t hxq_linear_bwd_x_workspace(int fmt, int dy_dtype, int64_t M, int64_t N, int64_t K, int64_t nnz) {
   if (fmt != HXQ_FMT_U8 && fmt != HXQ_FMT_PK12) return HXQ_ERR_SHAPE;
-  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return HXQ_ERR_SHAPE;
+  if (dy_dtype != HXQ_F32 && dy_dtype != HXQ_BF16) return HXQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || nnz < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || nnz > kMaxDim)
+    return HXQ_ERR_SHAPE;
   if (fmt == HXQ_FMT_PK12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
+  if (M == 0 || N == 0 || K == 0) return 0;
+  // the kernel AUTO would pick with aligned pointers
+  hxq::BwdArgs a = {};
+  a.indices = reinterpret_cast<const uint8_t*>(uintptr_t(256));
+  a.dy = reinterpret_cast<const void*>(uintptr_t(256));
+  a.dx = reinterpret_cast<float*>(uintptr_t(256));
+  a.dy_bf16 = dy_dtype == HXQ_BF16;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  if (M >= kBwdMfmaMinM && hxq::bwdx_mfma_ok(a, fmt == HXQ_FMT_PK12)) {
+    const hxq::BwdMPlan p = hxq::bwdx_mfma_plan(a.M, a.N, a.K, nnz);
+    return p.split_bytes + p.bin_bytes;
+  }
   return hxq::bwdx_workspace_bytes((int)M, (int)N, (int)K);
 }
 

@@ -344,28 +344,25 @@ __global__ __launch_bounds__(bx::THREADS) void bwdx_valu(BwdArgs ba) {
   }
 }
 
-// dx[i] = sum over the splits of ws[s][i], in a fixed order: a workgroup
-// takes 64 consecutive elements (one per lane); wave w sums splits w, w + 4,
-// ... with all its loads issued together, and the four wave sums are added
-// in wave order.  S <= 64.
+// dx[i] = sum over the splits of ws[s][i], added in split order.  VEC: four
+// consecutive elements per thread (16-byte loads and stores).
+template <bool VEC>
 __global__ __launch_bounds__(256) void bwdx_reduce(const float* __restrict__ ws, float* __restrict__ dx, int64_t n,
                                                    int S) {
-  __shared__ float part[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
-  const int64_t ic = i < n ? i : n - 1;
-  float v[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int s = wave + 4 * q;
-    v[q] = s < S ? ws[(int64_t)s * n + ic] : 0.f;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (VEC ? 4 : 1);
+  if (i >= n) return;
+  if (VEC) {
+    float4 v = *reinterpret_cast<const float4*>(ws + i);
+    for (int s = 1; s < S; ++s) {
+      const float4 t = *reinterpret_cast<const float4*>(ws + (int64_t)s * n + i);
+      v = make_float4(v.x + t.x, v.y + t.y, v.z + t.z, v.w + t.w);
+    }
+    *reinterpret_cast<float4*>(dx + i) = v;
+  } else {
+    float v = ws[i];
+    for (int s = 1; s < S; ++s) v += ws[(int64_t)s * n + i];
+    dx[i] = v;
   }
-  float a = 0.f;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) a += v[q];
-  part[wave][lane] = a;
-  __syncthreads();
-  if (wave == 0 && i < n) dx[i] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
 }
 
 __global__ __launch_bounds__(256) void fill_zero_f32(float* __restrict__ p, int64_t n) {
@@ -459,10 +456,17 @@ hipError_t launch_bwdx_valu(const BwdArgs& a0, bool pk12, hipStream_t stream) {
     e = a.dy_bf16 ? launch_bx_v<false, true>(a, p.mt, vec, p.lpr, grid, stream)
                   : launch_bx_v<false, false>(a, p.mt, vec, p.lpr, grid, stream);
   if (e != hipSuccess || S == 1) return e;
-  const int64_t n = (int64_t)a.M * a.K;
-  const int64_t rb = (n + 63) / 64;
-  if (rb > INT_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(bwdx_reduce, dim3((unsigned)rb), dim3(256), 0, stream, a.ws, a.dx, n, (int)S);
+  return launch_bwdx_reduce(a.ws, a.dx, (int64_t)a.M * a.K, (int)S, stream);
+}
+
+hipError_t launch_bwdx_reduce(const float* ws, float* dx, int64_t n, int S, hipStream_t stream) {
+  const bool vec = n % 4 == 0 && reinterpret_cast<uintptr_t>(dx) % 16 == 0 && reinterpret_cast<uintptr_t>(ws) % 16 == 0;
+  const int64_t rb = (n + (vec ? 1023 : 255)) / (vec ? 1024 : 256);
+  if (rb > INT_MAX || S > 64) return hipErrorInvalidConfiguration;
+  if (vec)
+    hipLaunchKernelGGL(bwdx_reduce<true>, dim3((unsigned)rb), dim3(256), 0, stream, ws, dx, n, S);
+  else
+    hipLaunchKernelGGL(bwdx_reduce<false>, dim3((unsigned)rb), dim3(256), 0, stream, ws, dx, n, S);
   return hipGetLastError();
 }
 

@@ -193,5 +193,14 @@ bool bwdx_vec_ok(const BwdArgs& a, bool pk12);
 BwdPlan bwdx_plan(int M, int N, int K);
 int64_t bwdx_workspace_bytes(int M, int N, int K);
 hipError_t launch_bwdx_valu(const BwdArgs& a, bool pk12, hipStream_t stream);
+hipError_t launch_bwdx_reduce(const float* ws, float* dx, int64_t n, int S, hipStream_t stream);
+
+struct BwdMPlan {
+  int ctw, mtiles, S, R, CT;
+  int64_t split_bytes, bin_bytes;
+};
+bool bwdx_mfma_ok(const BwdArgs& a, bool pk12);
+BwdMPlan bwdx_mfma_plan(int M, int N, int K, int64_t nnz);
+hipError_t launch_bwdx_mfma(const BwdArgs& a, bool pk12, hipStream_t stream);
 
 }  // namespace hxq
