@@ -172,6 +172,7 @@ __global__ __launch_bounds__(bm::THREADS, 1) void bwdx_mfma(BwdMArgs a) {
   __shared__ float cbf[PK12 ? 8192 : 256];  // fp32 codebook for the patches
   __shared__ int bsl[MAXST * 5];             // per step: bin starts of the 4 waves and the end
   __shared__ int ovf;
+  __shared__ uint32_t pslot[WAVES * 64];     // patch words on their way to their owner lanes
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -335,17 +336,39 @@ __global__ __launch_bounds__(bm::THREADS, 1) void bwdx_mfma(BwdMArgs a) {
         break;
     }
   };
+  // the bin's first 64 words are in lanes 0..63 (one each): every lane with
+  // a word writes it to its owner lane's LDS slot, every lane applies the word
+  // it finds in its own slot (per-lane selects, no branches), and a round
+  // repeats only for the rare words that lost a slot to another word of the
+  // same owner
+  uint32_t* slot = pslot + wave * 64;
   auto patch = [&](const Hits& h, auto rare_c) {
     // (the empty asm uses the word here, in straight-line code, so the wait
-    // for its load counts only what was issued after it; read first inside
-    // the loop, it would wait for every load in flight)
+    // for its load counts only what was issued after it)
     uint32_t hw = h.w;
     asm volatile("" : "+v"(hw));
-    const int n1 = min(h.n, 64);
-    for (int i = 0; i < n1; ++i) patch_one(__builtin_amdgcn_readlane(hw, i));
+    if (h.n == 0) return;
+    const uint32_t tagged = hw | 0x1000u;  // bit 12: slot holds a word
+    bool pending = lane < min(h.n, 64);
+    while (__ballot(pending)) {
+      if (pending) slot[hw & 63u] = tagged;
+      const uint32_t w = slot[lane];
+      if (w & 0x1000u) {
+        const uint32_t fq = ((w >> 6) & 7u) * 4u + ((w >> 9) & 3u);
+        const uint32_t keep = (w & 2048u) ? 0x0000ffffu : 0xffff0000u;
+        const uint32_t put = ((w >> 16) * 0x10001u) & ~keep;
+#pragma unroll
+        for (int ff = 0; ff < 8; ++ff)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+            if (fq == (uint32_t)(ff * 4 + qq)) A[ff][qq] = (A[ff][qq] & keep) | put;
+      }
+      if (pending && slot[hw & 63u] == tagged) pending = false;
+      slot[lane] = 0u;
+    }
     // words past the first 64 of a bin: only in the copy of the loop for
-    // workgroups that have such bins (its loads would make the waits after
-    // it count every load in flight)
+    // workgroups that have such bins (scalar loads, waited for in the same
+    // asm block)
     if (!decltype(rare_c)::value) return;
     for (int i = 64; i < h.n; ++i) {
       const uint32_t* wp = a.bpat + h.b + i;
@@ -397,6 +420,7 @@ __global__ __launch_bounds__(bm::THREADS, 1) void bwdx_mfma(BwdMArgs a) {
   };
   // does any bin of this workgroup hold more than 64 patch words?
   if (tid == 0) ovf = 0;
+  pslot[tid] = 0u;
   __syncthreads();
   if (a.CT > 0)
     for (int i = tid; i < steps * 4; i += THREADS) {
