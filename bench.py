@@ -15,9 +15,10 @@ value: algorithmic GB/s of the step (the compressed bytes the method must
 move: indices, codebooks, sidecar triplets, x once per launch, bias, y) over
 the GPU time of the timed steps.  Also reported: the same step issued as seven
 single-layer calls, the M = 8 step, the bf16 prefill GEMM at M = 2048
-(TFLOP/s; u8 layer set and two pk12 layers), the read bandwidth of a plain streaming kernel over the same
-rotated buffers, the roofline of the dominant launch (gate|up) and the CPU
-oracle baseline.
+(TFLOP/s; u8 layer set and two pk12 layers), the input gradient dx = dy W of
+the layer set (M = 1 fp32 in GB/s, M = 2048 bf16 in TFLOP/s), the read
+bandwidth of a plain streaming kernel over the same rotated buffers, the
+roofline of the dominant launch (gate|up) and the CPU oracle baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -136,6 +137,72 @@ class LayerCall:
         st = self.fn(*self.args)
         if st != 0:
             raise RuntimeError("HelixLinear forward failed with status %d" % st)
+
+
+class BwdCall:
+    """One pre-marshalled hxq_linear_bwd_x call (dx = dy W, the input gradient)."""
+
+    def __init__(self, L, B, d, dy, dx, M, N, K, stream, ws):
+        self.fn = L.hxq_linear_bwd_x
+        dyt = B.HXQ_BF16 if dy.element_size() == 2 else B.HXQ_F32
+        self.args = (B.HXQ_FMT_U8, d["codebook"].data_ptr(), d["indices"].data_ptr(), d["rows"].data_ptr(),
+                     d["cols"].data_ptr(), d["deltas"].data_ptr(), d["rows"].numel(), dy.data_ptr(), dyt,
+                     dx.data_ptr(), M, N, K, ws.data_ptr(), ws.numel(), stream)
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError("hxq_linear_bwd_x failed with status %d" % st)
+
+
+def bwd_bytes(l, M, dy_bytes):
+    """Bytes the input gradient of one u8 layer must move: index storage,
+    codebook, sidecar triplets, dy once and the fp32 dx."""
+    return l.N * l.K + 256 * 4 + 12 * l.nnz + M * l.N * dy_bytes + 4 * M * l.K
+
+
+def input_gradient(torch, L, B, layers, devs, M, dtype, steps, warmup, stream):
+    """dx = dy W for every layer of the set, one call per layer (devs[r][i]:
+    copy r of layer i).  Returns per-layer averages and the seven-layer step."""
+    import numpy as np
+
+    rng = np.random.Generator(np.random.PCG64(77))
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    dys = [torch.from_numpy(rng.standard_normal((M, l.N)).astype(np.float32)).cuda().to(tdt) for l in layers]
+    dxs = [torch.empty((M, l.K), dtype=torch.float32, device="cuda") for l in layers]
+    need = max(L.hxq_linear_bwd_x_workspace(B.HXQ_FMT_U8, B.HXQ_F32 if dtype == "f32" else B.HXQ_BF16, M, l.N,
+                                            l.K, l.nnz) for l in layers)
+    ws = torch.empty(max(int(need), 16), dtype=torch.uint8, device="cuda")
+    calls = [[BwdCall(L, B, row[i], dys[i], dxs[i], M, l.N, l.K, stream, ws) for i, l in enumerate(layers)]
+             for row in devs]
+    total = time_steps(torch, calls, steps, warmup)
+    avg = []
+    for i in range(len(layers)):
+        ti = time_steps(torch, [[row[i]] for row in calls], steps, 1)
+        avg.append(ti / steps)
+    xb = 4 if dtype == "f32" else 2
+    rows = []
+    for l, m in zip(layers, avg):
+        r = dict(layer=l.name, N=l.N, K=l.K, avg_us=round(m * 1e3, 3))
+        if M == 1:
+            r["gbs"] = round(bwd_bytes(l, M, xb) / (m * 1e-3) / 1e9, 1)
+        else:
+            r["tflops"] = round(2.0 * M * l.N * l.K / (m * 1e-3) / 1e12, 1)
+        rows.append(r)
+    step_us = total / steps * 1e3
+    out = dict(M=M, dy_dtype=dtype, step_us=round(step_us, 2), layers=rows, workspace_bytes=int(need))
+    if M == 1:
+        gbs = sum(bwd_bytes(l, M, xb) for l in layers) / (step_us * 1e-6) / 1e9
+        out.update(workload="input gradient dx = dy W of the Qwen2.5-3B-shaped u8 layer set, M=1, fp32 dy, "
+                            "one call per layer, rotating copies", gbs=round(gbs, 1),
+                   frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        tfs = sum(2.0 * M * l.N * l.K for l in layers) / (step_us * 1e-6) / 1e12
+        out.update(workload="input gradient dx = dy W of the Qwen2.5-3B-shaped u8 layer set, M=%d, bf16 dy "
+                            "(bf16 matrix cores), one call per layer" % M, tflops=round(tfs, 1),
+                   frac_of_mfma_peak=round(tfs / MFMA_BF16_PEAK_TFS, 4))
+    del dys, dxs, ws
+    return out
 
 
 def hold_gpu(torch, ms):
@@ -414,6 +481,10 @@ def main(argv=None):
                     for l, b, m in zip(layers, s1.layer_bytes, avg1)])
         extras["stream_ceiling"] = stream_ceiling(torch, L, s1, args.steps)
         log("stream ceiling %.1f GB/s" % extras["stream_ceiling"]["gbs"])
+        extras["input_gradient_m1"] = input_gradient(torch, L, B, layers, s1.devs, 1, "f32", args.steps,
+                                                     args.warmup, stream)
+        log("input gradient M=1 step %.1f us, %.1f GB/s" % (extras["input_gradient_m1"]["step_us"],
+                                                            extras["input_gradient_m1"]["gbs"]))
     del s1
     torch.cuda.empty_cache()
 
@@ -460,6 +531,10 @@ def main(argv=None):
                                                           tflops=round(2.0 * M * l.N * l.K / (m * 1e-3) / 1e12, 1))
                                                      for l, m in zip(layers, avgp)])
         log("prefill M=2048 step %.1f us, %.1f TFLOP/s" % (total_p / steps * 1e3, tfs))
+        extras["input_gradient_m2048"] = input_gradient(torch, L, B, layers, sp.devs, M, "bf16", steps,
+                                                        max(1, args.warmup // 5), stream)
+        log("input gradient M=2048 step %.1f us, %.1f TFLOP/s" % (extras["input_gradient_m2048"]["step_us"],
+                                                                  extras["input_gradient_m2048"]["tflops"]))
         del sp
         torch.cuda.empty_cache()
         extras["prefill_pk12"] = prefill_pk12(torch, L, B, stream, M, steps)
