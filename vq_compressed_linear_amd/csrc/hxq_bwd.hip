@@ -351,16 +351,34 @@ __global__ __launch_bounds__(256) void bwdx_reduce(const float* __restrict__ ws,
                                                    int S) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (VEC ? 4 : 1);
   if (i >= n) return;
+  // loads go out sixteen splits at a time (a plain loop would wait for each
+  // before issuing the next); the adds stay in split order
   if (VEC) {
     float4 v = *reinterpret_cast<const float4*>(ws + i);
-    for (int s = 1; s < S; ++s) {
+    int s = 1;
+    for (; s + 16 <= S; s += 16) {
+      float4 t[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) t[u] = *reinterpret_cast<const float4*>(ws + (int64_t)(s + u) * n + i);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v = make_float4(v.x + t[u].x, v.y + t[u].y, v.z + t[u].z, v.w + t[u].w);
+    }
+    for (; s < S; ++s) {
       const float4 t = *reinterpret_cast<const float4*>(ws + (int64_t)s * n + i);
       v = make_float4(v.x + t.x, v.y + t.y, v.z + t.z, v.w + t.w);
     }
     *reinterpret_cast<float4*>(dx + i) = v;
   } else {
     float v = ws[i];
-    for (int s = 1; s < S; ++s) v += ws[(int64_t)s * n + i];
+    int s = 1;
+    for (; s + 16 <= S; s += 16) {
+      float t[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) t[u] = ws[(int64_t)(s + u) * n + i];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v += t[u];
+    }
+    for (; s < S; ++s) v += ws[(int64_t)s * n + i];
     dx[i] = v;
   }
 }

@@ -25,7 +25,7 @@
 // Sidecar: a prologue kernel turns every distinct (row, col) of the triplets
 // into a patch word, bf16(C + deltas) with the lane, fragment and operand
 // half that hold that weight, sorted into (32-row step, 128-column) bins in
-// stored order, in the workspace.  A wave reads its bin for the step and
+// the workspace.  A wave reads its bin for the step and
 // overwrites the operand halves its words name.
 //
 // Row splits (to fill the GPU) store into the workspace and are summed by
@@ -49,60 +49,65 @@ constexpr int MAXCT = 128;          // bins per step: K <= 16384
 constexpr int MAXST = 1024;         // steps per row split (bin starts kept in LDS)
 }  // namespace bm
 
-// ---- sidecar patches: one 64-thread workgroup per 32-row step.  Every
-// distinct (row, col) of the step becomes one patch word, sorted into its
-// 128-column bin in stored order: the owner lane (bits 0-5: 16 (row / 8 in
+// ---- sidecar patches: one 256-thread workgroup per 32-row step.  Every
+// distinct (row, col) of the step becomes one patch word, placed in its
+// 128-column bin: the owner lane (bits 0-5: 16 (row / 8 in
 // the step) + column / 8 in the bin), the fragment (6-8: column % 8), the
 // operand word (9-10) and half (11) of its row, and the bf16 value (16-31)
 // of the codebook value plus the run's deltas, added in fp32 in stored order
 // and rounded once to nearest even.
 template <bool PK12>
-__global__ __launch_bounds__(64) void bwdx_bin(const float* __restrict__ codebook, const uint8_t* __restrict__ indices,
+__global__ __launch_bounds__(256) void bwdx_bin(const float* __restrict__ codebook, const uint8_t* __restrict__ indices,
                                                const int32_t* __restrict__ rows, const int32_t* __restrict__ cols,
                                                const float* __restrict__ deltas, int64_t nnz, int N, int K, int CT,
                                                int* __restrict__ binstart, uint32_t* __restrict__ bpat) {
   __shared__ int off[bm::MAXCT];
   __shared__ int run[bm::MAXCT];
-  const int s = blockIdx.x, lane = threadIdx.x;
+  const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int r_lo = s * bm::STEP, r_hi = min(N, r_lo + bm::STEP);
   const int64_t lo = wave_lower_bound_rows_near(rows, nnz, r_lo, (int64_t)((double)nnz * r_lo / N));
   const int64_t hi = wave_lower_bound_rows_near(rows, nnz, r_hi, (int64_t)((double)nnz * r_hi / N));
-  for (int i = lane; i < bm::MAXCT; i += 64) {
+  for (int i = tid; i < bm::MAXCT; i += 256) {
     off[i] = 0;
     run[i] = 0;
   }
   __syncthreads();
   // a triplet heads its run when the one before it has another coordinate
   auto head = [&](int64_t e, int r, int c) { return e == 0 || rows[e - 1] != r || cols[e - 1] != c; };
-  for (int64_t e = lo + lane; e < hi; e += 64) {
+  for (int64_t e = lo + tid; e < hi; e += 256) {
     const int r = rows[e], c = cols[e];
     if (head(e, r, c)) atomicAdd(&off[c / bm::CWW], 1);
   }
   __syncthreads();
-  // exclusive prefix over the bin counts, two bins per lane
+  // exclusive prefix over the bin counts, two bins per lane of wave 0
   const int b0 = 2 * lane, b1 = 2 * lane + 1;
-  const int c0 = b0 < CT ? off[b0] : 0, c1 = b1 < CT ? off[b1] : 0;
-  int inc = c0 + c1;
+  int c0 = 0, c1 = 0, inc = 0;
+  if (tid < 64) {
+    c0 = b0 < CT ? off[b0] : 0;
+    c1 = b1 < CT ? off[b1] : 0;
+    inc = c0 + c1;
 #pragma unroll
-  for (int d = 1; d < 64; d *= 2) {
-    const int t = __shfl_up(inc, d, 64);
-    if (lane >= d) inc += t;
+    for (int d = 1; d < 64; d *= 2) {
+      const int t = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += t;
+    }
   }
-  const int exc = inc - c0 - c1;
   __syncthreads();
-  if (b0 < CT) off[b0] = exc;
-  if (b1 < CT) off[b1] = exc + c0;
-  int* bs = binstart + (int64_t)s * (CT + 1);
-  if (b0 < CT) bs[b0] = (int)lo + exc;
-  if (b1 < CT) bs[b1] = (int)lo + exc + c0;
-  const int total = __shfl(inc, 63, 64);  // distinct coordinates in the step
-  if (lane == 0) bs[CT] = (int)lo + total;
+  if (tid < 64) {
+    const int exc = inc - c0 - c1;
+    if (b0 < CT) off[b0] = exc;
+    if (b1 < CT) off[b1] = exc + c0;
+    int* bs = binstart + (int64_t)s * (CT + 1);
+    if (b0 < CT) bs[b0] = (int)lo + exc;
+    if (b1 < CT) bs[b1] = (int)lo + exc + c0;
+    const int total = __shfl(inc, 63, 64);  // distinct coordinates in the step
+    if (lane == 0) bs[CT] = (int)lo + total;
+  }
   __syncthreads();
   const int64_t pitch = PK12 ? (int64_t)((K + 3) / 4) * 3 : (int64_t)K;
-  // stable scatter, 64 triplets at a time in stored order; heads of one bin
-  // are ranked by lane order
-  for (int64_t base = lo; base < hi; base += 64) {
-    const int64_t e = base + lane;
+  // the words, 256 triplets at a time
+  for (int64_t base = lo; base < hi; base += 256) {
+    const int64_t e = base + tid;
     const bool v = e < hi;
     const int64_t ec = v ? e : hi - 1;
     const int r = rows[ec], c = cols[ec];
@@ -124,19 +129,10 @@ __global__ __launch_bounds__(64) void bwdx_bin(const float* __restrict__ codeboo
       word = (uint32_t)(16 * (jj >> 3) + (cw >> 3)) | ((uint32_t)(cw & 7) << 6) | ((uint32_t)((jj & 7) >> 1) << 9) |
              ((uint32_t)(jj & 1) << 11) | (f32_to_bf16_rne(val) << 16);
     }
-    const int b = c / bm::CWW;
-    uint64_t pending = __ballot(h);
+    // a word's place within its bin does not matter (each names its own
+    // operand half), so positions come from an LDS counter per bin
     int pos = 0;
-    while (pending) {
-      const int leader = __builtin_ctzll(pending);
-      const int bl = __shfl(b, leader, 64);
-      const uint64_t same = __ballot(h && b == bl);
-      if (h && b == bl) pos = off[bl] + run[bl] + __popcll(same & ((1ull << lane) - 1));
-      __syncthreads();
-      if (lane == leader) run[bl] += __popcll(same);
-      __syncthreads();
-      pending &= ~same;
-    }
+    if (h) pos = off[c / bm::CWW] + atomicAdd(&run[c / bm::CWW], 1);
     if (h) bpat[lo + pos] = word;
   }
 }
@@ -514,10 +510,10 @@ hipError_t launch_bwdx_mfma(const BwdArgs& a, bool pk12, hipStream_t stream) {
     q += al((int64_t)nsteps * (p.CT + 1) * 4);
     uint32_t* bpat = reinterpret_cast<uint32_t*>(q);
     if (pk12)
-      hipLaunchKernelGGL(bwdx_bin<true>, dim3((unsigned)nsteps), dim3(64), 0, stream, a.codebook, a.indices, a.sc_rows,
+      hipLaunchKernelGGL(bwdx_bin<true>, dim3((unsigned)nsteps), dim3(256), 0, stream, a.codebook, a.indices, a.sc_rows,
                          a.sc_cols, a.sc_deltas, a.nnz, a.N, a.K, p.CT, binstart, bpat);
     else
-      hipLaunchKernelGGL(bwdx_bin<false>, dim3((unsigned)nsteps), dim3(64), 0, stream, a.codebook, a.indices, a.sc_rows,
+      hipLaunchKernelGGL(bwdx_bin<false>, dim3((unsigned)nsteps), dim3(256), 0, stream, a.codebook, a.indices, a.sc_rows,
                          a.sc_cols, a.sc_deltas, a.nnz, a.N, a.K, p.CT, binstart, bpat);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
