@@ -235,3 +235,27 @@ def test_bwd_x_mfma_needs_its_workspace():
     with pytest.raises(hx.HxqError):
         hx.hxq_linear_bwd_x(hx.HXQ_FMT_U8, d["codebook"], d["indices"], d["rows"], d["cols"], d["deltas"], dy, dx,
                             K, variant=hx.HXQ_VARIANT_GEMM_BF16, workspace=t.zeros(4, dtype=t.uint8, device="cuda"))
+
+
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_layer_autograd_input_gradient(fmt, xdt):
+    # HelixLinear under autograd: y = layer(x), y.backward(dy) leaves dy W in
+    # x.grad (computed by the library), in x's dtype
+    t = G.torch()
+    N, K, M = 1000, 1024, 5
+    G.say("layer autograd %s x=%s" % (fmt, xdt))
+    lay = gen.random_layer(105, N, K, fmt, nnz=N * K // 1000, duplicates=True)
+    m = hx.HelixLinear.from_layer(lay, device="cuda")
+    rng = np.random.Generator(np.random.PCG64(106))
+    x_np = rng.standard_normal((M, K)).astype(np.float32)
+    x = G.dev_x(x_np if xdt == "f32" else gen.to_bf16_bits(x_np), xdt).requires_grad_(True)
+    y = m(x)
+    assert y.requires_grad and y.dtype == t.float32
+    dy_np = _dy(107, M, N, "f32")
+    y.backward(t.from_numpy(dy_np).cuda())
+    t.cuda.synchronize()
+    assert x.grad is not None and x.grad.dtype == x.dtype
+    Y, B = _oracle(lay, dy_np, "f32")
+    tol = G.TOL_FP32 if xdt == "f32" else G.TOL_BF16  # bf16 x: the gradient is rounded to bf16
+    G.check(x.grad.float(), Y, B, tol, "layer autograd %s %s" % (fmt, xdt))

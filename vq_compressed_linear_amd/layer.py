@@ -3,6 +3,9 @@
 The layer keeps the compressed form resident on the GPU (codebook, indices or
 packed 12-bit indices, sidecar triplets, bias) and calls the library for every
 forward; the dense weight is never built (model cards, "What is HelixCode?").
+The weights are frozen (model cards, "Good to Know": LoRA adapters train
+through the layer): when x requires a gradient, the backward pass computes
+dx = dy W with the library's input-gradient kernels and nothing else.
 """
 
 from __future__ import annotations
@@ -50,6 +53,13 @@ class HelixLinear:
     def forward(self, x, out=None, stream=None, variant: int = B.HXQ_VARIANT_AUTO):
         import torch
 
+        if x.requires_grad and torch.is_grad_enabled() and out is None:
+            return _helix_fn().apply(x, self)
+        return self._forward(x, out, stream, variant)
+
+    def _forward(self, x, out=None, stream=None, variant: int = B.HXQ_VARIANT_AUTO):
+        import torch
+
         if x.shape[-1] != self.in_features:
             raise ValueError("x has %d features, layer expects %d" % (x.shape[-1], self.in_features))
         lead = x.shape[:-1]
@@ -63,6 +73,22 @@ class HelixLinear:
 
     __call__ = forward
 
+    def backward_input(self, dy, out=None, stream=None, variant: int = B.HXQ_VARIANT_AUTO):
+        """dx = dy W (the gradient of the forward's output with respect to x) for
+        dy [..., out_features] float32 or bfloat16; dx is float32 [..., in_features]."""
+        import torch
+
+        if dy.shape[-1] != self.out_features:
+            raise ValueError("dy has %d features, layer has %d outputs" % (dy.shape[-1], self.out_features))
+        lead = dy.shape[:-1]
+        dy2 = dy.reshape(-1, self.out_features).contiguous()
+        dx = out if out is not None else torch.empty((dy2.shape[0], self.in_features), dtype=torch.float32,
+                                                     device=dy.device)
+        fmt = B.HXQ_FMT_U8 if self.fmt == "u8" else B.HXQ_FMT_PK12
+        B.hxq_linear_bwd_x(fmt, self.codebook, self.indices, self.sc_rows, self.sc_cols, self.sc_deltas, dy2, dx,
+                           self.in_features, stream=stream, variant=variant)
+        return dx.reshape(*lead, self.in_features)
+
     def compressed_bytes(self) -> int:
         n = 0
         for t in (self.codebook, self.indices, self.sc_rows, self.sc_cols, self.sc_deltas):
@@ -74,3 +100,29 @@ class HelixLinear:
         return "fmt=%s, in=%d, out=%d, nnz=%d" % (
             self.fmt, self.in_features, self.out_features,
             0 if self.sc_rows is None else self.sc_rows.numel())
+
+
+_FN = None
+
+
+def _helix_fn():
+    """torch.autograd.Function over the library: forward y = x W^T + b, backward
+    dx = dy W (no gradient for the frozen compressed weights)."""
+    global _FN
+    if _FN is None:
+        import torch
+
+        class HelixFn(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, x, layer):
+                ctx.layer = layer
+                ctx.x_dtype = x.dtype
+                return layer._forward(x.detach())
+
+            @staticmethod
+            def backward(ctx, dy):
+                dx = ctx.layer.backward_input(dy.contiguous())
+                return dx.to(ctx.x_dtype), None
+
+        _FN = HelixFn
+    return _FN
