@@ -259,3 +259,20 @@ def test_layer_autograd_input_gradient(fmt, xdt):
     Y, B = _oracle(lay, dy_np, "f32")
     tol = G.TOL_FP32 if xdt == "f32" else G.TOL_BF16  # bf16 x: the gradient is rounded to bf16
     G.check(x.grad.float(), Y, B, tol, "layer autograd %s %s" % (fmt, xdt))
+
+
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_x_vector_kernel_long_runs(fmt, dtype):
+    # many tiles, so few row splits: each workgroup's run (4096 rows) is longer
+    # than the rows of dy it stages at once (256 at 8 tokens), so dy is staged
+    # again mid-run and the sidecar terms read dy from global memory; bf16 dy
+    # forced onto the vector kernel
+    N, K, M = 8192, 4096, 64
+    G.say("bwd_x vector long runs %s %s" % (fmt, dtype))
+    lay = gen.random_layer(108, N, K, fmt, nnz=N * K // 1000, duplicates=True)
+    d = G.dev_layer(lay)
+    dy_np = _dy(109, M, N, dtype)
+    dx = _run(lay, d, G.dev_x(dy_np, dtype), variant=hx.HXQ_VARIANT_GEMV_VALU)
+    Y, B = _oracle(lay, dy_np, dtype)
+    G.check(dx, Y, B, G.TOL_FP32, "bwd_x vector long runs %s %s" % (fmt, dtype))
