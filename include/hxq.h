@@ -212,8 +212,9 @@ int hxq_dequant_bf16(int fmt, const float* codebook, const uint8_t* indices,
  * rounded once to bf16, as in the forward bf16 GEMM.  Row splits are added in
  * a fixed order; on the vector path, sidecar terms that land in the same
  * column of one workgroup's tile are added in no fixed order.
- * N == 0 sets dx to zero; M == 0 or K == 0 does nothing.  Work is one or two
- * launches on `stream`.
+ * N == 0 sets dx to zero; M == 0 or K == 0 does nothing.  Work is one to
+ * three launches on `stream` (sidecar binning, the product, the sum of the
+ * row splits).
  * Errors: HXQ_ERR_SHAPE for an unknown fmt, negative or oversized M, N, K, nnz,
  * negative workspace_bytes, or odd K with pk12; HXQ_ERR_DTYPE for an unknown
  * dy_dtype; HXQ_ERR_NULL; HXQ_ERR_ALIGN (dy to its element size, dx, codebook,

@@ -19,14 +19,15 @@
 // holds column kc + 8 i + f in its row i.  The lane's 8 dy values of those
 // rows per token block (16 bytes) are the B operand.  In the result, lane l
 // holds for token 16 b + l16 the 32 consecutive columns kc + 32 g .. + 31, so
-// the epilogue is whole float4 stores.  Index bytes load two steps ahead, dy
-// and sidecar patches one step ahead.
+// the epilogue is whole float4 stores.  Index bytes, dy and the sidecar
+// patches of a step are loaded two steps ahead.
 //
 // Sidecar: a prologue kernel turns every distinct (row, col) of the triplets
 // into a patch word, bf16(C + deltas) with the lane, fragment and operand
 // half that hold that weight, sorted into (32-row step, 128-column) bins in
-// the workspace.  A wave reads its bin for the step and
-// overwrites the operand halves its words name.
+// the workspace.  A wave reads its bin for the step (its start from LDS);
+// each lane with a word passes it to the owner lane through an LDS slot, and
+// the owner overwrites the operand half it names.
 //
 // Row splits (to fill the GPU) store into the workspace and are summed by
 // the reduction kernel of the vector path.
