@@ -9,10 +9,11 @@
 // and "2D vector quantization"), read here along its columns and never formed.
 //
 // bwdx_valu: the general kernel (fp32 or bf16 dy, any M, N, K).  A workgroup
-// owns a column tile, a run of R rows and up to 8 tokens.  Tiles are 128 columns (lane l holds
-// columns 8 (l % 16) .. + 7 in one of four rows at a time, l / 16, so a load
-// instruction reads a whole 128-byte line of four rows) or, for long rows,
-// 512 columns (one row per instruction); the workgroup's row positions take
+// owns a column tile, a run of R rows and up to 8 tokens.  Tiles are 128
+// columns (lane l holds columns 8 (l % 16) .. + 7 in one of four rows at a
+// time, l / 16, so a load instruction reads a whole 128-byte line of four
+// rows) or, for long rows, 512 columns (one row per instruction); the
+// workgroup's row positions take
 // interleaved rows of the run.  Per row a lane loads its 8 index bytes (u8)
 // or 6 (pk12: four pairs), gathers the codebook values from LDS and adds
 // dy[m][n] * w to its 8 x MT accumulators (dy staged in LDS).  The first
@@ -24,8 +25,8 @@
 // loads issued at the start).  The tile is stored into dx, or, when the rows
 // are split over several workgroups to fill the GPU, into its split of a
 // caller-provided workspace, which a second kernel sums in split order.
-// (Device-wide fp32 atomics are too slow to combine the splits: a few per
-// nanosecond over the whole chip.)
+// (Device-wide fp32 atomics are too slow to combine the splits: about a
+// dozen per nanosecond over the whole chip.)
 
 #include "hxq_device.h"
 #include "hxq_launch.h"
