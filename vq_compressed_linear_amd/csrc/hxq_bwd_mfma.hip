@@ -395,15 +395,27 @@ __global__ __launch_bounds__(bm::THREADS, 1) void bwdx_mfma(BwdMArgs a) {
       load_B(st + 2, B2);
       load_H(st + 2, H2);
     }
+    // this step's matrix ops and the next step's operand gathers in one
+    // block, interleaved (one matrix op, then two LDS reads (u8; one for
+    // pk12, which gathers half as often) and two vector ops), so the gathers
+    // run while the matrix unit is busy; past the last step the gathers read
+    // a stand-in row and go unused
+    const u32x4 Acur[8] = {A[0], A[1], A[2], A[3], A[4], A[5], A[6], A[7]};
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-      const bf16x8 af = __builtin_bit_cast(bf16x8, A[f]);
+      const bf16x8 af = __builtin_bit_cast(bf16x8, Acur[f]);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, B0[t]), acc[t][f], 0, 0, 0);
     }
+    build_A(I1);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // matrix op
+      __builtin_amdgcn_sched_group_barrier(0x0100, PK12 ? 1 : 2, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x0002, 2, 0);  // vector op
+    }
     if (st + 1 < steps) {
-      build_A(I1);
       patch(H1, rare_c);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
