@@ -208,6 +208,26 @@ def test_dense_sidecar_rows(fmt, variant, M, xdt):
           what="heavy sidecar")
 
 
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
+def test_gemm_full_sidecar_block(fmt):
+    """Every weight of a 16-row x 64-column block in the sidecar (1024 triplets
+    in one stage of one wave, far past 64) plus a second dense block and
+    scattered entries, within the tile's patch area."""
+    N, K = 64, 256
+    lay = gen.random_layer(41, N, K, fmt)
+    rng = np.random.Generator(np.random.PCG64(9))
+    r0, c0 = np.meshgrid(np.arange(16), np.arange(64), indexing="ij")
+    r1, c1 = np.meshgrid(np.arange(16, 32), np.arange(64, 128), indexing="ij")
+    rows = np.concatenate([r0.ravel(), r1.ravel(), rng.integers(0, N, 200)])
+    cols = np.concatenate([c0.ravel(), c1.ravel(), rng.integers(0, K, 200)])
+    order = np.lexsort((cols, rows))
+    lay.rows = rows[order].astype(np.int32)
+    lay.cols = cols[order].astype(np.int32)
+    lay.deltas = (0.05 * rng.standard_normal(rows.size)).astype(np.float32)
+    G.say("gemm full sidecar block %s nnz=%d" % (fmt, rows.size))
+    _case(lay, 150, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=3, what="full sidecar block")
+
+
 @pytest.mark.parametrize("fmt,variant,M,xdt", [
     ("u8", hx.HXQ_VARIANT_GEMV_VALU, 8, "f32"), ("pk12", hx.HXQ_VARIANT_GEMV_VALU, 16, "f32"),
     ("u8", hx.HXQ_VARIANT_GEMM_BF16, 300, "bf16"), ("u8", hx.HXQ_VARIANT_GENERIC, 3, "f32")])

@@ -279,7 +279,9 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_bf16(GemmArgs ga) {
   using namespace gemm3;
   constexpr int BN = 16 * WAVES * FN;
   typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-  typedef u32x8 vecB[FN];  // operands of one stage: fragment j, words 0-3 sub-step 0, 4-7 sub-step 1
+  // operands of one stage in one vector: fragment j at words 8 j .. 8 j + 7,
+  // the first four for sub-step 0, the last four for sub-step 1
+  typedef uint32_t vecB __attribute__((ext_vector_type(8 * FN)));
   // u8: 64 copies per entry, bf16 in the upper half; pk12: entry e at byte 4 e,
   // bf16 of component 0 (even k) in the low half, component 1 in the high half
   __shared__ __align__(16) unsigned char cbs[PK12 ? 4096 * 4 : 256 * 256];
@@ -527,8 +529,8 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_bf16(GemmArgs ga) {
                            : d == 1 ? (__builtin_amdgcn_alignbit(iq[j][1], iq[j][0], 24) & 0xffffffu)
                            : d == 2 ? (__builtin_amdgcn_alignbit(iq[j][2], iq[j][1], 16) & 0xffffffu)
                                     : (iq[j][2] >> 8);
-          out[j][2 * d] = lds_load<uint32_t>((v & 0xfffu) << 2, cbs);
-          out[j][2 * d + 1] = lds_load<uint32_t>((v >> 12) << 2, cbs);
+          out[8 * j + 2 * d] = lds_load<uint32_t>((v & 0xfffu) << 2, cbs);
+          out[8 * j + 2 * d + 1] = lds_load<uint32_t>((v >> 12) << 2, cbs);
           continue;
         }
         const uint32_t wd = iq[j][d];
@@ -536,8 +538,8 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_bf16(GemmArgs ga) {
         const uint32_t f1 = lds_load<uint32_t>(byte_addr256<1>(wd, lane4), cbs);
         const uint32_t f2 = lds_load<uint32_t>(byte_addr256<2>(wd, lane4), cbs);
         const uint32_t f3 = lds_load<uint32_t>(byte_addr256<3>(wd, lane4), cbs);
-        out[j][2 * d] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
-        out[j][2 * d + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+        out[8 * j + 2 * d] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+        out[8 * j + 2 * d + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
       }
   };
   // patches: the bin of (stage st, this wave) and its first PRE words, read early
@@ -553,15 +555,20 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_bf16(GemmArgs ga) {
     for (int t = 0; t < PRE; ++t) pp.w[t] = patch[pp.q0 + t];
   };
   auto patch_one = [&](uint32_t ent, vecB& v) {
-    const uint32_t e = (ent >> 7) & 7u;  // uniform: the word is picked by register index
-    const uint32_t jj = (ent >> 10) & 3u;
     const uint32_t keep = (ent & 64u) ? 0x0000ffffu : 0xffff0000u;
     const uint32_t put = ((ent >> 16) * 0x10001u) & ~keep;
     const bool mine = lane == (int)(ent & 63u);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const uint32_t old = v[j][e];
-      v[j][e] = (mine && jj == (uint32_t)j) ? ((old & keep) | put) : old;
+    if constexpr (FN == 1) {
+      // one fragment: the compiler selects among the eight words (faster here
+      // than without the fragment test, as measured)
+      const uint32_t e = (ent >> 7) & 7u;
+      const uint32_t old = v[e];
+      v[e] = (mine && ((ent >> 10) & 3u) == 0u) ? ((old & keep) | put) : old;
+    } else {
+      // uniform (fragment, word): one indexed register read and write
+      const uint32_t at = ((ent >> 10) & 3u) * 8u + ((ent >> 7) & 7u);
+      const uint32_t old = v[at];
+      v[at] = mine ? ((old & keep) | put) : old;
     }
   };
   auto patch_apply = [&](const PatchPre& pp, vecB& v) {
@@ -616,8 +623,8 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_bf16(GemmArgs ga) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             if (e == (p >> 1)) {
-              const uint32_t old = v[j][e];
-              v[j][e] = (p & 1) ? ((old & 0xffffu) | (h << 16)) : ((old & 0xffff0000u) | h);
+              const uint32_t old = v[8 * j + e];
+              v[8 * j + e] = (p & 1) ? ((old & 0xffffu) | (h << 16)) : ((old & 0xffff0000u) | h);
             }
         }
         ++scur[j];
@@ -672,8 +679,8 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_bf16(GemmArgs ga) {
           const bf16x8 aop = *reinterpret_cast<const bf16x8*>(abuf + (u ? aoff1 : aoff0) + i * 2048);
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const u32x4 bw = u ? __builtin_shufflevector(Bc[j], Bc[j], 4, 5, 6, 7)
-                               : __builtin_shufflevector(Bc[j], Bc[j], 0, 1, 2, 3);
+            const u32x4 bw = u32x4{Bc[8 * j + 4 * u], Bc[8 * j + 4 * u + 1], Bc[8 * j + 4 * u + 2],
+                                   Bc[8 * j + 4 * u + 3]};
             // weights as the A operand, x as B: the result tile is y transposed,
             // so each lane ends up with four consecutive outputs of one token
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bw), aop, acc[i][j], 0, 0, 0);
