@@ -209,6 +209,17 @@ def test_dense_sidecar_rows(fmt, variant, M, xdt):
 
 
 @pytest.mark.parametrize("fmt", ["u8", "pk12"])
+def test_gemm_wide_tiles_ragged(fmt):
+    """2000 tokens x 4100 outputs: 256-output tiles take fewer rounds over the
+    CUs than 128-output ones, so the wide tiles run, with a 4-output last
+    tile and an 80-token last tile row."""
+    N, K, M = 4100, 128, 2000
+    G.say("gemm wide tiles ragged %s" % fmt)
+    lay = gen.random_layer(57, N, K, fmt, nnz=N * K // 1000, duplicates=True)
+    _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=5, what="wide tiles ragged")
+
+
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
 def test_gemm_full_sidecar_block(fmt):
     """Every weight of a 16-row x 64-column block in the sidecar (1024 triplets
     in one stage of one wave, far past 64) plus a second dense block and

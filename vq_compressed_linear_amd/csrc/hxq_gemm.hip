@@ -763,8 +763,9 @@ bool gemm2_path_ok(const LayerArgs& a, bool pk12) {
   return (int64_t)a.M * a.K * 2 < ((int64_t)1 << 32);
 }
 
-// Output tile width by how many tiles the launch has: 256 outputs when that
-// still gives every CU a tile, else 128.
+// Output tile width by rounds of tiles over the CUs: a 128-output tile takes
+// about as long as a 256-output one (the per-stage LDS work of a wave is the
+// same), so 256 outputs unless 128 needs no more rounds.
 hipError_t launch_gemm_grouped(const GemmSeg* segs, int nseg, bool pk12, const void* x, int M, int K,
                                hipStream_t stream) {
   if (nseg < 1 || nseg > kMaxSegments) return hipErrorInvalidValue;
@@ -774,14 +775,17 @@ hipError_t launch_gemm_grouped(const GemmSeg* segs, int nseg, bool pk12, const v
   ga.K = K;
   ga.tiles_m = (M + gemm3::BM - 1) / gemm3::BM;
   ga.nseg = nseg;
-  int64_t wide = 0;
+  int64_t wide = 0, narrow = 0;
   for (int i = 0; i < nseg; ++i) {
     ga.seg[i] = segs[i];
     wide += (int64_t)ga.tiles_m * ((segs[i].N + 255) / 256);
+    narrow += (int64_t)ga.tiles_m * ((segs[i].N + 127) / 128);
   }
   for (int i = nseg; i < kMaxSegments; ++i) ga.seg[i] = segs[0];
-  if (pk12) return wide >= device_cu_count() ? launch_gemm3<2, true>(ga, stream) : launch_gemm3<1, true>(ga, stream);
-  return wide >= device_cu_count() ? launch_gemm3<2, false>(ga, stream) : launch_gemm3<1, false>(ga, stream);
+  const int64_t cus = device_cu_count();
+  const bool use_wide = (wide + cus - 1) / cus < (narrow + cus - 1) / cus;
+  if (pk12) return use_wide ? launch_gemm3<2, true>(ga, stream) : launch_gemm3<1, true>(ga, stream);
+  return use_wide ? launch_gemm3<2, false>(ga, stream) : launch_gemm3<1, false>(ga, stream);
 }
 
 hipError_t launch_gemm2_bf16(const LayerArgs& a, bool pk12, hipStream_t stream) {
