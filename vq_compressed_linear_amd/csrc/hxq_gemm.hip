@@ -227,7 +227,9 @@ hipError_t launch_gemm_bf16(const LayerArgs& a, hipStream_t stream) {
 //   - Workgroup tile 128 tokens x (128 * FN) outputs.  Eight waves (two per
 //     SIMD, so one can issue while the other waits) sit side by side along the
 //     outputs; each owns 16 * FN outputs for all 128 tokens (8 x FN MFMA
-//     tiles, accumulators in AGPRs).
+//     tiles of fp32 accumulators, in ordinary VGPRs: at two waves per SIMD a
+//     wave has 256 registers in all).  FN is 2, or 1 when 128-output tiles
+//     need no more rounds over the CUs.
 //   - A k-stage is 64 deep.  x reaches the MFMAs through a ring of four LDS
 //     tiles; stages go in pairs with one barrier per pair, and the x of a
 //     stage is loaded into registers two stages before it is stored.  A tile
