@@ -410,7 +410,7 @@ def main(argv=None):
                     help="only run a plain 256 MiB device copy 10 times (for HBM counter scaling)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
 
