@@ -81,10 +81,14 @@ def test_grouped_token_groups_match_single_calls(fmt, M):
 
 
 @pytest.mark.parametrize("fmt,M,K", [("u8", 17, 2048), ("u8", 130, 2048), ("u8", 300, 1024), ("u8", 130, 96),
-                                      ("pk12", 17, 2048), ("pk12", 300, 1024), ("pk12", 130, 96)])
+                                      ("pk12", 17, 2048), ("pk12", 300, 1024), ("pk12", 130, 96),
+                                      ("u8", 2000, 256), ("pk12", 2000, 256)])
 def test_grouped_prefill_gemm(fmt, M, K):
     # bf16 x past the decode sizes: one matrix-core launch over all layers
-    # (K % 64 == 0), else one call per layer; both equal single-layer calls bitwise
+    # (K % 64 == 0), else one call per layer; both equal single-layer calls
+    # bitwise.  At 2000 tokens the grouped launch takes 256-output tiles while
+    # the 1000-output layer alone takes 128-output ones: the tile width does
+    # not change any output's summation order.
     G.say("grouped gemm %s M=%d K=%d" % (fmt, M, K))
     lays, ds = _group(fmt, [1000, 96, 2500], K, seed=M + K)
     x_np = _x(M + 1, M, K, "bf16")
