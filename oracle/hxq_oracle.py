@@ -47,7 +47,10 @@ bytes, one-hot column reconstruction, the u8/pk12 cross-format special case,
 and bf16 rounding against the library cast.  The input gradient is pinned by
 its own brute force, a hand-computed example, the constant-index closed form,
 one-hot rows, and the adjoint identity sum(dY * (Y - b)) = sum(dX * X) that
-ties it to the pinned forward.  No function here is unpinned.
+ties it to the pinned forward.  The tolerance scales (error_bound,
+error_bound_bwd and the bound of hxq_sidecar_add) are pinned by their own
+fsum brute force on square and non-square shapes and by a hand-worked example
+with exact values.  No function here is unpinned.
 """
 
 from __future__ import annotations
@@ -204,7 +207,9 @@ def hxq_linear_fwd_pk12(codebook2, packed, rows, cols, deltas, x, x_dtype, bias,
 def hxq_sidecar_add(rows, cols, deltas, x, x_dtype, N):
     """The sparse term alone: Z[m, r] = sum over triplets of delta * x[m, c]
     (the sidecar acting on the activations, W never formed).  Returns (Z, B)
-    with B = |X| @ |S|^T."""
+    with B[m, r] = sum over the triplets of row r of |delta| * |x[m, c]|: the
+    absolute values of the terms the sum adds, the scale of its rounding error
+    (at least |X| @ |S|^T, where repeated coordinates would cancel first)."""
     X = activations_f64(x, x_dtype)
     M = X.shape[0]
     r = np.asarray(rows, dtype=np.int64)

@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 from oracle import hxq_oracle as H
+import test_oracle_bound_pins as BP
 import test_oracle_pins as P
 
 PINS = [
@@ -29,6 +30,16 @@ PINS = [
     P.test_bwd_one_hot_rows_give_weight_rows,
     lambda: P.test_bwd_adjoint_of_forward("u8"),
     lambda: P.test_bwd_adjoint_of_forward("pk12"),
+    lambda: BP.test_bound_u8_bruteforce(7, 12, 3),
+    lambda: BP.test_bound_u8_bruteforce(6, 6, 4),
+    lambda: BP.test_bound_pk12_bruteforce(6, 16, 3),
+    BP.test_bound_bf16_activations_bruteforce,
+    lambda: BP.test_bound_bwd_u8_bruteforce(7, 12, 3),
+    lambda: BP.test_bound_bwd_u8_bruteforce(6, 6, 4),
+    BP.test_bound_sidecar_add_bruteforce,
+    BP.test_bound_golden_hand_example,
+    BP.test_bound_bwd_golden_hand_example,
+    BP.test_bound_sidecar_golden_hand_example,
 ]
 
 
@@ -102,6 +113,81 @@ def _bwd_sign_lost(W, DY):
     return DY @ np.abs(W)
 
 
+def _bound_scaled(W, X):
+    return 1000.0 * (np.abs(X) @ np.abs(W).T)
+
+
+def _bound_untransposed(W, X):
+    # only defined when W is square
+    return np.abs(X) @ np.abs(W)
+
+
+def _bound_abs_x_only(W, X):
+    return np.abs(X) @ W.T
+
+
+def _bound_abs_w_only(W, X):
+    return X @ np.abs(W).T
+
+
+def _bound_plus_one(W, X):
+    return np.abs(X) @ np.abs(W).T + 1.0
+
+
+_real_fwd_u8 = H.hxq_linear_fwd_u8
+
+
+def _fwd_u8_bound_plus_bias(codebook, indices, rows, cols, deltas, x, x_dtype, bias, m_rows=None,
+                            want_bound=True):
+    Y, B = _real_fwd_u8(codebook, indices, rows, cols, deltas, x, x_dtype, bias, m_rows, want_bound)
+    if B is not None and bias is not None:
+        B = B + np.abs(np.asarray(bias, np.float32).astype(np.float64))[None, :]
+    return Y, B
+
+
+def _fwd_u8_bound_abs_before_sidecar(codebook, indices, rows, cols, deltas, x, x_dtype, bias, m_rows=None,
+                                     want_bound=True):
+    # |C[idx]| + |deltas| instead of |C[idx] + deltas|
+    Y, _ = _real_fwd_u8(codebook, indices, rows, cols, deltas, x, x_dtype, bias, m_rows, False)
+    W = np.abs(H.dequant_u8(codebook, H.unpack_u8(indices)))
+    W = H.apply_sidecar(W, rows, cols, np.abs(np.asarray(deltas, np.float32)))
+    X = H.activations_f64(x, x_dtype)
+    if m_rows is not None:
+        X = X[np.asarray(m_rows, np.int64)]
+    return Y, np.abs(X) @ W.T
+
+
+def _bound_bwd_scaled(W, DY):
+    return 1000.0 * (np.abs(DY) @ np.abs(W))
+
+
+def _bound_bwd_transposed(W, DY):
+    # the forward's orientation: only defined when W is square
+    return np.abs(DY) @ np.abs(W).T
+
+
+def _bound_bwd_abs_dy_only(W, DY):
+    return np.abs(DY) @ W
+
+
+_real_sidecar_add = H.hxq_sidecar_add
+
+
+def _sidecar_add_bound_summed_first(rows, cols, deltas, x, x_dtype, N):
+    # |S| |x| with the repeated coordinates summed before the absolute value
+    Z, _ = _real_sidecar_add(rows, cols, deltas, x, x_dtype, N)
+    X = H.activations_f64(x, x_dtype)
+    S = np.zeros((N, X.shape[1]))
+    np.add.at(S, (np.asarray(rows, np.int64), np.asarray(cols, np.int64)),
+              np.asarray(deltas, np.float32).astype(np.float64))
+    return Z, np.abs(X) @ np.abs(S).T
+
+
+def _sidecar_add_bound_scaled(rows, cols, deltas, x, x_dtype, N):
+    Z, B = _real_sidecar_add(rows, cols, deltas, x, x_dtype, N)
+    return Z, 2.0 * B
+
+
 MUTATIONS = {
     "transposed_weight": ("linear_forward", _transposed_forward),
     "dropped_bias": ("linear_forward", _no_bias_forward),
@@ -115,6 +201,18 @@ MUTATIONS = {
     "bwd_forward_orientation": ("linear_backward_x", _bwd_forward_orientation),
     "bwd_columns_shifted": ("linear_backward_x", _bwd_columns_shifted),
     "bwd_sign_lost": ("linear_backward_x", _bwd_sign_lost),
+    "bound_scaled": ("error_bound", _bound_scaled),
+    "bound_untransposed": ("error_bound", _bound_untransposed),
+    "bound_abs_x_only": ("error_bound", _bound_abs_x_only),
+    "bound_abs_w_only": ("error_bound", _bound_abs_w_only),
+    "bound_plus_one": ("error_bound", _bound_plus_one),
+    "bound_plus_bias": ("hxq_linear_fwd_u8", _fwd_u8_bound_plus_bias),
+    "bound_abs_before_sidecar": ("hxq_linear_fwd_u8", _fwd_u8_bound_abs_before_sidecar),
+    "bound_bwd_scaled": ("error_bound_bwd", _bound_bwd_scaled),
+    "bound_bwd_transposed": ("error_bound_bwd", _bound_bwd_transposed),
+    "bound_bwd_abs_dy_only": ("error_bound_bwd", _bound_bwd_abs_dy_only),
+    "sidecar_bound_summed_first": ("hxq_sidecar_add", _sidecar_add_bound_summed_first),
+    "sidecar_bound_scaled": ("hxq_sidecar_add", _sidecar_add_bound_scaled),
 }
 
 
