@@ -39,8 +39,13 @@
  *     beyond, which are exact fp32 products summed in fp32); bf16 activations
  *     are upcast exactly and take the same fp32 path, except with M > 16
  *     (and K % 64 == 0 for pk12), which runs on bf16 matrix cores with fp32
- *     accumulation, the codebook value (plus any sidecar delta at that
- *     position, added in fp32) rounded once to bf16.
+ *     accumulation.  There the weight operand at (n, k) is the codebook value
+ *     plus every sidecar delta at (n, k), summed in fp32 in stored order and
+ *     rounded once to bf16 (nearest, ties to even): the sidecar correction is
+ *     folded into the operand, so an outlier's corrected weight carries one
+ *     bf16 rounding like every other weight (relative 2^-9), instead of
+ *     entering as an exact fp32 delta * x term.  The tolerance of that path,
+ *     8e-3 of |X| |W|^T, covers it.
  *   - Errors are returned as a negative hxq_status before anything is
  *     launched; HXQ_ERR_HIP reports a failed launch.
  */
@@ -91,7 +96,9 @@ int hxq_linear_fwd_u8(const float* codebook, const uint8_t* indices,
  *             (HXQ whitepaper, "Method", 12-bit index packing; the byte order is this
  *             library's choice).
  *   K must be even.  All other arguments as for hxq_linear_fwd_u8.  bf16 x is
- *   accepted at every M and always takes the fp32 path. */
+ *   accepted at every M: up to 16 tokens, or when K % 64 != 0, it takes the
+ *   fp32 path; past 16 tokens with K % 64 == 0 it runs on the bf16 matrix
+ *   cores like the u8 format (weights rounded to bf16 as described above). */
 int hxq_linear_fwd_pk12(const float* codebook2, const uint8_t* packed,
                         const int32_t* sc_rows, const int32_t* sc_cols,
                         const float* sc_deltas, int64_t nnz,
@@ -283,6 +290,11 @@ const char* hxq_status_str(int status);
 
 /* Library version: major * 10000 + minor * 100 + patch. */
 int hxq_version(void);
+
+/* Digest of the sources this library was built from (static text, 32 hex
+ * digits, or "unknown" for a build that did not record it), so a caller can
+ * tell a stale build from a current one. */
+const char* hxq_source_digest(void);
 
 #ifdef __cplusplus
 }

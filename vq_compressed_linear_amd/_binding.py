@@ -13,9 +13,12 @@ import os
 import re
 from typing import Optional
 
+from ._digest import source_digest
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhxq.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "hxq.h")
+CSRC_DIR = os.path.join(HERE, "csrc")
 
 HXQ_OK = 0
 HXQ_ERR_NULL = -1
@@ -85,6 +88,7 @@ SIGNATURES = {
     "hxq_select_variant": (_INT, [_INT, _INT, _I64, _I64, _I64]),
     "hxq_status_str": (ctypes.c_char_p, [_INT]),
     "hxq_version": (_INT, []),
+    "hxq_source_digest": (ctypes.c_char_p, []),
 }
 
 
@@ -97,7 +101,9 @@ def header_symbols(path: str = HEADER):
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded library; raises if it has not been built."""
+    """The loaded library; raises if it has not been built, or if it was built
+    from sources other than the ones in the tree (rebuild it then: a process
+    that has used the GPU should not compile and reload it itself)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
@@ -108,6 +114,12 @@ def lib() -> ctypes.CDLL:
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
+        built = handle.hxq_source_digest().decode()
+        if os.path.isdir(CSRC_DIR):
+            want = source_digest()
+            if built != want:
+                raise RuntimeError("libhxq.so was built from other sources (digest %s, sources %s); "
+                                   "rebuild it with python -m vq_compressed_linear_amd.build" % (built, want))
         _lib = handle
     return _lib
 
@@ -131,10 +143,10 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
+def _stream(stream, dev=None) -> Optional[int]:
     torch = _torch()
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -145,6 +157,22 @@ def _x_dtype(x) -> int:
     if x.dtype == torch.bfloat16:
         return HXQ_BF16
     raise TypeError("x must be float32 or bfloat16, got %s" % x.dtype)
+
+
+def _check_device(*tensors):
+    """Every tensor given (None skipped) must live on one GPU: the kernels read
+    raw device pointers, and a host tensor's pointer would fault them."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor must be on a GPU; got one on %s" % t.device)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors on different devices: %s and %s" % (dev, t.device))
+    return dev
 
 
 def _check_sidecar(sc_rows, sc_cols, sc_deltas):
@@ -187,9 +215,10 @@ def hxq_linear_fwd_u8(codebook, indices, sc_rows, sc_cols, sc_deltas, x, bias, y
     if Kx != K:
         raise ValueError("x has K=%d, indices K=%d" % (Kx, K))
     nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
+    dev = _check_device(codebook, indices, sc_rows, sc_cols, sc_deltas, x, bias, y)
     st = lib().hxq_linear_fwd_u8_ex(
         _ptr(codebook), _ptr(indices), _ptr(sc_rows), _ptr(sc_cols), _ptr(sc_deltas), nnz,
-        _ptr(x), _x_dtype(x), _ptr(bias), _ptr(y), M, N, K, _stream(stream), variant)
+        _ptr(x), _x_dtype(x), _ptr(bias), _ptr(y), M, N, K, _stream(stream, dev), variant)
     if st != HXQ_OK:
         raise HxqError(st, "hxq_linear_fwd_u8")
 
@@ -207,9 +236,10 @@ def hxq_linear_fwd_pk12(codebook2, packed, sc_rows, sc_cols, sc_deltas, x, bias,
     if packed.shape[1] != 3 * ((K + 3) // 4):
         raise ValueError("packed rows must hold 3*ceil(K/4) = %d bytes" % (3 * ((K + 3) // 4)))
     nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
+    dev = _check_device(codebook2, packed, sc_rows, sc_cols, sc_deltas, x, bias, y)
     st = lib().hxq_linear_fwd_pk12_ex(
         _ptr(codebook2), _ptr(packed), _ptr(sc_rows), _ptr(sc_cols), _ptr(sc_deltas), nnz,
-        _ptr(x), _x_dtype(x), _ptr(bias), _ptr(y), M, N, K, _stream(stream), variant)
+        _ptr(x), _x_dtype(x), _ptr(bias), _ptr(y), M, N, K, _stream(stream, dev), variant)
     if st != HXQ_OK:
         raise HxqError(st, "hxq_linear_fwd_pk12")
 
@@ -219,8 +249,9 @@ def hxq_sidecar_add(sc_rows, sc_cols, sc_deltas, x, y, stream=None) -> None:
     nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
     N = y.shape[1]
     M, K = _check_common(x, None, y, N)
+    dev = _check_device(sc_rows, sc_cols, sc_deltas, x, y)
     st = lib().hxq_sidecar_add(_ptr(sc_rows), _ptr(sc_cols), _ptr(sc_deltas), nnz, _ptr(x),
-                               _x_dtype(x), _ptr(y), M, N, K, _stream(stream))
+                               _x_dtype(x), _ptr(y), M, N, K, _stream(stream, dev))
     if st != HXQ_OK:
         raise HxqError(st, "hxq_sidecar_add")
 
@@ -241,8 +272,9 @@ def hxq_dequant_bf16(fmt: int, codebook, indices, sc_rows, sc_cols, sc_deltas, w
     if codebook.dtype != torch.float32 or codebook.numel() != (256 if fmt == HXQ_FMT_U8 else 8192):
         raise ValueError("wrong codebook size or dtype")
     nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
+    dev = _check_device(codebook, indices, sc_rows, sc_cols, sc_deltas, w)
     st = lib().hxq_dequant_bf16(fmt, _ptr(codebook), _ptr(indices), _ptr(sc_rows), _ptr(sc_cols),
-                                _ptr(sc_deltas), nnz, _ptr(w), N, K, _stream(stream))
+                                _ptr(sc_deltas), nnz, _ptr(w), N, K, _stream(stream, dev))
     if st != HXQ_OK:
         raise HxqError(st, "hxq_dequant_bf16")
 
@@ -270,6 +302,8 @@ def hxq_linear_bwd_x(fmt: int, codebook, indices, sc_rows, sc_cols, sc_deltas, d
     if dx.dtype != torch.float32 or tuple(dx.shape) != (M, K) or not dx.is_contiguous():
         raise ValueError("dx must be a contiguous float32 [M, K] tensor")
     nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
+    dev = _check_device(codebook, indices, sc_rows, sc_cols, sc_deltas, dy, dx,
+                        workspace if workspace is not None and workspace.numel() > 0 else None)
     if workspace is None:
         need = lib().hxq_linear_bwd_x_workspace(fmt, _x_dtype(dy), M, N, K, nnz)
         if need < 0:
@@ -281,12 +315,12 @@ def hxq_linear_bwd_x(fmt: int, codebook, indices, sc_rows, sc_cols, sc_deltas, d
         wptr, wbytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     st = lib().hxq_linear_bwd_x_ex(fmt, _ptr(codebook), _ptr(indices), _ptr(sc_rows), _ptr(sc_cols),
                                    _ptr(sc_deltas), nnz, _ptr(dy), _x_dtype(dy), _ptr(dx), M, N, K,
-                                   wptr, wbytes, _stream(stream), variant)
+                                   wptr, wbytes, _stream(stream, dev), variant)
     if st != HXQ_OK:
         raise HxqError(st, "hxq_linear_bwd_x")
 
 
-def grouped_layers(fmt: int, layers, M: int, K: int):
+def grouped_layers(fmt: int, layers, M: int, K: int, x=None):
     """HxqLayer array for hxq_linear_fwd_grouped from dicts holding the
     tensors codebook, indices, sc_rows, sc_cols, sc_deltas, bias (or None) and
     y.  Checks dtypes and shapes like the single-layer functions."""
@@ -309,6 +343,7 @@ def grouped_layers(fmt: int, layers, M: int, K: int):
         if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N):
             raise ValueError("layer %d: bias must be float32 [N]" % i)
         nnz = _check_sidecar(l.get("sc_rows"), l.get("sc_cols"), l.get("sc_deltas"))
+        _check_device(x, cb, idx, l.get("sc_rows"), l.get("sc_cols"), l.get("sc_deltas"), bias, y)
         arr[i] = HxqLayer(_ptr(cb), _ptr(idx), _ptr(l.get("sc_rows")), _ptr(l.get("sc_cols")),
                           _ptr(l.get("sc_deltas")), nnz, _ptr(bias), _ptr(y), N)
     return arr
@@ -319,8 +354,9 @@ def hxq_linear_fwd_grouped(fmt: int, layers, x, stream=None) -> None:
     if x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous [M, K] tensor")
     M, K = x.shape
-    arr = grouped_layers(fmt, layers, M, K)
-    st = lib().hxq_linear_fwd_grouped(fmt, arr, len(layers), _ptr(x), _x_dtype(x), M, K, _stream(stream))
+    arr = grouped_layers(fmt, layers, M, K, x)
+    dev = _check_device(x)
+    st = lib().hxq_linear_fwd_grouped(fmt, arr, len(layers), _ptr(x), _x_dtype(x), M, K, _stream(stream, dev))
     if st != HXQ_OK:
         raise HxqError(st, "hxq_linear_fwd_grouped")
 

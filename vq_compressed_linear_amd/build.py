@@ -12,6 +12,12 @@ import shutil
 import subprocess
 import sys
 
+try:
+    from ._digest import source_digest
+except ImportError:  # run as a script
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from vq_compressed_linear_amd._digest import source_digest
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libhxq.so")
@@ -34,9 +40,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, digest: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), "--offload-arch=" + ARCH, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src == "hxq_api.cpp":
+        cmd.insert(1, '-DHXQ_SOURCE_DIGEST="%s"' % digest)
     if src.endswith(".cpp"):
         cmd.insert(1, "-x")
         cmd.insert(2, "hip")
@@ -48,8 +56,9 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
+    digest = source_digest()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, digest), SOURCES))
     tmp = OUT + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

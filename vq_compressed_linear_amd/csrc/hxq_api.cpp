@@ -429,4 +429,10 @@ const char* hxq_status_str(int status) {
 
 int hxq_version(void) { return 100; }
 
+#ifndef HXQ_SOURCE_DIGEST
+#define HXQ_SOURCE_DIGEST "unknown"
+#endif
+
+const char* hxq_source_digest(void) { return HXQ_SOURCE_DIGEST; }
+
 }  // extern "C"

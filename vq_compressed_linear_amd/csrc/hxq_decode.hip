@@ -57,7 +57,7 @@ constexpr int LDS_LIMIT = 160 * 1024;
 constexpr int kLgkmOnly = 0xc07f;
 
 struct Lay {
-  int xs, part, srow, scol, sdl, rs, re, misc, total;
+  int xs, part, scol, sdl, rs, re, misc, total;
 };
 
 __host__ __device__ inline int a16(int v) { return (v + 15) & ~15; }
@@ -68,8 +68,7 @@ __host__ __device__ inline Lay layout(int MT, int xb, int kp, int rows_cap, int 
   Lay L;
   L.xs = 0;
   L.part = a16(MT * kp * xb);
-  L.srow = L.part + a16(rows_cap * S * MT * 4);
-  L.scol = L.srow + SIDE_CAP * 4;
+  L.scol = L.part + a16(rows_cap * S * MT * 4);
   L.sdl = L.scol + SIDE_CAP * 4;
   L.rs = L.sdl + SIDE_CAP * 4;
   L.re = L.rs + a16(rows_cap * 4);
@@ -268,7 +267,6 @@ __global__ __launch_bounds__(dec::THREADS, 1) void decode_gemv(DecodeArgs a) {
   const Lay Lo = layout(MT, XB, kp, rows_cap, S);
   unsigned char* xs = smem + Lo.xs;
   float* part = reinterpret_cast<float*>(smem + Lo.part);
-  int* srow = reinterpret_cast<int*>(smem + Lo.srow);
   int* scol = reinterpret_cast<int*>(smem + Lo.scol);
   float* sdl = reinterpret_cast<float*>(smem + Lo.sdl);
   int* rs = reinterpret_cast<int*>(smem + Lo.rs);
@@ -433,19 +431,30 @@ __global__ __launch_bounds__(dec::THREADS, 1) void decode_gemv(DecodeArgs a) {
       for (int q = 0; q < NB; ++q) {
         const int i = q * kWave + lane;
         if (q * kWave < cnt && i < cnt) {
-          srow[i] = tr[q];
           scol[i] = tc[q];
           sdl[i] = td[q];
         }
       }
-      // run boundaries, from the neighbours in LDS (this wave wrote them)
+      // run boundaries: the neighbours' rows come from registers by lane
+      // shuffles (reading the other lanes' LDS stores would need a wave-level
+      // fence to be ordered after them)
 #pragma unroll
       for (int q = 0; q < NB; ++q) {
-        const int i = q * kWave + lane;
-        if (q * kWave < cnt && i < cnt) {
-          const int r = srow[i];
-          if (i == 0 || srow[i - 1] != r) rs[r - r0] = i;
-          if (i + 1 == cnt || srow[i + 1] != r) re[r - r0] = i + 1;
+        if (q * kWave < cnt) {  // uniform
+          const int r = tr[q];
+          const int up = __shfl_up(r, 1, kWave);    // lane - 1 (lane 0: its own)
+          const int dn = __shfl_down(r, 1, kWave);  // lane + 1 (lane 63: its own)
+          // the last row of the previous 64 and the first of the next
+          const int prevq = q > 0 ? __shfl(tr[q > 0 ? q - 1 : 0], kWave - 1, kWave) : 0;
+          const bool more = q + 1 < NB && (q + 1) * kWave < cnt;
+          const int nextq = more ? __shfl(tr[q + 1 < NB ? q + 1 : q], 0, kWave) : 0;
+          const int i = q * kWave + lane;
+          if (i < cnt) {
+            const int prev = lane == 0 ? prevq : up;
+            const int next = lane == kWave - 1 ? nextq : dn;
+            if (i == 0 || prev != r) rs[r - r0] = i;
+            if (i + 1 == cnt || next != r) re[r - r0] = i + 1;
+          }
         }
       }
     }

@@ -7,6 +7,8 @@
 // never written anywhere: each index is turned into its codebook value in a
 // register right before the multiply.
 
+#include <atomic>
+
 #include "hxq_device.h"
 #include "hxq_launch.h"
 
@@ -457,11 +459,22 @@ __global__ __launch_bounds__(256) void sidecar_add_kernel(LayerArgs a) {
 
 // ---------------------------------------------------------------- launchers
 
+// Compute units of the current device, queried once per device and kept
+// (zero in the table means not yet queried).
 int device_cu_count() {
-  int dev = 0, cus = 0;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const bool slot = dev >= 0 && dev < kMaxDevices;
+  if (slot) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return 256;
+  if (slot) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
