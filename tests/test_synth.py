@@ -69,3 +69,26 @@ def test_small_pk12_layer():
     lay = gen.synth_layer(9, 0, 24, 40, "pk12", 2000)
     assert lay.indices.shape == (24, 30)
     assert lay.nnz == 24 * 40 // 2000
+
+
+def test_generator_outputs_match_stored_sha256(monkeypatch):
+    """The seeded generator reproduces, byte for byte, the outputs whose
+    SHA-256 tests/golden/make_synth_sha256.py stored (u8 and pk12 layers,
+    activations, a random parity layer)."""
+    import importlib.util
+    import os
+
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    monkeypatch.setenv("HXQ_SYNTH_CACHE", "")
+    monkeypatch.setattr(gen, "_MEM", {})
+    spec = importlib.util.spec_from_file_location("make_synth_sha256", os.path.join(here, "make_synth_sha256.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    want = {}
+    with open(os.path.join(here, "synth_sha256.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                label, field, h = line.split()
+                want[(label, field)] = h
+    got = {(label, field): h for label, field, h in mod.digests()}
+    assert got == want
