@@ -38,7 +38,7 @@
  *     accumulation (vector FMAs up to 4 tokens, fp32 matrix-core products
  *     beyond, which are exact fp32 products summed in fp32); bf16 activations
  *     are upcast exactly and take the same fp32 path, except with M > 16
- *     (and K % 64 == 0 for pk12), which runs on bf16 matrix cores with fp32
+ *     (and K % 32 == 0 for pk12), which runs on bf16 matrix cores with fp32
  *     accumulation.  There the weight operand at (n, k) is the codebook value
  *     plus every sidecar delta at (n, k), summed in fp32 in stored order and
  *     rounded once to bf16 (nearest, ties to even): the sidecar correction is
@@ -96,8 +96,8 @@ int hxq_linear_fwd_u8(const float* codebook, const uint8_t* indices,
  *             (HXQ whitepaper, "Method", 12-bit index packing; the byte order is this
  *             library's choice).
  *   K must be even.  All other arguments as for hxq_linear_fwd_u8.  bf16 x is
- *   accepted at every M: up to 16 tokens, or when K % 64 != 0, it takes the
- *   fp32 path; past 16 tokens with K % 64 == 0 it runs on the bf16 matrix
+ *   accepted at every M: up to 16 tokens, or when K % 32 != 0, it takes the
+ *   fp32 path; past 16 tokens with K % 32 == 0 it runs on the bf16 matrix
  *   cores like the u8 format (weights rounded to bf16 as described above). */
 int hxq_linear_fwd_pk12(const float* codebook2, const uint8_t* packed,
                         const int32_t* sc_rows, const int32_t* sc_cols,
@@ -124,7 +124,7 @@ int hxq_sidecar_add(const int32_t* sc_rows, const int32_t* sc_cols,
  * hxq_linear_fwd_u8 / hxq_linear_fwd_pk12 would compute for it, within the
  * same tolerance (bitwise the same where the single-layer call would run the
  * same kernel); the layers normally run in a single launch (up to 64 tokens,
- * and with bf16 x at any M where K % 64 == 0), otherwise one after another on
+ * and with bf16 x at any M where K % 32 == 0), otherwise one after another on
  * `stream`.
  *   fmt     HXQ_FMT_U8 or HXQ_FMT_PK12.
  *   layers  host array of `count` descriptors, 1 <= count <= HXQ_MAX_GROUP,
@@ -156,13 +156,13 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count,
                            hipStream_t stream);
 
 /* Measurement helper, not part of the forward pass: reads `bytes` bytes of
- * device memory at `src` once, with the decode kernels' grid shape (one
- * 512-thread workgroup per CU, 16-byte loads, the whole grid sweeping the
- * buffer in order, four loads in flight per thread), and writes a 32-bit
- * digest of what it read per workgroup into `sink`
- * (device memory, `sink_words` entries; the launch uses at most that many
- * workgroups).  Its duration is the attainable read bandwidth that the decode
- * GEMV's HBM fraction is compared against.
+ * device memory at `src` once with `sink_words` 512-thread workgroups (fewer
+ * when the buffer needs fewer, at most 65535; 16-byte loads, the whole grid
+ * sweeping the buffer in order, four loads in flight per thread), and writes a
+ * 32-bit digest of what it read per workgroup into `sink` (device memory,
+ * `sink_words` entries).  Timed over a sweep of grid sizes it gives the
+ * attainable read bandwidth that the decode kernels' HBM fraction is compared
+ * against.
  * Errors: HXQ_ERR_SHAPE if bytes < 0 or not a multiple of 16 or sink_words < 1,
  * HXQ_ERR_NULL for a NULL pointer with bytes > 0, HXQ_ERR_ALIGN if src is not
  * 16-byte aligned or sink not 4-byte aligned. */
@@ -263,8 +263,11 @@ enum hxq_variant {
   HXQ_VARIANT_AUTO = 0,
   HXQ_VARIANT_GEMV_VALU = 1,  /* fp32 GEMV family: vector FMAs up to 4 tokens, fp32 matrix cores beyond */
   HXQ_VARIANT_GEMV_MFMA = 2,  /* fp32 matrix-core GEMV (16x16x4 fp32 MFMA) at any M; needs K % 64 == 0 */
-  HXQ_VARIANT_GEMM_BF16 = 3,  /* bf16 matrix-core GEMM (bf16 x only; pk12 needs K % 64 == 0) */
-  HXQ_VARIANT_GENERIC = 4     /* any shape or alignment, one wave per output row */
+  HXQ_VARIANT_GEMM_BF16 = 3,  /* bf16 matrix-core GEMM (bf16 x only; K % 32 == 0) */
+  HXQ_VARIANT_GENERIC = 4,    /* any shape or alignment, one wave per output row */
+  HXQ_VARIANT_GEMM_BF16_T256 = 5  /* the bf16 matrix-core GEMM with 256 x 256 tiles (bf16 x only,
+                                     K % 32 == 0); AUTO and HXQ_VARIANT_GEMM_BF16 take it for
+                                     launches of at least two rounds of such tiles over the CUs */
 };
 
 int hxq_linear_fwd_u8_ex(const float* codebook, const uint8_t* indices,

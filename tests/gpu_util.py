@@ -88,3 +88,14 @@ def sample_rows(M, k=64, seed=0):
     rng = np.random.Generator(np.random.PCG64(seed))
     mid = rng.choice(np.arange(1, M - 1), size=k - 2, replace=False)
     return np.sort(np.concatenate(([0, M - 1], mid)))
+
+
+def tile_rows(M, seed=0):
+    """Token rows to compare for a large M: 64 random rows, one random row in
+    every 128-token block and the last row of every 256-token block, so every
+    tile of the prefill kernels (128 or 256 tokens tall) is looked at."""
+    rng = np.random.Generator(np.random.PCG64(seed + 17))
+    per128 = np.arange(0, M, 128) + rng.integers(0, 128, size=(M + 127) // 128)
+    last256 = np.arange(255, M + 255, 256)
+    rows = np.concatenate([sample_rows(M, 64, seed), per128, last256])
+    return np.unique(rows[rows < M])

@@ -101,12 +101,13 @@ def test_sidecar_add_rejects(L):
 
 def test_variant_selection(L):
     sel = L.hxq_select_variant
-    # bf16 x with M > 16 goes to the matrix-core GEMM (pk12: K % 64 == 0), everything else to a GEMV
+    # bf16 x with M > 16 goes to the matrix-core GEMM (K % 32 == 0), everything else to a GEMV
     assert sel(0, B.HXQ_BF16, 2048, 11008, 2048) == B.HXQ_VARIANT_GEMM_BF16
     assert sel(0, B.HXQ_BF16, 16, 11008, 2048) != B.HXQ_VARIANT_GEMM_BF16
     assert sel(0, B.HXQ_F32, 64, 8512, 2048) != B.HXQ_VARIANT_GEMM_BF16
     assert sel(1, B.HXQ_BF16, 2048, 11008, 2048) == B.HXQ_VARIANT_GEMM_BF16
-    assert sel(1, B.HXQ_BF16, 2048, 11008, 96) != B.HXQ_VARIANT_GEMM_BF16
+    assert sel(1, B.HXQ_BF16, 2048, 11008, 96) == B.HXQ_VARIANT_GEMM_BF16
+    assert sel(1, B.HXQ_BF16, 2048, 11008, 80) != B.HXQ_VARIANT_GEMM_BF16
     assert sel(0, B.HXQ_BF16, 2048, 11008, 96) == B.HXQ_VARIANT_GEMM_BF16
     assert sel(1, B.HXQ_F32, 2048, 11008, 2048) != B.HXQ_VARIANT_GEMM_BF16
     # shapes the fast kernels do not take go to the generic kernel
@@ -265,3 +266,4 @@ def test_bwd_x_workspace_query(L):
         assert n >= 0 and n % (M * K * 4) == 0
     # the matrix-core path also keeps the sidecar bins there
     assert q(B.HXQ_FMT_U8, BF, 256, 2048, 2048, 4096) > q(B.HXQ_FMT_U8, BF, 256, 2048, 2048, 0)
+

@@ -88,44 +88,51 @@ def test_generic(fmt, N, K, M):
 
 # ---------------------------------------------------------------- bf16 GEMM
 
+GEMMS = [hx.HXQ_VARIANT_GEMM_BF16, hx.HXQ_VARIANT_GEMM_BF16_T256]  # the automatic choice, and the 256 x 256 tile kernel forced
+
 @pytest.mark.parametrize("N,K", [(1000, 2048), (300, 96), (129, 32), (256, 11008 // 32 * 32)])
 @pytest.mark.parametrize("M", [17, 128, 200, 513])
-def test_u8_gemm_bf16(N, K, M):
-    G.say("u8 gemm N=%d K=%d M=%d" % (N, K, M))
+@pytest.mark.parametrize("variant", GEMMS)
+def test_u8_gemm_bf16(N, K, M, variant):
+    G.say("u8 gemm N=%d K=%d M=%d variant=%d" % (N, K, M, variant))
     lay = gen.random_layer(N + K + 5, N, K, "u8", nnz=max(1, N * K // 1000), duplicates=True)
-    _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=M, what="gemm")
+    _case(lay, M, "bf16", variant, G.TOL_BF16, seed=M, what="gemm")
 
 
 @pytest.mark.parametrize("N,K", [(1000, 2048), (300, 64), (2048, 4096 + 64), (11008, 2048)])
 @pytest.mark.parametrize("M", [17, 130, 300])
-def test_pk12_gemm_bf16(N, K, M):
+@pytest.mark.parametrize("variant", GEMMS)
+def test_pk12_gemm_bf16(N, K, M, variant):
     # 2D pairs on the matrix cores: 12-byte index groups, the bf16 pair table
-    G.say("pk12 gemm N=%d K=%d M=%d" % (N, K, M))
+    G.say("pk12 gemm N=%d K=%d M=%d variant=%d" % (N, K, M, variant))
     lay = gen.random_layer(N + K + 9, N, K, "pk12", nnz=max(1, N * K // 2000), duplicates=True)
-    _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=M, what="pk12 gemm")
+    _case(lay, M, "bf16", variant, G.TOL_BF16, seed=M, what="pk12 gemm")
 
 
 @pytest.mark.parametrize("N,K,nnz,M", [(64, 1024, 8192, 150), (96, 33024, 3000, 130)])
-def test_pk12_gemm_sidecar_paths(N, K, nnz, M):
-    G.say("pk12 gemm sidecar paths N=%d K=%d nnz=%d" % (N, K, nnz))
+@pytest.mark.parametrize("variant", GEMMS)
+def test_pk12_gemm_sidecar_paths(N, K, nnz, M, variant):
+    G.say("pk12 gemm sidecar paths N=%d K=%d nnz=%d variant=%d" % (N, K, nnz, variant))
     lay = gen.random_layer(N + K + 1, N, K, "pk12", nnz=nnz, duplicates=True)
-    _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=M, what="pk12 gemm sidecar paths")
+    _case(lay, M, "bf16", variant, G.TOL_BF16, seed=M, what="pk12 gemm sidecar paths")
 
 
 @pytest.mark.parametrize("M", [1, 5, 16])
-def test_gemm_small_m_forced(M):
+@pytest.mark.parametrize("variant", GEMMS)
+def test_gemm_small_m_forced(M, variant):
     lay = gen.random_layer(21, 260, 64, "u8", nnz=40)
-    _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=M, what="gemm small m")
+    _case(lay, M, "bf16", variant, G.TOL_BF16, seed=M, what="gemm small m")
 
 
 @pytest.mark.parametrize("N,K,nnz,M", [
     (64, 1024, 8192, 150),    # more triplets in one tile than the patch area holds
     (96, 33024, 3000, 130),   # more stages than the patch bins cover
     (300, 4096, 12000, 200)])  # dense sidecar, patch path in some tiles and walk path in others
-def test_gemm_sidecar_paths(N, K, nnz, M):
-    G.say("gemm sidecar paths N=%d K=%d nnz=%d" % (N, K, nnz))
+@pytest.mark.parametrize("variant", GEMMS)
+def test_gemm_sidecar_paths(N, K, nnz, M, variant):
+    G.say("gemm sidecar paths N=%d K=%d nnz=%d variant=%d" % (N, K, nnz, variant))
     lay = gen.random_layer(N + K, N, K, "u8", nnz=nnz, duplicates=True)
-    _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=M, what="gemm sidecar paths")
+    _case(lay, M, "bf16", variant, G.TOL_BF16, seed=M, what="gemm sidecar paths")
 
 
 def test_gemm_rejects_fp32_x():
@@ -201,10 +208,11 @@ def _heavy_sidecar_layer(fmt, N, K):
 @pytest.mark.parametrize("fmt,variant,M,xdt", [
     ("u8", hx.HXQ_VARIANT_GEMV_VALU, 1, "f32"), ("u8", hx.HXQ_VARIANT_GEMV_VALU, 16, "f32"),
     ("pk12", hx.HXQ_VARIANT_GEMV_VALU, 3, "f32"), ("u8", hx.HXQ_VARIANT_GENERIC, 2, "f32"),
-    ("pk12", hx.HXQ_VARIANT_GENERIC, 2, "f32"), ("u8", hx.HXQ_VARIANT_GEMM_BF16, 150, "bf16")])
+    ("pk12", hx.HXQ_VARIANT_GENERIC, 2, "f32"), ("u8", hx.HXQ_VARIANT_GEMM_BF16, 150, "bf16"),
+    ("u8", hx.HXQ_VARIANT_GEMM_BF16_T256, 150, "bf16"), ("pk12", hx.HXQ_VARIANT_GEMM_BF16_T256, 150, "bf16")])
 def test_dense_sidecar_rows(fmt, variant, M, xdt):
     lay = _heavy_sidecar_layer(fmt, 200, 1024)
-    _case(lay, M, xdt, variant, G.TOL_BF16 if variant == hx.HXQ_VARIANT_GEMM_BF16 else G.TOL_FP32,
+    _case(lay, M, xdt, variant, G.TOL_BF16 if variant in GEMMS else G.TOL_FP32,
           what="heavy sidecar")
 
 
@@ -216,7 +224,8 @@ def test_gemm_wide_tiles_ragged(fmt):
     N, K, M = 4100, 128, 2000
     G.say("gemm wide tiles ragged %s" % fmt)
     lay = gen.random_layer(57, N, K, fmt, nnz=N * K // 1000, duplicates=True)
-    _case(lay, M, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=5, what="wide tiles ragged")
+    for variant in GEMMS:
+        _case(lay, M, "bf16", variant, G.TOL_BF16, seed=5, what="wide tiles ragged")
 
 
 @pytest.mark.parametrize("fmt", ["u8", "pk12"])
@@ -236,12 +245,14 @@ def test_gemm_full_sidecar_block(fmt):
     lay.cols = cols[order].astype(np.int32)
     lay.deltas = (0.05 * rng.standard_normal(rows.size)).astype(np.float32)
     G.say("gemm full sidecar block %s nnz=%d" % (fmt, rows.size))
-    _case(lay, 150, "bf16", hx.HXQ_VARIANT_GEMM_BF16, G.TOL_BF16, seed=3, what="full sidecar block")
+    for variant in GEMMS:
+        _case(lay, 150, "bf16", variant, G.TOL_BF16, seed=3, what="full sidecar block")
 
 
 @pytest.mark.parametrize("fmt,variant,M,xdt", [
     ("u8", hx.HXQ_VARIANT_GEMV_VALU, 8, "f32"), ("pk12", hx.HXQ_VARIANT_GEMV_VALU, 16, "f32"),
-    ("u8", hx.HXQ_VARIANT_GEMM_BF16, 300, "bf16"), ("u8", hx.HXQ_VARIANT_GENERIC, 3, "f32")])
+    ("u8", hx.HXQ_VARIANT_GEMM_BF16, 300, "bf16"), ("u8", hx.HXQ_VARIANT_GENERIC, 3, "f32"),
+    ("pk12", hx.HXQ_VARIANT_GEMM_BF16_T256, 300, "bf16")])
 def test_canary_and_determinism(fmt, variant, M, xdt):
     """No writes outside y, and two runs give the same bits."""
     t = G.torch()
@@ -262,7 +273,8 @@ def test_canary_and_determinism(fmt, variant, M, xdt):
 
 @pytest.mark.parametrize("variant,xdt,M", [(hx.HXQ_VARIANT_GEMV_VALU, "f32", 1),
                                            (hx.HXQ_VARIANT_GEMV_VALU, "f32", 9),
-                                           (hx.HXQ_VARIANT_GEMM_BF16, "bf16", 140)])
+                                           (hx.HXQ_VARIANT_GEMM_BF16, "bf16", 140),
+                                           (hx.HXQ_VARIANT_GEMM_BF16_T256, "bf16", 140)])
 def test_codebook_permutation_invariance(variant, xdt, M):
     """Permuting the codebook and remapping the indices leaves y unchanged, bit for bit."""
     t = G.torch()
@@ -282,6 +294,7 @@ def test_codebook_permutation_invariance(variant, xdt, M):
 @pytest.mark.parametrize("fmt,variant,xdt,M", [
     ("u8", hx.HXQ_VARIANT_GEMV_VALU, "f32", 1), ("u8", hx.HXQ_VARIANT_GEMV_VALU, "f32", 16),
     ("pk12", hx.HXQ_VARIANT_GEMV_VALU, "f32", 4), ("u8", hx.HXQ_VARIANT_GEMM_BF16, "bf16", 130),
+    ("u8", hx.HXQ_VARIANT_GEMM_BF16_T256, "bf16", 130), ("pk12", hx.HXQ_VARIANT_GEMM_BF16_T256, "bf16", 130),
     ("u8", hx.HXQ_VARIANT_GENERIC, "f32", 3)])
 def test_constant_index_bit_exact(fmt, variant, xdt, M):
     """idx == j, no sidecar, C[j] = 0.375, integer x: every partial sum is exact,
@@ -311,6 +324,8 @@ def test_constant_index_bit_exact(fmt, variant, xdt, M):
 @pytest.mark.parametrize("fmt,variant", [("u8", hx.HXQ_VARIANT_GEMV_VALU),
                                          ("pk12", hx.HXQ_VARIANT_GEMV_VALU),
                                          ("u8", hx.HXQ_VARIANT_GEMM_BF16),
+                                         ("u8", hx.HXQ_VARIANT_GEMM_BF16_T256),
+                                         ("pk12", hx.HXQ_VARIANT_GEMM_BF16_T256),
                                          ("u8", hx.HXQ_VARIANT_GENERIC)])
 def test_one_hot_dequant_bit_exact(fmt, variant):
     """x = e_k reads column k of the weight: y[k][n] = fp32(C[idx] + delta) on the
@@ -321,9 +336,10 @@ def test_one_hot_dequant_bit_exact(fmt, variant):
 @pytest.mark.parametrize("fmt", ["u8", "pk12"])
 @pytest.mark.parametrize("N,K,nnz", [(260, 128, 300), (40, 256, 6000)])
 def test_one_hot_gemm_k64(fmt, N, K, nnz):
-    """The same probe on the K % 64 == 0 matrix-core kernel: sidecar patches
+    """The same probe on the 256-token matrix-core kernel: sidecar patches
     (few triplets) and the per-row walk (more triplets than the patch area)."""
-    _one_hot_case(fmt, hx.HXQ_VARIANT_GEMM_BF16, N, K, nnz)
+    for variant in GEMMS:
+        _one_hot_case(fmt, variant, N, K, nnz)
 
 
 def _one_hot_case(fmt, variant, N, K, nnz):
@@ -332,8 +348,8 @@ def _one_hot_case(fmt, variant, N, K, nnz):
          oracle.dequant_pk12(lay.codebook, oracle.unpack_pk12(lay.indices, N, K), K)).astype(np.float32)
     Wf = W.copy()
     Wf[lay.rows, lay.cols] = W[lay.rows, lay.cols] + lay.deltas  # fp32 add, one rounding
-    xdt = "bf16" if variant == hx.HXQ_VARIANT_GEMM_BF16 else "f32"
-    if variant == hx.HXQ_VARIANT_GEMM_BF16:
+    xdt = "bf16" if variant in GEMMS else "f32"
+    if variant in GEMMS:
         Wf = oracle.bf16_round_f32(Wf)
     eye = np.eye(K, dtype=np.float32)
     x_np = gen.to_bf16_bits(eye) if xdt == "bf16" else eye

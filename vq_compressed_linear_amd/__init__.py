@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     HXQ_MAX_GROUP,
     HXQ_VARIANT_AUTO,
     HXQ_VARIANT_GEMM_BF16,
+    HXQ_VARIANT_GEMM_BF16_T256,
     HXQ_VARIANT_GEMV_MFMA,
     HXQ_VARIANT_GEMV_VALU,
     HXQ_VARIANT_GENERIC,

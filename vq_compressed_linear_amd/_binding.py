@@ -36,6 +36,7 @@ HXQ_VARIANT_GEMV_VALU = 1
 HXQ_VARIANT_GEMV_MFMA = 2
 HXQ_VARIANT_GEMM_BF16 = 3
 HXQ_VARIANT_GENERIC = 4
+HXQ_VARIANT_GEMM_BF16_T256 = 5
 
 HXQ_FMT_U8 = 0
 HXQ_FMT_PK12 = 1
@@ -47,6 +48,7 @@ VARIANT_NAMES = {
     HXQ_VARIANT_GEMV_MFMA: "gemv_mfma",
     HXQ_VARIANT_GEMM_BF16: "gemm_bf16",
     HXQ_VARIANT_GENERIC: "generic",
+    HXQ_VARIANT_GEMM_BF16_T256: "gemm_bf16_t256",
 }
 
 

@@ -45,6 +45,15 @@ int select(bool pk12, bool x_bf16, int64_t M, int64_t K, bool gemv_ok, bool gemm
 
 int status_of(hipError_t e) { return e == hipSuccess ? HXQ_OK : HXQ_ERR_HIP; }
 
+// The 256 x 256 tile GEMM (gemm5) against the 128-token one (gemm3): per
+// tile it does more work per LDS byte and per gather, but a launch with few
+// tiles leaves CUs idle (the prefill layers at 2048 tokens: q|k|v, o and down
+// have 64 to 80 such tiles, gate|up 688).  It takes a launch of at least two
+// rounds of tiles over the CUs, and the shapes only it can take.
+bool gemm5_preferred(const hxq::GemmSeg* segs, int nseg, int M) {
+  return hxq::gemm5_tiles(segs, nseg, M) >= 2 * (int64_t)hxq::device_cu_count();
+}
+
 int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32_t* sc_rows,
             const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* x, int x_dtype,
             const float* bias, float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream,
@@ -52,7 +61,7 @@ int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32
   int st = validate_forward(codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, x, x_dtype, bias,
                             y, M, N, K, pk12);
   if (st != HXQ_OK) return st;
-  if (variant < HXQ_VARIANT_AUTO || variant > HXQ_VARIANT_GENERIC) return HXQ_ERR_UNSUPPORTED;
+  if (variant < HXQ_VARIANT_AUTO || variant > HXQ_VARIANT_GEMM_BF16_T256) return HXQ_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return HXQ_OK;
   hxq::LayerArgs a;
   a.codebook = codebook;
@@ -69,7 +78,7 @@ int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32
   a.N = (int)N;
   a.K = (int)K;
   const bool gemv_ok = K > 0 && hxq::gemv_fast_path_ok(a, pk12);
-  const bool gemm_ok = K > 0 && (pk12 ? hxq::gemm2_path_ok(a, true) : hxq::gemm_path_ok(a));
+  const bool gemm_ok = K > 0 && (hxq::gemm5_path_ok(a, pk12) || (pk12 ? hxq::gemm2_path_ok(a, true) : hxq::gemm_path_ok(a)));
   int v = variant;
   if (v == HXQ_VARIANT_AUTO) v = select(pk12, a.x_bf16, M, K, gemv_ok, gemm_ok);
   (void)hipGetLastError();  // start from a clean error state
@@ -81,9 +90,21 @@ int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32
       if (!gemv_ok || !hxq::gemv_mfma_takes(a, pk12)) return HXQ_ERR_UNSUPPORTED;
       return status_of(hxq::launch_gemv_mfma_tokens(a, pk12, stream));
     case HXQ_VARIANT_GEMM_BF16:
+    case HXQ_VARIANT_GEMM_BF16_T256: {
       if (!gemm_ok) return HXQ_ERR_UNSUPPORTED;
-      if (hxq::gemm2_path_ok(a, pk12)) return status_of(hxq::launch_gemm2_bf16(a, pk12, stream));
+      const hxq::GemmSeg sg = {static_cast<const float*>(a.codebook), a.indices, a.sc_rows, a.sc_cols,
+                               a.sc_deltas, a.nnz, a.bias, a.y, a.N, 0};
+      const bool g5 = hxq::gemm5_path_ok(a, pk12);
+      const bool g3 = hxq::gemm2_path_ok(a, pk12);
+      if (v == HXQ_VARIANT_GEMM_BF16_T256) {
+        if (!g5) return HXQ_ERR_UNSUPPORTED;
+        return status_of(hxq::launch_gemm5_grouped(&sg, 1, pk12, a.x, a.M, a.K, stream));
+      }
+      if (g5 && (!g3 || gemm5_preferred(&sg, 1, a.M)))
+        return status_of(hxq::launch_gemm5_grouped(&sg, 1, pk12, a.x, a.M, a.K, stream));
+      if (g3) return status_of(hxq::launch_gemm2_bf16(a, pk12, stream));
       return status_of(hxq::launch_gemm_bf16(a, stream));  // u8 only (pk12 passed the check above)
+    }
     case HXQ_VARIANT_GENERIC:
       return status_of(hxq::launch_generic(a, pk12, stream));
     default:
@@ -317,7 +338,7 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
   if (x_dtype == HXQ_BF16 && M > 16 && K > 0) {
     hxq::GemmSeg gs[hxq::kMaxSegments];
     int ng = 0;
-    bool ok = true;
+    bool ok5 = true, ok3 = true, ok = true;
     for (int i = 0; i < count && ok; ++i) {
       const hxq_layer& l = layers[i];
       if (l.N == 0) continue;
@@ -330,13 +351,17 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
       a.M = (int)M;
       a.N = (int)l.N;
       a.K = (int)K;
-      ok = hxq::gemm2_path_ok(a, pk12);
+      ok5 = ok5 && hxq::gemm5_path_ok(a, pk12);
+      ok3 = ok3 && hxq::gemm2_path_ok(a, pk12);
+      ok = ok5 || ok3;
       gs[ng++] = {static_cast<const float*>(l.codebook), l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz,
                   l.bias, l.y, (int)l.N, 0};
     }
     if (ok && ng == 0) return HXQ_OK;
     if (ok) {
       (void)hipGetLastError();
+      if (ok5 && (!ok3 || gemm5_preferred(gs, ng, (int)M)))
+        return status_of(hxq::launch_gemm5_grouped(gs, ng, pk12, x, (int)M, (int)K, stream));
       return status_of(hxq::launch_gemm_grouped(gs, ng, pk12, x, (int)M, (int)K, stream));
     }
   }
@@ -410,7 +435,7 @@ int hxq_select_variant(int fmt_pk12, int x_dtype, int64_t M, int64_t N, int64_t 
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return HXQ_ERR_SHAPE;
   if (fmt_pk12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
   const bool gemv_ok = K > 0 && K % 16 == 0;
-  const bool gemm_ok = x_dtype == HXQ_BF16 && K > 0 && K % (fmt_pk12 ? 64 : 32) == 0;
+  const bool gemm_ok = x_dtype == HXQ_BF16 && K > 0 && K % 32 == 0;
   return select(fmt_pk12 != 0, x_dtype == HXQ_BF16, M, K, gemv_ok, gemm_ok);
 }
 

@@ -614,8 +614,13 @@ __global__ __launch_bounds__(512) void stream_read_kernel(const u32x4* __restric
 }
 
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream) {
-  int grid = device_cu_count();
-  if (grid > sink_words) grid = sink_words;
+  // one workgroup per sink word (the caller picks the grid), no more than the
+  // buffer's pieces need
+  int64_t grid = sink_words;
+  const int64_t need = (bytes / 16 + 511) / 512;
+  if (grid > need) grid = need;
+  if (grid > 65535) grid = 65535;
+  if (grid < 1) grid = 1;
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(512), 0, stream,
                      static_cast<const u32x4*>(src), bytes / 16, sink);
   return hipGetLastError();
