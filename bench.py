@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2516.6   # MI355X dense bf16 matrix (256 CU x 2.4 GHz x 4096 flop/clk)
+FP32_PEAK_TFS = 157.3         # MI355X fp32 vector / matrix-core rate (the fp32-arithmetic paths)
 MALL_BYTES = 256 << 20
 ROTATE_BYTES = 2 * MALL_BYTES
 GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
@@ -268,33 +269,171 @@ class LayerSet:
         self.layer_bytes = [layer_bytes(l.fmt, l.N, l.K, l.nnz, M, xb) for l in layers]
 
 
-def stream_ceiling(torch, L, sets, steps):
-    """GB/s of hxq_stream_read over the gate and up index buffers of every
-    rotating copy (each launch reads one of them: the same bytes the
-    dominant launch streams, in the same rotation)."""
+def stream_ceiling(torch, L, nbytes, steps):
+    """Attainable read bandwidth at the dominant launch's size: hxq_stream_read
+    over contiguous buffers of `nbytes` (as many rotating copies as exceed
+    twice the Infinity Cache), for a sweep of grid sizes; the best is the
+    ceiling the decode kernels are compared against."""
+    nb = nbytes // 16 * 16
+    copies = max(2, -(-ROTATE_BYTES // nb))
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(i & 255) for i in range(copies)]
+    stream = torch.cuda.current_stream().cuda_stream
+    sweep = []
+    for words in (256, 512, 1024, 2048, 4096, 8192):
+        sink = torch.zeros(words, dtype=torch.int32, device="cuda")
+
+        def reader(b, sink=sink, words=words):
+            def f():
+                st = L.hxq_stream_read(b.data_ptr(), nb, sink.data_ptr(), words, stream)
+                if st != 0:
+                    raise RuntimeError("hxq_stream_read failed with status %d" % st)
+            return f
+
+        calls = [[reader(b)] for b in bufs]
+        n = max(steps, len(bufs))
+        avg = time_steps(torch, calls, n, 2) / n
+        sweep.append(dict(workgroups=words, avg_us=round(avg * 1e3, 3), gbs=round(nb / (avg * 1e-3) / 1e9, 1)))
+    best = max(sweep, key=lambda r: r["gbs"])
+    del bufs
+    torch.cuda.empty_cache()
+    return dict(kernel="stream_read_kernel (hxq_stream_read)", bytes_per_launch=nb, rotating_copies=copies,
+                best_workgroups=best["workgroups"], avg_us=best["avg_us"], gbs=best["gbs"], sweep=sweep)
+
+
+def percentiles(torch, calls, n):
+    """p10 / p50 / p90 of single launch durations (an event pair around each
+    launch, copies rotating; the first launches are warm-up)."""
     import numpy as np
 
-    bufs = []
-    for devs in sets.devs:
-        for n in GROUPS[DOMINANT]:
-            bufs.append(devs[sets.by_name[n]]["indices"])
-    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream().cuda_stream
+    R = len(calls)
+    for s in range(4):
+        for f in calls[s % R]:
+            f()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    hold_gpu(torch, 20 + n * 0.05)
+    for s in range(n):
+        evs[s][0].record()
+        for f in calls[s % R]:
+            f()
+        evs[s][1].record()
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return dict(p10_us=round(float(np.percentile(d, 10)), 3), p50_us=round(float(np.percentile(d, 50)), 3),
+                p90_us=round(float(np.percentile(d, 90)), 3), launches=n)
 
-    def reader(b):
-        def f():
-            st = L.hxq_stream_read(b.data_ptr(), b.numel(), sink.data_ptr(), 4096, stream)
-            if st != 0:
-                raise RuntimeError("hxq_stream_read failed with status %d" % st)
-        return f
 
-    calls = [[reader(b)] for b in bufs]
-    n = max(steps, len(bufs))
-    total = time_steps(torch, calls, n, 2)
-    avg = total / n
-    nbytes = bufs[0].numel()
-    return dict(kernel="stream_read_kernel (hxq_stream_read)", bytes_per_launch=nbytes,
-                avg_us=round(avg * 1e3, 3), gbs=round(nbytes / (avg * 1e-3) / 1e9, 1))
+def roof(bytes_, flops, t_us, arith):
+    """GB/s and TFLOP/s of one measurement and its fraction of the binding
+    roof: HBM, or the compute rate of its arithmetic (fp32 vector / matrix
+    cores at 157.3 TFLOP/s, bf16 matrix cores at 2516.6), whichever would take
+    longer at 100%."""
+    t = t_us * 1e-6
+    peak = FP32_PEAK_TFS if arith == "f32" else MFMA_BF16_PEAK_TFS
+    t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
+    t_cmp = flops / (peak * 1e12)
+    bound = "hbm" if t_hbm >= t_cmp else ("fp32_alu" if arith == "f32" else "mfma_bf16")
+    return dict(gbs=round(bytes_ / t / 1e9, 1), tflops=round(flops / t / 1e12, 2),
+                frac_hbm=round(bytes_ / t / 1e9 / HBM_PEAK_GBS, 4),
+                frac_compute=round(flops / t / 1e12 / peak, 4), bound=bound,
+                frac_of_binding=round(max(t_hbm, t_cmp) / t, 4))
+
+
+def measure_layers(torch, L, B, layers, cases, steps, warmup, stream, cfg_x):
+    """Single-layer forwards of `layers` for each (M, x dtype) in `cases`, over
+    rotating copies of the layers (>= 512 MB in all), timed back to back.
+    Returns one record per (layer, M, dtype) with its binding-roof fraction."""
+    import numpy as np
+
+    from hxq_synth import gen
+
+    nbytes = sum(l.compressed_bytes() for l in layers)
+    copies = max(1, -(-ROTATE_BYTES // nbytes))
+    devs = [[to_dev(l, torch) for l in layers] for _ in range(copies)]
+    rows = []
+    for M, xdt in cases:
+        for i, lay in enumerate(layers):
+            xf = gen.synth_x(cfg_x, i, M, lay.K)
+            if xdt == "bf16":
+                x = torch.from_numpy(gen.to_bf16_bits(xf).view(np.int16)).cuda().view(torch.bfloat16)
+            else:
+                x = torch.from_numpy(xf).cuda()
+            y = torch.empty((M, lay.N), dtype=torch.float32, device="cuda")
+            calls = [[LayerCall(L, B, row[i], y, x, M, lay.N, lay.K, stream, pk12=lay.fmt == "pk12")]
+                     for row in devs]
+            n = max(steps, copies)
+            t_us = time_steps(torch, calls, n, warmup) / n * 1e3
+            xb = 2 if xdt == "bf16" else 4
+            arith = "bf16" if (xdt == "bf16" and M > 16) else "f32"
+            r = dict(layer=lay.name, fmt=lay.fmt, N=lay.N, K=lay.K, M=M, x=xdt, avg_us=round(t_us, 3))
+            r.update(roof(layer_bytes(lay.fmt, lay.N, lay.K, lay.nnz, M, xb), 2.0 * M * lay.N * lay.K, t_us, arith))
+            rows.append(r)
+            del x, y
+    del devs
+    torch.cuda.empty_cache()
+    return dict(rotating_copies=copies, layers=rows)
+
+
+def config_blocks(torch, L, B, stream, steps, warmup):
+    """The single-layer configuration (0), the Mamba2-shaped projections at
+    1, 16 and 64 tokens in fp32 and bf16 (2) and the pk12 gate/down shapes at
+    1 and 16 tokens (3), each with its binding roof."""
+    from hxq_synth import gen
+
+    out = {}
+    out["config0"] = measure_layers(torch, L, B, gen.config_layers(0), [(1, "f32")], steps, warmup, stream, 0)
+    out["config0"]["workload"] = "single 256x256 u8 layer, M=1, fp32 x (latency-bound: 70 KB)"
+    log("config 0: %.2f us" % out["config0"]["layers"][0]["avg_us"])
+    out["config2"] = measure_layers(torch, L, B, gen.config_layers(2),
+                                    [(m, d) for d in ("f32", "bf16") for m in (1, 16, 64)], steps, warmup, stream, 2)
+    out["config2"]["workload"] = ("Mamba2-1.3B-shaped u8 projections (in_proj 8512x2048, out_proj 2048x4096), "
+                                  "0.1% sidecar, M = 1, 16, 64, fp32 and bf16 x")
+    log("config 2: " + ", ".join("%s M=%d %s %.1f us" % (r["layer"], r["M"], r["x"], r["avg_us"])
+                                 for r in out["config2"]["layers"]))
+    pk = [gen.random_layer(9100 + i, N, K, "pk12", nnz=N * K // 2000) for i, (_, N, K) in enumerate(gen.PK12_LAYERS)]
+    for l, (name, _, _) in zip(pk, gen.PK12_LAYERS):
+        l.name = name
+    out["config3"] = measure_layers(torch, L, B, pk, [(1, "f32"), (16, "f32")], steps, warmup, stream, 3)
+    out["config3"]["workload"] = ("2D-VQ pk12 gate/down shapes (11008x2048, 2048x11008), 0.05% sidecar, "
+                                  "M = 1 and 16, fp32 x; seeded random pair indices and codebook (the "
+                                  "kernels' speed does not depend on how the codebook was fit)")
+    log("config 3: " + ", ".join("%s M=%d %.1f us" % (r["layer"], r["M"], r["avg_us"])
+                                 for r in out["config3"]["layers"]))
+    return out
+
+
+def prefill_big(torch, L, B, layers, stream, steps):
+    """Config 4 at M = 25600 (50 chunks of 512 tokens, bf16 x): gate|up as one
+    launch sharing x, then down, as a prefill step issues them."""
+    import numpy as np
+
+    from hxq_synth import gen
+
+    M = 25600
+    by = {l.name: l for l in layers}
+    sel = [by["gate"], by["up"], by["down"]]
+    devs = [to_dev(l, torch) for l in sel]
+    x_gu = torch.from_numpy(gen.to_bf16_bits(gen.synth_x(4, 4, M, 2048)).view(np.int16)).cuda().view(torch.bfloat16)
+    x_dn = torch.from_numpy(gen.to_bf16_bits(gen.synth_x(4, 6, M, 11008)).view(np.int16)).cuda().view(torch.bfloat16)
+    ys = [torch.empty((M, l.N), dtype=torch.float32, device="cuda") for l in sel]
+    gu = GroupCall(L, B, devs[:2], ys[:2], x_gu, M, 2048, stream)
+    dn = LayerCall(L, B, devs[2], ys[2], x_dn, M, sel[2].N, sel[2].K, stream)
+    t_gu = time_steps(torch, [[gu]], steps, 1) / steps * 1e3
+    t_dn = time_steps(torch, [[dn]], steps, 1) / steps * 1e3
+    f_gu = 2.0 * 2.0 * M * 11008 * 2048
+    f_dn = 2.0 * M * 2048 * 11008
+    b_gu = group_bytes(sel[:2], M, 2)
+    b_dn = layer_bytes("u8", sel[2].N, sel[2].K, sel[2].nnz, M, 2)
+    r_gu = dict(launch="gate|up", avg_us=round(t_gu, 2))
+    r_gu.update(roof(b_gu, f_gu, t_gu, "bf16"))
+    r_dn = dict(launch="down", avg_us=round(t_dn, 2))
+    r_dn.update(roof(b_dn, f_dn, t_dn, "bf16"))
+    tf = (f_gu + f_dn) / ((t_gu + t_dn) * 1e-6) / 1e12
+    del devs, x_gu, x_dn, ys
+    torch.cuda.empty_cache()
+    return dict(workload="gate|up and down of the Qwen2.5-3B-shaped u8 set at M=25600 (50 x 512 tokens), bf16 x",
+                M=M, step_us=round(t_gu + t_dn, 2), tflops=round(tf, 1),
+                frac_of_mfma_peak=round(tf / MFMA_BF16_PEAK_TFS, 4), launches=[r_gu, r_dn])
 
 
 def prefill_pk12(torch, L, B, stream, M, steps):
@@ -371,31 +510,112 @@ def buffered_baseline(torch, L, B, layers, stream, M, steps, fused_step_us):
 
 
 def cpu_baseline(layers, M, budget_s=15.0):
-    """The CPU oracle over the same layer set, as many whole steps as fit in
-    about `budget_s` seconds (at least one)."""
+    """The CPU oracle (fp64 numpy) over the same layer set: three runs, each
+    as many whole steps as fit in a third of `budget_s` (at least one), the
+    median reported; BLAS threads as numpy has them (normally one per core the
+    process may run on)."""
+    import numpy as np
+
     import oracle
     from hxq_synth import gen
 
     xs = [gen.synth_x(1, i, M, l.K) for i, l in enumerate(layers)]
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        for lay, x in zip(layers, xs):
-            oracle.hxq_linear_fwd_u8(lay.codebook, lay.indices, lay.rows, lay.cols, lay.deltas, x,
-                                     "f32", lay.bias, want_bound=False)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 500:
-            break
+    byts = sum(layer_bytes(l.fmt, l.N, l.K, l.nnz, M, 4) for l in layers)
+    rates, total_steps, total_s = [], 0, 0.0
+    for _ in range(3):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            for lay, x in zip(layers, xs):
+                oracle.hxq_linear_fwd_u8(lay.codebook, lay.indices, lay.rows, lay.cols, lay.deltas, x,
+                                         "f32", lay.bias, want_bound=False)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s / 3 or steps >= 200:
+                break
+        rates.append(byts * steps / el / 1e9)
+        total_steps += steps
+        total_s += el
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        cores = 1
-    byts = sum(layer_bytes(l.fmt, l.N, l.K, l.nnz, M, 4) for l in layers)
-    return dict(value=round(byts * steps / el / 1e9, 4), unit="GB/s", cores=int(cores), kind="oracle",
-                sample="%d full step(s) of the 7-layer set at M=%d (fp64 numpy oracle), %.1f s"
-                       % (steps, M, el))
+        blas = None
+    return dict(value=round(float(np.median(rates)), 4), unit="GB/s", cores=len(os.sched_getaffinity(0)),
+                blas_threads=blas, kind="oracle", runs=[round(r, 4) for r in rates],
+                sample="3 runs (median reported) of whole steps of the 7-layer Qwen2.5-3B-shaped u8 set at M=%d "
+                       "(fp64 numpy oracle); %d steps in %.1f s" % (M, total_steps, total_s))
+
+
+def cpu_single_thread(layer_sets):
+    """The CPU oracle on one thread: one forward per layer of each
+    configuration at one token (configs 0-3), median of three."""
+    import numpy as np
+
+    import oracle
+    from hxq_synth import gen
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        return None
+    out = {}
+    with threadpool_limits(limits=1):
+        for name, cfg, lays in layer_sets:
+            byts = sum(layer_bytes(l.fmt, l.N, l.K, l.nnz, 1, 4) for l in lays)
+            times = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                for i, lay in enumerate(lays):
+                    x = gen.synth_x(cfg, i, 1, lay.K)
+                    if lay.fmt == "u8":
+                        oracle.hxq_linear_fwd_u8(lay.codebook, lay.indices, lay.rows, lay.cols, lay.deltas, x,
+                                                 "f32", lay.bias, want_bound=False)
+                    else:
+                        oracle.hxq_linear_fwd_pk12(lay.codebook, lay.indices, lay.rows, lay.cols, lay.deltas, x,
+                                                   "f32", lay.bias, lay.N, lay.K, want_bound=False)
+                times.append(time.perf_counter() - t0)
+            t = float(np.median(times))
+            out[name] = dict(step_ms=round(t * 1e3, 2), gbs=round(byts / t / 1e9, 4))
+    return out
+
+
+def receipt(torch, props, layers):
+    """What the numbers were measured on and with: hardware, software
+    versions, and the SHA-256 of the seeded inputs (per layer, over its
+    codebook, indices, sidecar and bias arrays)."""
+    import hashlib
+    import platform
+
+    import numpy as np
+
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    inputs = {}
+    for l in layers:
+        h = hashlib.sha256()
+        for k, v in sorted(l.sha256().items()):
+            h.update((k + v).encode())
+        inputs[l.name] = h.hexdigest()[:16]
+    return dict(gpu=props.name, arch=getattr(props, "gcnArchName", None), cus=props.multi_processor_count,
+                gpu_mem_gib=round(props.total_memory / 2 ** 30, 1), host_cpu=cpu,
+                host_cores=len(os.sched_getaffinity(0)), rocm=rocm, torch=torch.__version__,
+                torch_hip=getattr(torch.version, "hip", None), numpy=np.__version__,
+                python=platform.python_version(), inputs_sha256=inputs,
+                input_seeds="SeedSequence([20260403, cfg, layer, stream]) (hxq_synth)")
 
 
 def main(argv=None):
@@ -408,6 +628,9 @@ def main(argv=None):
     ap.add_argument("--no-extras", action="store_true", help="only the headline step (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (for HBM counter scaling)")
+    ap.add_argument("--profile-decode", type=int, default=0, metavar="M",
+                    help="only run --steps grouped decode steps at M tokens (fp32 x) and print their "
+                         "per-launch times (for profiler runs at other token counts)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -447,6 +670,17 @@ def main(argv=None):
     copies = max(1, -(-ROTATE_BYTES // set_bytes))
     log("set %.1f MB compressed, %d rotating copies" % (set_bytes / 1e6, copies))
 
+    if args.profile_decode > 0:
+        sp = LayerSet(torch, L, B, layers, args.profile_decode, "f32", 1, copies, stream)
+        total = time_steps(torch, sp.grouped, args.steps, args.warmup)
+        per = []
+        for g in range(len(GROUPS)):
+            tg = time_steps(torch, [[row[g]] for row in sp.grouped], args.steps, 2)
+            per.append(dict(launch="|".join(GROUPS[g]), avg_us=round(tg / args.steps * 1e3, 3)))
+        print(json.dumps(dict(profile_decode_m=args.profile_decode, steps=args.steps,
+                              step_us=round(total / args.steps * 1e3, 3), launches=per)))
+        return 0
+
     # ---- headline: M = 1, grouped launches
     s1 = LayerSet(torch, L, B, layers, 1, "f32", 1, copies, stream)
     total_ms = time_steps(torch, s1.grouped, args.steps, args.warmup)
@@ -479,14 +713,17 @@ def main(argv=None):
             layers=[dict(layer=l.name, N=l.N, K=l.K, bytes=b, avg_us=round(m * 1e3, 3),
                          gbs=round(b / (m * 1e-3) / 1e9, 1))
                     for l, b, m in zip(layers, s1.layer_bytes, avg1)])
-        extras["stream_ceiling"] = stream_ceiling(torch, L, s1, args.steps)
-        log("stream ceiling %.1f GB/s" % extras["stream_ceiling"]["gbs"])
+        extras["dominant_launch_percentiles"] = percentiles(torch, [[row[DOMINANT]] for row in s1.grouped], 200)
         extras["input_gradient_m1"] = input_gradient(torch, L, B, layers, s1.devs, 1, "f32", args.steps,
                                                      args.warmup, stream)
         log("input gradient M=1 step %.1f us, %.1f GB/s" % (extras["input_gradient_m1"]["step_us"],
                                                             extras["input_gradient_m1"]["gbs"]))
     del s1
     torch.cuda.empty_cache()
+    if not args.no_extras:
+        extras["stream_ceiling"] = stream_ceiling(torch, L, dom_bytes, args.steps)
+        log("stream ceiling %.1f GB/s (%d workgroups)" % (extras["stream_ceiling"]["gbs"],
+                                                          extras["stream_ceiling"]["best_workgroups"]))
 
     if not args.no_extras:
         s8 = LayerSet(torch, L, B, layers, 8, "f32", 1, copies, stream)
@@ -500,10 +737,32 @@ def main(argv=None):
             gbs=round(sum(s8.group_bytes) / (total8 / args.steps * 1e-3) / 1e9, 1),
             launches=[dict(launch="|".join(g), avg_us=round(m * 1e3, 3)) for g, m in zip(GROUPS, avg8)])
         log("M=8 grouped step %.2f us" % (total8 / args.steps * 1e3))
+        m8_bytes = sum(s8.group_bytes)
+        extras["decode_m8"].update(roof(m8_bytes, sum(2.0 * 8 * l.N * l.K for l in layers),
+                                        total8 / args.steps * 1e3, "f32"))
         del s8
         torch.cuda.empty_cache()
+        extras.update(config_blocks(torch, L, B, stream, args.steps, args.warmup))
 
     if not args.no_extras and not args.no_prefill:
+        # config 4 at 512 tokens: the grouped step
+        s5 = LayerSet(torch, L, B, layers, 512, "bf16", 4, 1, stream)
+        st5 = max(5, args.steps // 5)
+        t5 = time_steps(torch, s5.grouped, st5, 2) / st5
+        avg5 = []
+        for g in range(len(GROUPS)):
+            avg5.append(time_steps(torch, [[row[g]] for row in s5.grouped], st5, 1) / st5)
+        fl5 = sum(2.0 * 512 * l.N * l.K for l in layers)
+        tf5 = fl5 / (t5 * 1e-3) / 1e12
+        gfl5 = [sum(2.0 * 512 * layers[s5.by_name[n]].N * layers[s5.by_name[n]].K for n in g) for g in GROUPS]
+        extras["prefill_m512"] = dict(
+            workload="Qwen2.5-3B-shaped u8 layer set, M=512, bf16 x; launches q|k|v, o, gate|up, down", M=512,
+            step_us=round(t5 * 1e3, 2), tflops=round(tf5, 2), frac_of_mfma_peak=round(tf5 / MFMA_BF16_PEAK_TFS, 4),
+            launches=[dict(launch="|".join(g), avg_us=round(m * 1e3, 2), **roof(b, f, m * 1e3, "bf16"))
+                      for g, m, f, b in zip(GROUPS, avg5, gfl5, s5.group_bytes)])
+        log("prefill M=512 step %.1f us, %.1f TFLOP/s" % (t5 * 1e3, tf5))
+        del s5
+        torch.cuda.empty_cache()
         M = 2048
         sp = LayerSet(torch, L, B, layers, M, "bf16", 4, 1, stream)
         steps = max(3, args.steps // 10)
@@ -544,6 +803,9 @@ def main(argv=None):
             % extras["buffered_baseline"]["step_us"])
         log("pk12 prefill M=2048: %s" % ", ".join("%s %.1f us" % (r["layer"], r["avg_us"])
                                                   for r in extras["prefill_pk12"]["layers"]))
+        extras["prefill_m25600"] = prefill_big(torch, L, B, layers, stream, 3)
+        log("prefill M=25600 gate|up + down %.1f us, %.1f TFLOP/s" % (extras["prefill_m25600"]["step_us"],
+                                                                      extras["prefill_m25600"]["tflops"]))
 
     out = {
         "metric": "HelixLinear decode GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak)",
@@ -567,14 +829,23 @@ def main(argv=None):
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic("decode_gemv_gate_up_m1"),
                      "avg_launch_us": round(dom_avg_s * 1e6, 3),
-                     "algorithmic_bytes_per_launch": int(dom_bytes)},
+                     "algorithmic_bytes_per_launch": int(dom_bytes),
+                     "frac_of_stream_ceiling": (round(achieved / extras["stream_ceiling"]["gbs"], 4)
+                                                if "stream_ceiling" in extras else None)},
         "per_launch_m1": per_group,
         "cpu_baseline": None,
     }
     out.update(extras)
+    out["receipt"] = receipt(torch, props, layers)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(layers, 1)
+        if not args.no_extras:
+            pk = [gen.random_layer(9100 + i, N, K, "pk12", nnz=N * K // 2000)
+                  for i, (_, N, K) in enumerate(gen.PK12_LAYERS)]
+            out["cpu_baseline"]["single_thread_m1"] = cpu_single_thread(
+                [("config0", 0, gen.config_layers(0)), ("config1", 1, layers), ("config2", 2, gen.config_layers(2)),
+                 ("config3", 3, pk)])
     print(json.dumps(out), flush=True)
     return 0
 
