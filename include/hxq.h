@@ -68,7 +68,8 @@ enum hxq_status {
   HXQ_ERR_ALIGN = -4,       /* x not aligned to its element size, or y / codebook / bias /
                                sidecar arrays not 4-byte aligned */
   HXQ_ERR_UNSUPPORTED = -5, /* a combination this version does not implement */
-  HXQ_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+  HXQ_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
+  HXQ_ERR_SCRATCH = -7      /* hxq_linear_bwd_x_noalloc: the call needs more than HXQ_SCRATCH_BYTES */
 };
 
 enum hxq_dtype { HXQ_F32 = 0, HXQ_BF16 = 1 };
@@ -233,6 +234,29 @@ int hxq_linear_bwd_x(int fmt, const float* codebook, const uint8_t* indices,
                      const void* dy, int dy_dtype, float* dx,
                      int64_t M, int64_t N, int64_t K,
                      void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the input
+ * gradient of hxq_linear_bwd_x without a workspace argument.  Its row-split
+ * partial sums and sidecar bins live in a device array the library owns,
+ * HXQ_SCRATCH_BYTES per GPU (each GPU the library runs on holds its own copy
+ * until the process ends; nothing is allocated at call time).
+ *   Arguments, arithmetic and result as for hxq_linear_bwd_x with a workspace
+ *   of hxq_linear_bwd_x_workspace(...) bytes: the same kernels run.
+ *   Calls on one GPU share its array and its contents are left behind: two
+ *   calls that overlap on one GPU (two streams, or two host threads without
+ *   ordering between their streams) race and give undefined results.
+ *   The first call on a device looks up the array's device address with that
+ *   device current (HXQ_ERR_HIP if that fails).
+ * Errors: those of hxq_linear_bwd_x, and HXQ_ERR_SCRATCH (nothing launched)
+ * when the workspace query exceeds HXQ_SCRATCH_BYTES. */
+#define HXQ_SCRATCH_BYTES (48 * 1024 * 1024)
+
+int hxq_linear_bwd_x_noalloc(int fmt, const float* codebook, const uint8_t* indices,
+                             const int32_t* sc_rows, const int32_t* sc_cols,
+                             const float* sc_deltas, int64_t nnz,
+                             const void* dy, int dy_dtype, float* dx,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /* Bytes of workspace hxq_linear_bwd_x uses on the current device for these
  * sizes with pointers aligned to 16 bytes (0 when it needs none), or a

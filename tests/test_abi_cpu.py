@@ -267,3 +267,23 @@ def test_bwd_x_workspace_query(L):
     # the matrix-core path also keeps the sidecar bins there
     assert q(B.HXQ_FMT_U8, BF, 256, 2048, 2048, 4096) > q(B.HXQ_FMT_U8, BF, 256, 2048, 2048, 0)
 
+
+def test_noalloc_bwd_rejects_oversize_before_any_hip_call(L):
+    # a call whose workspace would exceed the library's scratch returns
+    # HXQ_ERR_SCRATCH after validating its arguments and before touching a
+    # device (this container has none); bad arguments still come first
+    M, N, K = 512, 65536, 16384
+    need = L.hxq_linear_bwd_x_workspace(B.HXQ_FMT_U8, B.HXQ_BF16, M, N, K, N * K // 1000)
+    assert need > B.HXQ_SCRATCH_BYTES
+    st = L.hxq_linear_bwd_x_noalloc(B.HXQ_FMT_U8, FAKE, FAKE, FAKE, FAKE, FAKE, N * K // 1000, FAKE, B.HXQ_BF16,
+                                    FAKE, M, N, K, None)
+    assert st == B.HXQ_ERR_SCRATCH
+    assert b"scratch" in L.hxq_status_str(B.HXQ_ERR_SCRATCH)
+    st = L.hxq_linear_bwd_x_noalloc(B.HXQ_FMT_U8, FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, 7, FAKE, M, N, K, None)
+    assert st == B.HXQ_ERR_DTYPE
+    st = L.hxq_linear_bwd_x_noalloc(B.HXQ_FMT_U8, FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, B.HXQ_F32, None, M, N, K,
+                                    None)
+    assert st == B.HXQ_ERR_NULL
+    # M == 0 does nothing
+    assert L.hxq_linear_bwd_x_noalloc(B.HXQ_FMT_U8, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, B.HXQ_F32, FAKE, 0, N, K,
+                                      None) == B.HXQ_OK

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     HxqLayer,
     hxq_dequant_bf16,
     hxq_linear_bwd_x,
+    hxq_linear_bwd_x_noalloc,
     hxq_linear_bwd_x_workspace,
     hxq_linear_fwd_grouped,
     hxq_linear_fwd_pk12,

@@ -27,6 +27,8 @@ HXQ_ERR_DTYPE = -3
 HXQ_ERR_ALIGN = -4
 HXQ_ERR_UNSUPPORTED = -5
 HXQ_ERR_HIP = -6
+HXQ_ERR_SCRATCH = -7
+HXQ_SCRATCH_BYTES = 48 * 1024 * 1024
 
 HXQ_F32 = 0
 HXQ_BF16 = 1
@@ -86,6 +88,7 @@ SIGNATURES = {
     "hxq_linear_bwd_x": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "hxq_linear_bwd_x_ex": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P, _I64, _P,
                                    _INT]),
+    "hxq_linear_bwd_x_noalloc": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P]),
     "hxq_linear_bwd_x_workspace": (_I64, [_INT, _INT, _I64, _I64, _I64, _I64]),
     "hxq_select_variant": (_INT, [_INT, _INT, _I64, _I64, _I64]),
     "hxq_status_str": (ctypes.c_char_p, [_INT]),
@@ -320,6 +323,34 @@ def hxq_linear_bwd_x(fmt: int, codebook, indices, sc_rows, sc_cols, sc_deltas, d
                                    wptr, wbytes, _stream(stream, dev), variant)
     if st != HXQ_OK:
         raise HxqError(st, "hxq_linear_bwd_x")
+
+
+def hxq_linear_bwd_x_noalloc(fmt: int, codebook, indices, sc_rows, sc_cols, sc_deltas, dy, dx, K: int,
+                             stream=None) -> None:
+    """dx <- dy (C[indices] + S), like hxq_linear_bwd_x, with the library's own
+    device scratch instead of a workspace (nothing is allocated, here or in
+    the library).  Calls that overlap on one GPU race on that scratch."""
+    torch = _torch()
+    if codebook.dtype != torch.float32 or codebook.numel() != (256 if fmt == HXQ_FMT_U8 else 8192):
+        raise ValueError("wrong codebook size or dtype")
+    if indices.dtype != torch.uint8 or indices.dim() != 2 or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous uint8 matrix")
+    N = indices.shape[0]
+    row = K if fmt == HXQ_FMT_U8 else 3 * ((K + 3) // 4)
+    if indices.shape[1] != row:
+        raise ValueError("index rows hold %d bytes, expected %d" % (indices.shape[1], row))
+    if dy.dim() != 2 or not dy.is_contiguous() or dy.shape[1] != N:
+        raise ValueError("dy must be a contiguous [M, N] tensor")
+    M = dy.shape[0]
+    if dx.dtype != torch.float32 or tuple(dx.shape) != (M, K) or not dx.is_contiguous():
+        raise ValueError("dx must be a contiguous float32 [M, K] tensor")
+    nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
+    dev = _check_device(codebook, indices, sc_rows, sc_cols, sc_deltas, dy, dx)
+    st = lib().hxq_linear_bwd_x_noalloc(fmt, _ptr(codebook), _ptr(indices), _ptr(sc_rows), _ptr(sc_cols),
+                                        _ptr(sc_deltas), nnz, _ptr(dy), _x_dtype(dy), _ptr(dx), M, N, K,
+                                        _stream(stream, dev))
+    if st != HXQ_OK:
+        raise HxqError(st, "hxq_linear_bwd_x_noalloc")
 
 
 def grouped_layers(fmt: int, layers, M: int, K: int, x=None):

@@ -3,8 +3,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdint>
+#include <cstdlib>
+#include <mutex>
 
 #include "../../include/hxq.h"
 #include "hxq_launch.h"
@@ -112,10 +115,11 @@ int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32
   }
 }
 
-int backward_x(int fmt, const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
-               const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* dy, int dy_dtype,
-               float* dx, int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
-               hipStream_t stream, int variant) {
+// Argument checks of the input gradient (host only).  Returns HXQ_OK or an error.
+int validate_bwd(int fmt, const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
+                 const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* dy, int dy_dtype,
+                 const float* dx, int64_t M, int64_t N, int64_t K, const void* workspace, int64_t workspace_bytes,
+                 int variant) {
   if (fmt != HXQ_FMT_U8 && fmt != HXQ_FMT_PK12) return HXQ_ERR_SHAPE;
   const bool pk12 = fmt == HXQ_FMT_PK12;
   if (dy_dtype != HXQ_F32 && dy_dtype != HXQ_BF16) return HXQ_ERR_DTYPE;
@@ -132,6 +136,18 @@ int backward_x(int fmt, const float* codebook, const uint8_t* indices, const int
   if (misaligned(dy, ds) || misaligned(dx, 4) || misaligned(codebook, 4) || misaligned(sc_rows, 4) ||
       misaligned(sc_cols, 4) || misaligned(sc_deltas, 4) || misaligned(workspace, 4))
     return HXQ_ERR_ALIGN;
+  return HXQ_OK;
+}
+
+int backward_x(int fmt, const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
+               const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* dy, int dy_dtype,
+               float* dx, int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+               hipStream_t stream, int variant) {
+  const int vst = validate_bwd(fmt, codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, dy, dy_dtype, dx, M, N, K,
+                               workspace, workspace_bytes, variant);
+  if (vst != HXQ_OK) return vst;
+  const bool pk12 = fmt == HXQ_FMT_PK12;
+  if (M == 0 || K == 0) return HXQ_OK;
   (void)hipGetLastError();
   if (N == 0) return status_of(hxq::launch_fill_zero(dx, M * K, stream));
   hxq::BwdArgs a = {};
@@ -163,9 +179,58 @@ int backward_x(int fmt, const float* codebook, const uint8_t* indices, const int
   return status_of(hxq::launch_bwdx_valu(a, pk12, stream));
 }
 
+// ---- device scratch of the allocation-free input gradient.  One array per
+// GPU (each device holds its own copy of this module's globals), kept until
+// the process ends.  In host code `scratch` only names the symbol: its
+// device address comes from hipGetSymbolAddress, taken once per device.
+static __device__ __align__(256) unsigned char scratch[HXQ_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address (set up on the first call on that
+// device, with it current).
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HXQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return HXQ_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HXQ_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return HXQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int hxq_linear_bwd_x_noalloc(int fmt, const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
+                             const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* dy,
+                             int dy_dtype, float* dx, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int vst = validate_bwd(fmt, codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, dy, dy_dtype, dx, M, N, K,
+                               nullptr, 0, HXQ_VARIANT_AUTO);
+  if (vst != HXQ_OK) return vst;
+  if (M == 0 || K == 0) return HXQ_OK;
+  // the workspace the allocating entry point would be given
+  const int64_t need = hxq_linear_bwd_x_workspace(fmt, dy_dtype, M, N, K, nnz);
+  if (need < 0) return (int)need;
+  if (need > (int64_t)HXQ_SCRATCH_BYTES) return HXQ_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int st = scratch_address(&ws);
+    if (st != HXQ_OK) return st;
+  }
+  return backward_x(fmt, codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, dy, dy_dtype, dx, M, N, K, ws, need,
+                    stream, HXQ_VARIANT_AUTO);
+}
 
 int hxq_linear_bwd_x(int fmt, const float* codebook, const uint8_t* indices, const int32_t* sc_rows,
                      const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* dy, int dy_dtype,
@@ -448,6 +513,7 @@ const char* hxq_status_str(int status) {
     case HXQ_ERR_ALIGN: return "misaligned pointer";
     case HXQ_ERR_UNSUPPORTED: return "unsupported combination";
     case HXQ_ERR_HIP: return "HIP launch error";
+    case HXQ_ERR_SCRATCH: return "the call needs more device scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }
