@@ -618,6 +618,118 @@ def receipt(torch, props, layers):
                 input_seeds="SeedSequence([20260403, cfg, layer, stream]) (hxq_synth)")
 
 
+# ---- summaries of rocprofv3 databases (host only: sqlite3, no GPU)
+
+def _db(path):
+    """The rocpd database at `path`, or the one file *_results.db under it."""
+    import glob
+    import sqlite3
+    if os.path.isdir(path):
+        found = sorted(glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True))
+        if len(found) != 1:
+            raise SystemExit("expected one *_results.db under %s, found %d" % (path, len(found)))
+        path = found[0]
+    return sqlite3.connect(path)
+
+
+def summarise_trace(path):
+    """Per kernel and grid size: calls, mean, median, p10, p90, min, max
+    duration (us)."""
+    rows = _db(path).execute("select name, grid_x, workgroup_x, duration from kernels order by start").fetchall()
+    by = {}
+    for name, gx, wx, d in rows:
+        by.setdefault("%s [%d wg]" % (name, gx // max(wx, 1)), []).append(d / 1e3)
+    out = ["%-90s %6s %9s %9s %9s %9s %9s %9s" % ("kernel", "calls", "avg_us", "median", "p10", "p90", "min",
+                                                  "max")]
+    for name, ds in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        v = sorted(ds)
+        q = lambda f: v[min(len(v) - 1, int(f * len(v)))]
+        out.append("%-90s %6d %9.3f %9.3f %9.3f %9.3f %9.3f %9.3f" % (name[:90], len(v), sum(v) / len(v), q(0.5),
+                                                                     q(0.1), q(0.9), v[0], v[-1]))
+    return "\n".join(out)
+
+
+def counters_by_kernel(path):
+    """{"kernel [workgroups wg]": {counter: [value per dispatch, in dispatch order]}}."""
+    rows = _db(path).execute("select kernel_name, grid_size_x, workgroup_size_x, counter_name, value, dispatch_id "
+                             "from counters_collection order by dispatch_id").fetchall()
+    by = {}
+    for k, gx, wx, c, v, _ in rows:
+        by.setdefault("%s [%d wg]" % (k, gx // max(wx, 1)), {}).setdefault(c, []).append(v)
+    return by
+
+
+def summarise_counters(path, match):
+    out = []
+    for k, cs in counters_by_kernel(path).items():
+        if match not in k:
+            continue
+        out.append(k)
+        for c in sorted(cs):
+            vs = cs[c]
+            out.append("   %-28s %16.1f per dispatch (%d dispatches)" % (c, sum(vs) / len(vs), len(vs)))
+    return "\n".join(out)
+
+
+def summarise_traffic(d, steps=10, warmup=10):
+    """FETCH_SIZE / WRITE_SIZE of the M = 1 decode launches (the bench run with
+    --no-extras, `steps` timed steps after `warmup`: its first decode
+    dispatches are whole steps, q|k|v, o, gate|up, down in turn), scaled by
+    what the counters read for the plain device copy of --copy-calibration.
+    Writes profiles/traffic.json and returns a text summary."""
+    def series(sub, counter, match):
+        cs = counters_by_kernel(os.path.join(d, sub))
+        vals = []
+        for k, c in cs.items():
+            if match in k and counter in c:
+                vals += c[counter]
+        return vals
+    copy_kib = (64 << 20) * 4 / 1024
+    cf = series("copyf", "FETCH_SIZE", "copyBuffer")
+    cw = series("copyw", "WRITE_SIZE", "copyBuffer")
+    fscale = copy_kib / (sum(cf) / len(cf))
+    wscale = copy_kib / (sum(cw) / len(cw))
+    fe = series("fetch", "FETCH_SIZE", "decode1_gemv")
+    wr = series("write", "WRITE_SIZE", "decode1_gemv")
+    n = len(GROUPS)
+    lo, hi = warmup * n, (warmup + steps) * n
+    if len(fe) < hi or len(wr) < hi:
+        raise SystemExit("fewer decode dispatches than %d steps" % (warmup + steps))
+    import numpy as np
+    from hxq_synth import gen
+    layers = gen.config_layers(1)
+    algo = []
+    for grp in GROUPS:
+        sel = [l for l in layers if l.name in grp]
+        algo.append(group_bytes(sel, 1, 4))
+    rec = {}
+    lines = ["launch     FETCH_SIZE KiB  WRITE_SIZE KiB    HBM bytes  algorithmic bytes  ratio"]
+    for g in range(n):
+        f = float(np.mean(fe[lo + g:hi:n]))
+        w = float(np.mean(wr[lo + g:hi:n]))
+        hbm = int(round((f * fscale + w * wscale) * 1024))
+        name = "|".join(GROUPS[g])
+        rec[name] = dict(fetch_kib=f, write_kib=w, hbm_bytes_per_launch=hbm, algorithmic_bytes=algo[g],
+                         ratio=round(hbm / algo[g], 4))
+        lines.append("%-9s %15.1f %15.1f %12d %18d %6.3f" % (name, f, w, hbm, algo[g], hbm / algo[g]))
+    dom = "|".join(GROUPS[DOMINANT])
+    out = {"decode_gemv_gate_up_m1": dict(rec[dom], source_digest=source_digest(), fetch_scale=round(fscale, 4),
+                                          write_scale=round(wscale, 4),
+                                          counters="FETCH_SIZE, WRITE_SIZE (KiB per dispatch, mean over the "
+                                                   "%d timed steps)" % steps),
+           "all_launches_m1": rec}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    head = ["calibration (plain 256 MiB device copy):",
+            "  FETCH_SIZE reads %.0f KiB per copy -> scale %.4f" % (sum(cf) / len(cf), fscale),
+            "  WRITE_SIZE reads %.0f KiB per copy -> scale %.4f" % (sum(cw) / len(cw), wscale), "",
+            "decode launches of the %d timed steps (mean per dispatch), scaled:" % steps]
+    tail = ["", "digest of the decode kernels' sources and headers (%s) when taken: %s"
+            % (", ".join(DECODE_SOURCES), source_digest())]
+    return "\n".join(head + lines + tail)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -631,7 +743,22 @@ def main(argv=None):
     ap.add_argument("--profile-decode", type=int, default=0, metavar="M",
                     help="only run --steps grouped decode steps at M tokens (fp32 x) and print their "
                          "per-launch times (for profiler runs at other token counts)")
+    ap.add_argument("--summarise-trace", metavar="DB", help="print a kernel-trace summary of a rocprofv3 database")
+    ap.add_argument("--summarise-counters", metavar="DB", help="print per-kernel counter means of a rocprofv3 "
+                                                              "database (kernels whose name holds --match)")
+    ap.add_argument("--match", default="hxq", help="kernel-name filter for --summarise-counters")
+    ap.add_argument("--summarise-traffic", metavar="DIR",
+                    help="DIR/{fetch,write,copyf,copyw}: write profiles/traffic.json from those counter runs")
     args = ap.parse_args(argv)
+    if args.summarise_trace:
+        print(summarise_trace(args.summarise_trace))
+        return 0
+    if args.summarise_counters:
+        print(summarise_counters(args.summarise_counters, args.match))
+        return 0
+    if args.summarise_traffic:
+        print(summarise_traffic(args.summarise_traffic))
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

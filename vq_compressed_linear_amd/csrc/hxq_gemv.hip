@@ -583,23 +583,41 @@ __global__ __launch_bounds__(512) void stream_read_kernel(const u32x4* __restric
   // the grid sweeps the buffer in order: each round every thread requests P
   // pieces, round r of the grid covering one contiguous window of
   // P * threads pieces (faster than one stretch per wave: the requests in
-  // flight stay close together)
+  // flight stay close together).  The next round's requests go out before
+  // this round's data is folded, so 2 P pieces per thread are in flight
+  // across the round boundary.
   constexpr int P = 4;
   const int lane = threadIdx.x & 63;
   const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   uint32_t acc = 0;
-  for (int64_t i0 = 0; i0 < n16; i0 += P * nthr) {
-    u32x4 v[P];
-    uint32_t keep[P];
+  auto request = [&](int64_t i0, u32x4 (&v)[P], uint32_t (&keep)[P]) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int64_t i = i0 + p * nthr + t;
       keep[p] = i < n16 ? 0xffffffffu : 0u;  // a thread past the end re-reads a valid piece and drops it
       v[p] = src[i < n16 ? i : n16 - 1];
     }
+  };
+  auto fold = [&](const u32x4 (&v)[P], const uint32_t (&keep)[P]) {
 #pragma unroll
     for (int p = 0; p < P; ++p) acc ^= (v[p].x ^ v[p].y ^ v[p].z ^ v[p].w) & keep[p];
+  };
+  // two register sets in turn (no copies, so no wait for data still in
+  // flight); requests past the end read valid pieces that are dropped
+  u32x4 va[P], vb[P];
+  uint32_t ka[P], kb[P];
+  const int64_t R = P * nthr;
+  const int64_t rounds = (n16 + R - 1) / R;
+  request(0, va, ka);
+  for (int64_t r = 0; r < rounds; r += 2) {
+    // (scheduling barriers keep each fold below the next round's requests)
+    request((r + 1) * R, vb, kb);
+    __builtin_amdgcn_sched_barrier(0);
+    fold(va, ka);
+    request((r + 2) * R, va, ka);
+    __builtin_amdgcn_sched_barrier(0);
+    fold(vb, kb);
   }
   // fold across the wave and the block; one word per block
   for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, kWave);
