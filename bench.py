@@ -743,6 +743,9 @@ def main(argv=None):
     ap.add_argument("--profile-decode", type=int, default=0, metavar="M",
                     help="only run --steps grouped decode steps at M tokens (fp32 x) and print their "
                          "per-launch times (for profiler runs at other token counts)")
+    ap.add_argument("--profile-prefill", type=int, default=0, metavar="M",
+                    help="only run --steps grouped prefill steps at M tokens (bf16 x) and print their "
+                         "per-launch times (for profiler runs)")
     ap.add_argument("--summarise-trace", metavar="DB", help="print a kernel-trace summary of a rocprofv3 database")
     ap.add_argument("--summarise-counters", metavar="DB", help="print per-kernel counter means of a rocprofv3 "
                                                               "database (kernels whose name holds --match)")
@@ -797,6 +800,16 @@ def main(argv=None):
     copies = max(1, -(-ROTATE_BYTES // set_bytes))
     log("set %.1f MB compressed, %d rotating copies" % (set_bytes / 1e6, copies))
 
+    if args.profile_prefill > 0:
+        sp = LayerSet(torch, L, B, layers, args.profile_prefill, "bf16", 4, 1, stream)
+        total = time_steps(torch, sp.grouped, args.steps, args.warmup)
+        per = []
+        for g in range(len(GROUPS)):
+            tg = time_steps(torch, [[row[g]] for row in sp.grouped], args.steps, 1)
+            per.append(dict(launch="|".join(GROUPS[g]), avg_us=round(tg / args.steps * 1e3, 3)))
+        print(json.dumps(dict(profile_prefill_m=args.profile_prefill, steps=args.steps,
+                              step_us=round(total / args.steps * 1e3, 3), launches=per)))
+        return 0
     if args.profile_decode > 0:
         sp = LayerSet(torch, L, B, layers, args.profile_decode, "f32", 1, copies, stream)
         total = time_steps(torch, sp.grouped, args.steps, args.warmup)

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
   const int Gl = (si + 1 < ga.nseg ? ga.wg0[si + 1] : G) - ga.wg0[si];
   const int b = bb - ga.wg0[si];
   const int N = a.N, K = ga.K;
-  const int r0 = (int)((int64_t)b * N / Gl), r1 = (int)((int64_t)(b + 1) * N / Gl);
+  const int r0 = split_point(b, N, Gl), r1 = split_point(b + 1, N, Gl);
   const int nrow = r1 - r0;
   const int nj = nrow > wave ? (nrow - wave + WAVES - 1) / WAVES : 0;  // this wave's rows
   constexpr int CB = PK12 ? 12 : 16;                                   // index bytes per chunk
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
   const bool srch = a.nnz > 0 && wave < 2 && nrow > 0;
   const int target = wave == 0 ? r0 : r1;
   RowWindow win;
-  if (srch) row_window_load(a.sc_rows, a.nnz, (int64_t)((double)a.nnz * (double)target / (double)N), win);
+  if (srch) row_window_load(a.sc_rows, a.nnz, sidecar_guess(a.nnz, target, N), win);
 
   // ---- index bytes of the wave's row j (past its last row: a valid stand-in, unused)
   typedef unsigned u32x3 __attribute__((ext_vector_type(3)));

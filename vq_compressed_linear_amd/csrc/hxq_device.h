@@ -45,6 +45,22 @@ __device__ __forceinline__ uint32_t byte_addr256(uint32_t w, uint32_t lo) {
   return __builtin_amdgcn_perm(w, lo, sel);
 }
 
+// floor(b * n / parts) for the static split of n items over `parts`
+// workgroups (b <= parts): 32-bit arithmetic when the product fits, which is
+// every launch plan here (a 64-bit division costs a few hundred scalar cycles
+// at kernel start)
+__device__ __forceinline__ int split_point(int b, int n, int parts) {
+  const uint64_t p = (uint64_t)(uint32_t)b * (uint32_t)n;
+  if (p <= 0xffffffffull) return (int)((uint32_t)p / (uint32_t)parts);
+  return (int)(p / (uint32_t)parts);
+}
+
+// First guess of where row `target` of n rows starts among nnz row-sorted
+// sidecar triplets (rows spread evenly); only a search hint.
+__device__ __forceinline__ int64_t sidecar_guess(int64_t nnz, int target, int n) {
+  return (int64_t)((float)nnz * ((float)target / (float)n));
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_load(uint32_t byte_addr, const unsigned char* base) {
   return *reinterpret_cast<const T*>(base + byte_addr);

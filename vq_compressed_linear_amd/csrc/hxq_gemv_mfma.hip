@@ -81,7 +81,7 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
   const int Gl = (si + 1 < ga.nseg ? ga.wg0[si + 1] : G) - ga.wg0[si];
   const int b = bb - ga.wg0[si];
   const int M = ga.M, N = a.N, K = ga.K;
-  const int f0 = (int)((int64_t)b * a.nfrag / Gl), f1 = (int)((int64_t)(b + 1) * a.nfrag / Gl);
+  const int f0 = split_point(b, a.nfrag, Gl), f1 = split_point(b + 1, a.nfrag, Gl);
   const int F = f1 - f0;  // FN - 1 .. FN, uniform
   const int r0 = f0 * 16, r1 = min(f1 * 16, N);
   const int nsl = (K + KS - 1) / KS;
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(gmv::THREADS, 1) void gemv_mfma(GemvMArgs ga) {
   const bool srch = a.nnz > 0 && wave < 2 && F > 0;  // uniform
   const int target = wave == 0 ? r0 : r1;
   RowWindow win;
-  if (srch) row_window_load(a.sc_rows, a.nnz, (int64_t)((double)a.nnz * (double)target / (double)N), win);
+  if (srch) row_window_load(a.sc_rows, a.nnz, sidecar_guess(a.nnz, target, N), win);
   u32x4 IQ[3][FN], XR[3][XPT];
   load_x(0, XR[0]);
   constexpr int CBV = PK12 ? 4096 * 8 / 16 / THREADS : 1;  // 16-byte codebook pieces per thread

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(gm4::THREADS, 1) void gemv_mfma4(GemvMArgs ga) {
   const int Gl = (si + 1 < ga.nseg ? ga.wg0[si + 1] : G) - ga.wg0[si];
   const int b = bb - ga.wg0[si];
   const int M = ga.M, N = a.N, K = ga.K;
-  const int f0 = (int)((int64_t)b * a.nfrag / Gl), f1 = (int)((int64_t)(b + 1) * a.nfrag / Gl);
+  const int f0 = split_point(b, a.nfrag, Gl), f1 = split_point(b + 1, a.nfrag, Gl);
   const int F = f1 - f0;
   const int r0 = f0 * 4, r1 = min(f1 * 4, N);
   const int ngrp = (F + FG - 1) / FG;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(gm4::THREADS, 1) void gemv_mfma4(GemvMArgs ga) {
   const bool srch = a.nnz > 0 && wave < 2 && F > 0;  // uniform
   const int target = wave == 0 ? r0 : r1;
   RowWindow win;
-  if (srch) row_window_load(a.sc_rows, a.nnz, (int64_t)((double)a.nnz * (double)target / (double)N), win);
+  if (srch) row_window_load(a.sc_rows, a.nnz, sidecar_guess(a.nnz, target, N), win);
 
   // ---- step t = (group t / nchw, chunk wave + 8 (t % nchw)): index bytes of
   // the group's FG fragments and x of the chunk for the TG token groups.  x is
@@ -280,9 +280,8 @@ __global__ __launch_bounds__(gm4::THREADS, 1) void gemv_mfma4(GemvMArgs ga) {
     float xs[TG][16];
     if (!X1) stage_x(XR[X1 ? 0 : R], xs);
     const float(&xf)[TG][16] = X1 ? x1 : xs;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      float w[FG][4];
+    // codebook values of pair group d (weights 4 d .. 4 d + 3) of each fragment
+    auto gather = [&](int d, float (&w)[FG][4]) {
 #pragma unroll
       for (int f = 0; f < FG; ++f) {
         if (PK12) {
@@ -304,13 +303,24 @@ __global__ __launch_bounds__(gm4::THREADS, 1) void gemv_mfma4(GemvMArgs ga) {
           w[f][3] = lds_load<float>(byte_addr256<3>(wd, lane4), cbs);
         }
       }
+    };
+    // the gathers of pair group d + 1 go out before the products of group d
+    // (scheduling barriers keep that order), so their latency hides behind
+    // the matrix ops
+    float wb[2][FG][4];
+    gather(0, wb[0]);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      if (d < 3) gather(d + 1, wb[(d + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int f = 0; f < FG; ++f)
 #pragma unroll
           for (int u = 0; u < TG; ++u)
-            acc[f][u] = __builtin_amdgcn_mfma_f32_4x4x1f32(w[f][e], xf[u][4 * d + e], acc[f][u], 0, 0, 0);
+            acc[f][u] = __builtin_amdgcn_mfma_f32_4x4x1f32(wb[d & 1][f][e], xf[u][4 * d + e], acc[f][u], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (q == nchw - 1) {  // uniform: the group's last chunk
 #pragma unroll
@@ -490,9 +500,14 @@ static hipError_t launch_gemv_mfma4_k(const GemvMArgs& g, int grid, hipStream_t 
 
 template <bool PK12, bool XBF, int TG>
 static hipError_t launch_gemv_mfma4_f(const GemvMArgs& g, int fmax, int grid, hipStream_t stream) {
-  if (fmax <= 1) return launch_gemv_mfma4_k<PK12, XBF, TG, 1>(g, grid, stream);
-  if (fmax <= 2) return launch_gemv_mfma4_k<PK12, XBF, TG, 2>(g, grid, stream);
-  if (fmax <= 3) return launch_gemv_mfma4_k<PK12, XBF, TG, 3>(g, grid, stream);
+  // the group size that pads the busiest workgroup's fragments least (the
+  // larger on ties)
+  int fg = 4;
+  for (int c = 3; c >= 1; --c)
+    if ((fmax + c - 1) / c * c < (fmax + fg - 1) / fg * fg) fg = c;
+  if (fg == 1) return launch_gemv_mfma4_k<PK12, XBF, TG, 1>(g, grid, stream);
+  if (fg == 2) return launch_gemv_mfma4_k<PK12, XBF, TG, 2>(g, grid, stream);
+  if (fg == 3) return launch_gemv_mfma4_k<PK12, XBF, TG, 3>(g, grid, stream);
   return launch_gemv_mfma4_k<PK12, XBF, TG, 4>(g, grid, stream);
 }
 
