@@ -659,7 +659,26 @@ def counters_by_kernel(path):
     return by
 
 
-def summarise_counters(path, match):
+def summarise_counters(path, match, cycle=None, cycles=0):
+    """Per kernel (and grid) mean counter values per dispatch; with `cycle`
+    (launch names) the first `cycles` rounds of matching dispatches are taken
+    as that repeating sequence of launches and summarised per launch."""
+    if cycle:
+        rows = _db(path).execute("select dispatch_id, kernel_name, counter_name, value from counters_collection "
+                                 "order by dispatch_id").fetchall()
+        disp = {}
+        for did, k, c, v in rows:
+            if match in k:
+                disp.setdefault(did, {})[c] = v
+        order = sorted(disp)[:len(cycle) * cycles]
+        out = []
+        for i, name in enumerate(cycle):
+            sel = [disp[did] for did in order[i::len(cycle)]]
+            out.append("%s (%d dispatches)" % (name, len(sel)))
+            for c in sorted(sel[0]) if sel else []:
+                vs = [d[c] for d in sel if c in d]
+                out.append("   %-28s %16.1f per dispatch" % (c, sum(vs) / len(vs)))
+        return "\n".join(out)
     out = []
     for k, cs in counters_by_kernel(path).items():
         if match not in k:
@@ -678,12 +697,11 @@ def summarise_traffic(d, steps=10, warmup=10):
     what the counters read for the plain device copy of --copy-calibration.
     Writes profiles/traffic.json and returns a text summary."""
     def series(sub, counter, match):
-        cs = counters_by_kernel(os.path.join(d, sub))
-        vals = []
-        for k, c in cs.items():
-            if match in k and counter in c:
-                vals += c[counter]
-        return vals
+        # values of the matching dispatches in dispatch order
+        rows = _db(os.path.join(d, sub)).execute(
+            "select dispatch_id, kernel_name, value from counters_collection where counter_name = ? "
+            "order by dispatch_id", (counter,)).fetchall()
+        return [v for _, k, v in rows if match in k]
     copy_kib = (64 << 20) * 4 / 1024
     cf = series("copyf", "FETCH_SIZE", "copyBuffer")
     cw = series("copyw", "WRITE_SIZE", "copyBuffer")
@@ -750,6 +768,9 @@ def main(argv=None):
     ap.add_argument("--summarise-counters", metavar="DB", help="print per-kernel counter means of a rocprofv3 "
                                                               "database (kernels whose name holds --match)")
     ap.add_argument("--match", default="hxq", help="kernel-name filter for --summarise-counters")
+    ap.add_argument("--launch-cycle", default="", help="with --summarise-counters: comma-separated names of the "
+                                                       "launches the matching dispatches repeat in turn")
+    ap.add_argument("--cycles", type=int, default=0, help="with --launch-cycle: rounds of launches to take")
     ap.add_argument("--summarise-traffic", metavar="DIR",
                     help="DIR/{fetch,write,copyf,copyw}: write profiles/traffic.json from those counter runs")
     args = ap.parse_args(argv)
@@ -757,7 +778,8 @@ def main(argv=None):
         print(summarise_trace(args.summarise_trace))
         return 0
     if args.summarise_counters:
-        print(summarise_counters(args.summarise_counters, args.match))
+        cyc = [c for c in args.launch_cycle.split(",") if c]
+        print(summarise_counters(args.summarise_counters, args.match, cyc, args.cycles))
         return 0
     if args.summarise_traffic:
         print(summarise_traffic(args.summarise_traffic))
