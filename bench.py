@@ -279,7 +279,8 @@ def stream_ceiling(torch, L, nbytes, steps):
     bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(i & 255) for i in range(copies)]
     stream = torch.cuda.current_stream().cuda_stream
     sweep = []
-    for words in (256, 512, 1024, 2048, 4096, 8192):
+    for wgs in (256, 512, 1024, 2048, 4096, 8192):
+        words = 8 * wgs  # a word per wave
         sink = torch.zeros(words, dtype=torch.int32, device="cuda")
 
         def reader(b, sink=sink, words=words):
@@ -292,7 +293,7 @@ def stream_ceiling(torch, L, nbytes, steps):
         calls = [[reader(b)] for b in bufs]
         n = max(steps, len(bufs))
         avg = time_steps(torch, calls, n, 2) / n
-        sweep.append(dict(workgroups=words, avg_us=round(avg * 1e3, 3), gbs=round(nb / (avg * 1e-3) / 1e9, 1)))
+        sweep.append(dict(workgroups=wgs, avg_us=round(avg * 1e3, 3), gbs=round(nb / (avg * 1e-3) / 1e9, 1)))
     best = max(sweep, key=lambda r: r["gbs"])
     del bufs
     torch.cuda.empty_cache()

@@ -157,14 +157,17 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count,
                            hipStream_t stream);
 
 /* Measurement helper, not part of the forward pass: reads `bytes` bytes of
- * device memory at `src` once with `sink_words` 512-thread workgroups (fewer
- * when the buffer needs fewer, at most 65535; 16-byte loads, the whole grid
- * sweeping the buffer in order, four loads in flight per thread), and writes a
- * 32-bit digest of what it read per workgroup into `sink` (device memory,
- * `sink_words` entries).  Timed over a sweep of grid sizes it gives the
- * attainable read bandwidth that the decode kernels' HBM fraction is compared
- * against.
- * Errors: HXQ_ERR_SHAPE if bytes < 0 or not a multiple of 16 or sink_words < 1,
+ * device memory at `src` once with sink_words / 8 workgroups of 512 threads
+ * (fewer when the buffer needs fewer, at most 65535; 16-byte loads, the whole
+ * grid sweeping the buffer in order, four loads in flight per thread and the
+ * next four requested before they are used), and each wave stores a 32-bit
+ * digest of what it read into `sink` (device memory, `sink_words` entries;
+ * word 8 g + w for wave w of workgroup g; the words of workgroups not
+ * launched are left as they were, so with a zeroed sink the XOR of all words
+ * is the XOR of all 32-bit words read).  Timed over a sweep of grid sizes it
+ * gives the attainable read bandwidth that the decode kernels' HBM fraction
+ * is compared against.
+ * Errors: HXQ_ERR_SHAPE if bytes < 0 or not a multiple of 16 or sink_words < 8,
  * HXQ_ERR_NULL for a NULL pointer with bytes > 0, HXQ_ERR_ALIGN if src is not
  * 16-byte aligned or sink not 4-byte aligned. */
 int hxq_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words,

@@ -181,14 +181,15 @@ def test_grouped_rejects_call_arguments(L):
 
 def test_stream_read_rejects(L):
     f = L.hxq_stream_read
-    assert f(FAKE, 15, FAKE, 4, None) == B.HXQ_ERR_SHAPE
-    assert f(FAKE, -16, FAKE, 4, None) == B.HXQ_ERR_SHAPE
+    assert f(FAKE, 15, FAKE, 8, None) == B.HXQ_ERR_SHAPE
+    assert f(FAKE, -16, FAKE, 8, None) == B.HXQ_ERR_SHAPE
     assert f(FAKE, 16, FAKE, 0, None) == B.HXQ_ERR_SHAPE
-    assert f(None, 16, FAKE, 4, None) == B.HXQ_ERR_NULL
-    assert f(FAKE, 16, None, 4, None) == B.HXQ_ERR_NULL
-    assert f(FAKE + 4, 16, FAKE, 4, None) == B.HXQ_ERR_ALIGN
-    assert f(FAKE, 16, FAKE + 2, 4, None) == B.HXQ_ERR_ALIGN
-    assert f(None, 0, None, 4, None) == B.HXQ_OK
+    assert f(FAKE, 16, FAKE, 7, None) == B.HXQ_ERR_SHAPE  # a word per wave of at least one workgroup
+    assert f(None, 16, FAKE, 8, None) == B.HXQ_ERR_NULL
+    assert f(FAKE, 16, None, 8, None) == B.HXQ_ERR_NULL
+    assert f(FAKE + 4, 16, FAKE, 8, None) == B.HXQ_ERR_ALIGN
+    assert f(FAKE, 16, FAKE + 2, 8, None) == B.HXQ_ERR_ALIGN
+    assert f(None, 0, None, 8, None) == B.HXQ_OK
 
 
 def test_dequant_rejects(L):

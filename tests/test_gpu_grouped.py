@@ -170,10 +170,11 @@ def test_grouped_is_deterministic():
 
 
 @pytest.mark.parametrize("nbytes", [16, 1024 * 1024 + 48, 23 * 1000 * 1000 // 16 * 16])
-@pytest.mark.parametrize("words", [256, 1024, 4096])
+@pytest.mark.parametrize("words", [8, 256, 1024, 4096 * 8])
 def test_stream_read_digest(nbytes, words):
-    # the measurement helper reads every byte once whatever its grid: XOR of
-    # the digests is the XOR of all 32-bit words
+    # the measurement helper reads every byte once whatever its grid (a word
+    # per wave, words / 8 workgroups): XOR of the digests is the XOR of all
+    # 32-bit words
     t = G.torch()
     rng = np.random.Generator(np.random.PCG64(nbytes))
     host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
@@ -184,3 +185,24 @@ def test_stream_read_digest(nbytes, words):
     assert st == 0
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(host)
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M", [5, 8])
+@pytest.mark.parametrize("Ns,K,nnz_den", [((20000,), 2048, 1000), ((11008, 11008), 1280, 1000),
+                                          ((16392, 40), 2048, 100)])
+def test_large_layers_m5_to_8(x_dtype, M, Ns, K, nnz_den):
+    # 5-8 tokens on layers of gate|up size (tens of 4-row fragments per
+    # workgroup, groups of two): a ragged last fragment, a K that gives the
+    # waves different chunk counts, a tiny layer beside a large one, and a
+    # sidecar dense enough for several epilogue passes
+    G.say("large layers %s M=%d Ns=%s K=%d" % (x_dtype, M, Ns, K))
+    lays, ds = _group("u8", list(Ns), K, seed=M * 7 + K, nnz_den=nnz_den)
+    x_np = _x(M + K, M, K, x_dtype)
+    xd = G.dev_x(x_np, x_dtype)
+    ys = _grouped("u8", lays, ds, xd)
+    for lay, y in zip(lays, ys):
+        Y, B = G.oracle_fwd(lay, x_np, x_dtype)
+        G.check(y, Y, B, G.TOL_FP32, "large layer N=%d" % lay.N)
+    if len(lays) == 1:
+        assert G.torch().equal(ys[0], G.run(lays[0], ds[0], xd)), "grouped and single-layer results differ bitwise"

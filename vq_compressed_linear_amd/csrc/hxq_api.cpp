@@ -440,7 +440,7 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
 }
 
 int hxq_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream) {
-  if (bytes < 0 || bytes % 16 != 0 || sink_words < 1) return HXQ_ERR_SHAPE;
+  if (bytes < 0 || bytes % 16 != 0 || sink_words < 8) return HXQ_ERR_SHAPE;
   if (bytes == 0) return HXQ_OK;
   if (!src || !sink) return HXQ_ERR_NULL;
   if (misaligned(src, 16) || misaligned(sink, 4)) return HXQ_ERR_ALIGN;

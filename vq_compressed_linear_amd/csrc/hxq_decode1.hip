@@ -157,6 +157,7 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
     for (int k = K + 4 * tid; k < 1024 * CH; k += 4 * THREADS)
       *reinterpret_cast<float4*>(xs + xoff(k)) = make_float4(0.f, 0.f, 0.f, 0.f);
   asm volatile("" ::: "memory");  // the lookup (and its wait) stays below the loads
+  if (tid < RMAX) rsb[tid] = rse[tid] = 0;  // the first sidecar pass's row ranges
   if (srch) {
     const int64_t v = row_window_lower_bound(a.sc_rows, a.nnz, target, win);
     if (lane == 0) lohi[wave] = v;
@@ -238,24 +239,32 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
   }
   if (j < nj) row(std::integral_constant<int, 0>{}, j);
   if (j + 1 < nj) row(std::integral_constant<int, 1>{}, j + 1);
+  // the first sidecar pass's terms (x from LDS; the triplets arrived during
+  // the rows), before the barrier, so the epilogue only adds them
+  const int cnt0 = (int)min<int64_t>(SCAP, hi - lo);
+  if (lo < hi && tid < cnt0) {
+    tv[tid] = tdl * xs[xoff(tc)];
+    if (tid == 0 || trp != tr) rsb[tr - r0] = tid;
+    if (tid == cnt0 - 1 || trn != tr) rse[tr - r0] = tid + 1;
+  }
   __syncthreads();
 
   // ---- epilogue: thread r -> row r0 + r
   float out = tid < nrow ? part[tid] : 0.f;
-  for (int64_t e0 = lo; e0 < hi; e0 += SCAP) {
+  if (tid < nrow)
+    for (int e = rsb[tid]; e < rse[tid]; ++e) out += tv[e];
+  for (int64_t e0 = lo + SCAP; e0 < hi; e0 += SCAP) {  // more triplets than one pass takes
     const int cnt = (int)min<int64_t>(SCAP, hi - e0);
     __syncthreads();
     if (tid < RMAX) rsb[tid] = rse[tid] = 0;
     __syncthreads();
     if (tid < SCAP) {
-      if (e0 != lo) {
-        const int64_t ee = e0 + min(tid, cnt - 1);
-        tc = a.sc_cols[ee];
-        tdl = a.sc_deltas[ee];
-        tr = a.sc_rows[ee];
-        trp = a.sc_rows[ee > 0 ? ee - 1 : 0];
-        trn = a.sc_rows[ee + 1 < a.nnz ? ee + 1 : ee];
-      }
+      const int64_t ee = e0 + min(tid, cnt - 1);
+      tc = a.sc_cols[ee];
+      tdl = a.sc_deltas[ee];
+      tr = a.sc_rows[ee];
+      trp = a.sc_rows[ee > 0 ? ee - 1 : 0];
+      trn = a.sc_rows[ee + 1 < a.nnz ? ee + 1 : ee];
       if (tid < cnt) {
         tv[tid] = tdl * xs[xoff(tc)];
         if (tid == 0 || trp != tr) rsb[tr - r0] = tid;

@@ -619,22 +619,16 @@ __global__ __launch_bounds__(512) void stream_read_kernel(const u32x4* __restric
     __builtin_amdgcn_sched_barrier(0);
     fold(vb, kb);
   }
-  // fold across the wave and the block; one word per block
+  // fold across the wave; each wave stores its own word (no barrier and no
+  // atomics, so the waves retire independently, as in a plain read)
   for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, kWave);
-  __shared__ uint32_t red[8];
-  if (lane == 0) red[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t t = 0;
-    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t ^= red[i];
-    sink[blockIdx.x] = t;
-  }
+  if (lane == 0) sink[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = acc;
 }
 
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream) {
-  // one workgroup per sink word (the caller picks the grid), no more than the
-  // buffer's pieces need
-  int64_t grid = sink_words;
+  // one workgroup per 8 sink words (a word per wave; the caller picks the
+  // grid), no more than the buffer's pieces need
+  int64_t grid = sink_words / 8;
   const int64_t need = (bytes / 16 + 511) / 512;
   if (grid > need) grid = need;
   if (grid > 65535) grid = 65535;
