@@ -46,8 +46,10 @@ __device__ __forceinline__ int xoff(int k) {
 }
 
 // CH: chunks of 16 weights per lane and row (K <= 1024 CH); XL: x read from
-// LDS per chunk (else held in registers, K == 1024 CH)
-template <bool PK12, bool XBF, int CH, bool XL>
+// LDS per chunk (else held in registers, K == 1024 CH); ONE: no wave has more
+// than one row (the launch plan's rows per workgroup <= 8), so a wave requests
+// its row alone instead of a ring of three
+template <bool PK12, bool XBF, int CH, bool XL, bool ONE>
 __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
   using namespace dc1;
   __shared__ __align__(16) unsigned char cbs[PK12 ? 4096 * 8 : 256 * 256];
@@ -125,10 +127,12 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
       }
     }
   };
-  u32x4 IQ[3][CH];
+  u32x4 IQ[ONE ? 1 : 3][CH];
   load_row(0, IQ[0]);
-  load_row(1, IQ[1]);
-  load_row(2, IQ[2]);
+  if constexpr (!ONE) {
+    load_row(1, IQ[1]);
+    load_row(2, IQ[2]);
+  }
   if (PK12) {
 #pragma unroll
     for (int i = 0; i < CBV; ++i) reinterpret_cast<u32x4*>(cbs)[tid + i * THREADS] = cbv[i];
@@ -229,16 +233,20 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
     }
     const float t = wave_sum_dpp((s[0] + s[1]) + (s[2] + s[3]));
     if (lane == 0) part[wave + WAVES * j] = t;
-    load_row(j + 3, IQ[R]);
+    if constexpr (!ONE) load_row(j + 3, IQ[R]);
   };
-  int j = 0;
-  for (; j + 2 < nj; j += 3) {
-    row(std::integral_constant<int, 0>{}, j);
-    row(std::integral_constant<int, 1>{}, j + 1);
-    row(std::integral_constant<int, 2>{}, j + 2);
+  if constexpr (ONE) {
+    if (nj > 0) row(std::integral_constant<int, 0>{}, 0);
+  } else {
+    int j = 0;
+    for (; j + 2 < nj; j += 3) {
+      row(std::integral_constant<int, 0>{}, j);
+      row(std::integral_constant<int, 1>{}, j + 1);
+      row(std::integral_constant<int, 2>{}, j + 2);
+    }
+    if (j < nj) row(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < nj) row(std::integral_constant<int, 1>{}, j + 1);
   }
-  if (j < nj) row(std::integral_constant<int, 0>{}, j);
-  if (j + 1 < nj) row(std::integral_constant<int, 1>{}, j + 1);
   // the first sidecar pass's terms (x from LDS; the triplets arrived during
   // the rows), before the barrier, so the epilogue only adds them
   const int cnt0 = (int)min<int64_t>(SCAP, hi - lo);
@@ -322,36 +330,42 @@ static bool decode1_plan(GemvMArgs& g, int& grid) {
   return true;
 }
 
-template <bool PK12, bool XBF, int CH, bool XL>
-static hipError_t launch_decode1_x(const GemvMArgs& g, int grid, hipStream_t stream) {
+template <bool PK12, bool XBF, int CH, bool XL, bool ONE>
+static hipError_t launch_decode1_o(const GemvMArgs& g, int grid, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&decode1_gemv<PK12, XBF, CH, XL>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      dc1::LDS_DYN);
+      reinterpret_cast<const void*>(&decode1_gemv<PK12, XBF, CH, XL, ONE>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, dc1::LDS_DYN);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((decode1_gemv<PK12, XBF, CH, XL>), dim3((unsigned)grid), dim3(dc1::THREADS), dc1::LDS_DYN,
-                     stream, g);
+  hipLaunchKernelGGL((decode1_gemv<PK12, XBF, CH, XL, ONE>), dim3((unsigned)grid), dim3(dc1::THREADS),
+                     dc1::LDS_DYN, stream, g);
   return hipGetLastError();
+}
+
+template <bool PK12, bool XBF, int CH, bool XL>
+static hipError_t launch_decode1_x(const GemvMArgs& g, int grid, bool one, hipStream_t stream) {
+  return one ? launch_decode1_o<PK12, XBF, CH, XL, true>(g, grid, stream)
+             : launch_decode1_o<PK12, XBF, CH, XL, false>(g, grid, stream);
 }
 
 // K a multiple of 1024 up to 4096: x in registers; otherwise x from LDS with
 // the smallest instantiated chunk count that covers K
 template <bool PK12, bool XBF>
-static hipError_t launch_decode1_k(const GemvMArgs& g, int grid, hipStream_t stream) {
+static hipError_t launch_decode1_k(const GemvMArgs& g, int grid, bool one, hipStream_t stream) {
   if (g.K % 1024 == 0 && g.K <= 4096) {
     switch (g.K / 1024) {
-      case 1: return launch_decode1_x<PK12, XBF, 1, false>(g, grid, stream);
-      case 2: return launch_decode1_x<PK12, XBF, 2, false>(g, grid, stream);
-      case 3: return launch_decode1_x<PK12, XBF, 3, false>(g, grid, stream);
-      default: return launch_decode1_x<PK12, XBF, 4, false>(g, grid, stream);
+      case 1: return launch_decode1_x<PK12, XBF, 1, false>(g, grid, one, stream);
+      case 2: return launch_decode1_x<PK12, XBF, 2, false>(g, grid, one, stream);
+      case 3: return launch_decode1_x<PK12, XBF, 3, false>(g, grid, one, stream);
+      default: return launch_decode1_x<PK12, XBF, 4, false>(g, grid, one, stream);
     }
   }
   const int ch = (g.K + 1023) / 1024;
-  if (ch <= 2) return launch_decode1_x<PK12, XBF, 2, true>(g, grid, stream);
-  if (ch <= 4) return launch_decode1_x<PK12, XBF, 4, true>(g, grid, stream);
-  if (ch <= 6) return launch_decode1_x<PK12, XBF, 6, true>(g, grid, stream);
-  if (ch <= 8) return launch_decode1_x<PK12, XBF, 8, true>(g, grid, stream);
-  if (ch <= 11) return launch_decode1_x<PK12, XBF, 11, true>(g, grid, stream);
-  return launch_decode1_x<PK12, XBF, 12, true>(g, grid, stream);
+  if (ch <= 2) return launch_decode1_x<PK12, XBF, 2, true>(g, grid, one, stream);
+  if (ch <= 4) return launch_decode1_x<PK12, XBF, 4, true>(g, grid, one, stream);
+  if (ch <= 6) return launch_decode1_x<PK12, XBF, 6, true>(g, grid, one, stream);
+  if (ch <= 8) return launch_decode1_x<PK12, XBF, 8, true>(g, grid, one, stream);
+  if (ch <= 11) return launch_decode1_x<PK12, XBF, 11, true>(g, grid, one, stream);
+  return launch_decode1_x<PK12, XBF, 12, true>(g, grid, one, stream);
 }
 
 bool launch_decode1(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
@@ -369,10 +383,19 @@ bool launch_decode1(const DecodeSeg* segs, int nseg, bool pk12, const void* x, b
                 segs[i].sc_deltas, segs[i].nnz, segs[i].bias, segs[i].y, segs[i].N, segs[i].N};
   int grid = 0;
   if (!decode1_plan(g, grid)) return false;
+  // the most rows any workgroup owns: at most one per wave takes the ring-less instance
+  int most = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const int wgs = (i + 1 < nseg ? g.wg0[i + 1] : grid) - g.wg0[i];
+    const int r = (g.seg[i].N + wgs - 1) / wgs;
+    if (r > most) most = r;
+  }
+  const bool one = most <= dc1::WAVES;
   if (pk12)
-    err = xbf ? launch_decode1_k<true, true>(g, grid, stream) : launch_decode1_k<true, false>(g, grid, stream);
+    err = xbf ? launch_decode1_k<true, true>(g, grid, one, stream) : launch_decode1_k<true, false>(g, grid, one, stream);
   else
-    err = xbf ? launch_decode1_k<false, true>(g, grid, stream) : launch_decode1_k<false, false>(g, grid, stream);
+    err = xbf ? launch_decode1_k<false, true>(g, grid, one, stream)
+              : launch_decode1_k<false, false>(g, grid, one, stream);
   return true;
 }
 
