@@ -159,9 +159,10 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_grouped(const GemmSeg* segs, int nseg, bool pk12, const void* x, int M, int K,
                                hipStream_t stream);
-// The 256-token x 256-output tile GEMM with x and index bytes copied into LDS
-// rings by DMA (u8 or pk12, bf16 x, K % 32 == 0, x 16-byte and index rows
-// 16-byte (u8) / 4-byte (pk12) aligned); several layers sharing x in one launch.
+// The 256-token x 256-output tile GEMM, four waves of 128 x 128 with the
+// weight tile built in LDS two stages ahead (u8 or pk12, bf16 x, K % 32 == 0,
+// x 16-byte and index rows 16-byte (u8) / 4-byte (pk12) aligned); several
+// layers sharing x in one launch.
 bool gemm5_path_ok(const LayerArgs& a, bool pk12);
 int64_t gemm5_tiles(const GemmSeg* segs, int nseg, int M);
 hipError_t launch_gemm5_grouped(const GemmSeg* segs, int nseg, bool pk12, const void* x, int M, int K,
