@@ -65,6 +65,7 @@ CASES = [
     # (N, K, M): full-width decode shapes, tails, byte path, token tails, one split
     (11008, 2048, 1),
     (2048, 11008, 1),
+    (256, 2048, 1),
     (2048, 2048, 2),
     (300, 1024, 4),
     (257, 520, 3),
@@ -276,3 +277,30 @@ def test_bwd_x_vector_kernel_long_runs(fmt, dtype):
     dx = _run(lay, d, G.dev_x(dy_np, dtype), variant=hx.HXQ_VARIANT_GEMV_VALU)
     Y, B = _oracle(lay, dy_np, dtype)
     G.check(dx, Y, B, G.TOL_FP32, "bwd_x vector long runs %s %s" % (fmt, dtype))
+
+
+def test_bwd_x_split_sum_repeats():
+    # row-split shapes at one token, called in turn several times on one
+    # stream: within tolerance of the oracle every time, and without a
+    # sidecar (whose terms within a tile are added in no fixed order) the
+    # same bits every time (the row splits are summed in a fixed order)
+    t = G.torch()
+    shapes = [(2048, 2048), (11008, 2048), (2048, 11008), (257, 520)]
+    runs = []
+    for i, (N, K) in enumerate(shapes):
+        lay = gen.random_layer(700 + i, N, K, "u8", nnz=N * K // 1000, duplicates=True)
+        dy_np = _dy(800 + i, 1, N, "f32")
+        Y, B = _oracle(lay, dy_np, "f32")
+        Y0, B0 = _oracle(lay, dy_np, "f32", sidecar=False)
+        runs.append((lay, G.dev_layer(lay), G.dev_x(dy_np, "f32"), Y, B, Y0, B0))
+    first = []
+    for rep in range(3):
+        for i, (lay, d, dyd, Y, B, Y0, B0) in enumerate(runs):
+            G.say("bwd_x split sum repeat %d shape %d" % (rep, i))
+            G.check(_run(lay, d, dyd), Y, B, G.TOL_FP32, "bwd_x split sum shape %d repeat %d" % (i, rep))
+            dx0 = _run(lay, d, dyd, sidecar=False).cpu().numpy()
+            G.check(t.from_numpy(dx0), Y0, B0, G.TOL_FP32, "bwd_x split sum, no sidecar, shape %d" % i)
+            if rep == 0:
+                first.append(dx0)
+            else:
+                assert np.array_equal(dx0, first[i]), "repeat %d of shape %d differs" % (rep, i)

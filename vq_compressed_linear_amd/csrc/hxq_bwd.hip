@@ -346,40 +346,53 @@ __global__ __launch_bounds__(bx::THREADS) void bwdx_valu(BwdArgs ba) {
 }
 
 // dx[i] = sum over the splits of ws[s][i], added in split order.  VEC: four
-// consecutive elements per thread (16-byte loads and stores).
+// consecutive elements per thread (16-byte loads and stores), for large n;
+// otherwise one element per thread, so a small reduction (one token: a few
+// thousand elements) still spreads over several workgroups.
 template <bool VEC>
 __global__ __launch_bounds__(256) void bwdx_reduce(const float* __restrict__ ws, float* __restrict__ dx, int64_t n,
                                                    int S) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (VEC ? 4 : 1);
   if (i >= n) return;
-  // loads go out sixteen splits at a time (a plain loop would wait for each
-  // before issuing the next); the adds stay in split order
+  // loads go out 16 (four elements) or 32 (one element) splits at a time (a
+  // plain loop would wait for each before issuing the next); the adds stay
+  // in split order
+  constexpr int B = VEC ? 16 : 32;
   if (VEC) {
     float4 v = *reinterpret_cast<const float4*>(ws + i);
     int s = 1;
-    for (; s + 16 <= S; s += 16) {
-      float4 t[16];
+    for (; s + B <= S; s += B) {
+      float4 t[B];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) t[u] = *reinterpret_cast<const float4*>(ws + (int64_t)(s + u) * n + i);
+      for (int u = 0; u < B; ++u) t[u] = *reinterpret_cast<const float4*>(ws + (int64_t)(s + u) * n + i);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v = make_float4(v.x + t[u].x, v.y + t[u].y, v.z + t[u].z, v.w + t[u].w);
+      for (int u = 0; u < B; ++u) v = make_float4(v.x + t[u].x, v.y + t[u].y, v.z + t[u].z, v.w + t[u].w);
     }
-    for (; s < S; ++s) {
-      const float4 t = *reinterpret_cast<const float4*>(ws + (int64_t)s * n + i);
-      v = make_float4(v.x + t.x, v.y + t.y, v.z + t.z, v.w + t.w);
-    }
+    // the rest: loads clamped to the last split (unconditional, so they all
+    // go out together), adds only for the splits that exist
+    float4 t[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) t[u] = *reinterpret_cast<const float4*>(ws + (int64_t)min(s + u, S - 1) * n + i);
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (s + u < S) v = make_float4(v.x + t[u].x, v.y + t[u].y, v.z + t[u].z, v.w + t[u].w);
     *reinterpret_cast<float4*>(dx + i) = v;
   } else {
     float v = ws[i];
     int s = 1;
-    for (; s + 16 <= S; s += 16) {
-      float t[16];
+    for (; s + B <= S; s += B) {
+      float t[B];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) t[u] = ws[(int64_t)(s + u) * n + i];
+      for (int u = 0; u < B; ++u) t[u] = ws[(int64_t)(s + u) * n + i];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v += t[u];
+      for (int u = 0; u < B; ++u) v += t[u];
     }
-    for (; s < S; ++s) v += ws[(int64_t)s * n + i];
+    float t[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) t[u] = ws[(int64_t)min(s + u, S - 1) * n + i];
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (s + u < S) v += t[u];
     dx[i] = v;
   }
 }
@@ -433,7 +446,12 @@ BwdPlan bwdx_plan(int M, int N, int K) {
   const int64_t tiles = (int64_t)p.ct * p.mtiles;
   const int64_t target = 2 * (int64_t)device_cu_count();
   int64_t S = (target + tiles - 1) / tiles;
-  const int64_t smax = (N + 63) / 64;
+  int64_t smax = (N + 63) / 64;
+  // rows a workgroup takes per group of loads; a layer of at most two such
+  // groups is not split (one more round of loads costs less than the
+  // reduction launch)
+  const int group_rows = bx::WAVES * (64 / p.lpr) * (p.mt >= 8 ? 4 : 8);
+  if (N <= 2 * group_rows) smax = 1;
   if (S > smax) S = smax;
   if (S > 64) S = 64;  // the reduction kernel sums at most 64 splits
   if (S < 1) S = 1;
@@ -479,7 +497,9 @@ hipError_t launch_bwdx_valu(const BwdArgs& a0, bool pk12, hipStream_t stream) {
 }
 
 hipError_t launch_bwdx_reduce(const float* ws, float* dx, int64_t n, int S, hipStream_t stream) {
-  const bool vec = n % 4 == 0 && reinterpret_cast<uintptr_t>(dx) % 16 == 0 && reinterpret_cast<uintptr_t>(ws) % 16 == 0;
+  // four elements per thread only when that still gives a workgroup per CU
+  const bool vec = n % 4 == 0 && reinterpret_cast<uintptr_t>(dx) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(ws) % 16 == 0 && n / 1024 >= device_cu_count();
   const int64_t rb = (n + (vec ? 1023 : 255)) / (vec ? 1024 : 256);
   if (rb > INT_MAX || S > 64) return hipErrorInvalidConfiguration;
   if (vec)
