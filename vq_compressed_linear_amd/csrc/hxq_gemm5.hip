@@ -150,16 +150,20 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
       }
     }
   };
-  // first requests: x and index bytes of stages 0-3
+  // first requests: the sidecar search (a chain of dependent loads heads the
+  // set-up), then x and index bytes of stages 0 and 1; stages 2 and 3 after
+  // the set-up, so the chain does not queue behind them
+  if (sg.nnz > 0 && wave < 2) {
+    const int target = wave == 0 ? n0 : min(n0 + BN, N);
+    const int64_t guess = (int64_t)((double)sg.nnz * (double)target / (double)N);
+    const int64_t v = wave_lower_bound_rows_near(sg.sc_rows, sg.nnz, target, guess);
+    if (lane == 0) lohi[wave] = v;
+  }
   u32x4 xp0[4], xp1[4], xs0[4], xs1[4], ip0[2], ip1[2], iq0[2], iq1[2];
   load_i(0, ip0);
   load_x(0, xp0);
   load_i(1, ip1);
   load_x(1, xp1);
-  load_i(2, iq0);
-  load_x(2, xs0);
-  load_i(3, iq1);
-  load_x(3, xs1);
 
   // ---- codebook.  u8: 32 copies per entry, lane l reads copy l % 32; pk12:
   // each component rounded to nearest even on its own
@@ -186,12 +190,6 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
   int* cnt32 = reinterpret_cast<int*>(xbuf + 2 * XS);  // third x stage, first written in the loop
   if (!long_k)
     for (int i = tid; i <= nbins; i += THREADS) cnt32[i] = 0;
-  if (sg.nnz > 0 && wave < 2) {
-    const int target = wave == 0 ? n0 : min(n0 + BN, N);
-    const int64_t guess = (int64_t)((double)sg.nnz * (double)target / (double)N);
-    const int64_t v = wave_lower_bound_rows_near(sg.sc_rows, sg.nnz, target, guess);
-    if (lane == 0) lohi[wave] = v;
-  }
   __syncthreads();
   int64_t lo = 0, hi = 0;
   if (sg.nnz > 0) {
@@ -353,6 +351,10 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
     }
   };
 
+  load_i(2, iq0);
+  load_x(2, xs0);
+  load_i(3, iq1);
+  load_x(3, xs1);
   // W(0), W(1), x(0), x(1) into LDS.  Tiles on the walk path (more
   // triplets than patches, or K past the bins) build plain codebook weights
   // here and add their sidecar terms in the epilogue.
