@@ -765,6 +765,9 @@ def main(argv=None):
     ap.add_argument("--profile-prefill", type=int, default=0, metavar="M",
                     help="only run --steps grouped prefill steps at M tokens (bf16 x) and print their "
                          "per-launch times (for profiler runs)")
+    ap.add_argument("--profile-bwd", type=int, default=0, metavar="M",
+                    help="only run --steps input-gradient steps at M tokens (fp32 dy below 16 tokens, bf16 "
+                         "from 16) and print their per-layer times (for profiler runs)")
     ap.add_argument("--summarise-trace", metavar="DB", help="print a kernel-trace summary of a rocprofv3 database")
     ap.add_argument("--summarise-counters", metavar="DB", help="print per-kernel counter means of a rocprofv3 "
                                                               "database (kernels whose name holds --match)")
@@ -842,6 +845,13 @@ def main(argv=None):
             per.append(dict(launch="|".join(GROUPS[g]), avg_us=round(tg / args.steps * 1e3, 3)))
         print(json.dumps(dict(profile_decode_m=args.profile_decode, steps=args.steps,
                               step_us=round(total / args.steps * 1e3, 3), launches=per)))
+        return 0
+
+    if args.profile_bwd > 0:
+        sp = LayerSet(torch, L, B, layers, 1, "f32", 1, copies, stream)
+        out = input_gradient(torch, L, B, layers, sp.devs, args.profile_bwd,
+                             "f32" if args.profile_bwd < 16 else "bf16", args.steps, args.warmup, stream)
+        print(json.dumps(dict(profile_bwd_m=args.profile_bwd, steps=args.steps, **out)))
         return 0
 
     # ---- headline: M = 1, grouped launches
