@@ -44,8 +44,12 @@
  *     rounded once to bf16 (nearest, ties to even): the sidecar correction is
  *     folded into the operand, so an outlier's corrected weight carries one
  *     bf16 rounding like every other weight (relative 2^-9), instead of
- *     entering as an exact fp32 delta * x term.  The tolerance of that path,
- *     8e-3 of |X| |W|^T, covers it.
+ *     entering as an exact fp32 delta * x term.  (A 256 x 256 output tile
+ *     of the 256-token kernel with more than 4096 sidecar entries, or with
+ *     K > 12288, instead uses the plain codebook operand and adds
+ *     x * (bf16(C + deltas) - bf16(C)) per distinct (n, k) in fp32 after the
+ *     matrix ops: the same products, summed in another order.)  The
+ *     tolerance of that path, 8e-3 of |X| |W|^T, covers it.
  *   - Errors are returned as a negative hxq_status before anything is
  *     launched; HXQ_ERR_HIP reports a failed launch.
  */
