@@ -37,9 +37,10 @@
  *   - Arithmetic: fp32 activations are multiplied in fp32 with fp32
  *     accumulation (vector FMAs up to 4 tokens, fp32 matrix-core products
  *     beyond, which are exact fp32 products summed in fp32); bf16 activations
- *     are upcast exactly and take the same fp32 path, except with M > 16
- *     (and K % 32 == 0 for pk12), which runs on bf16 matrix cores with fp32
- *     accumulation.  There the weight operand at (n, k) is the codebook value
+ *     are upcast exactly and take the same fp32 path, except with M > 64, or
+ *     17 <= M <= 64 on a layer with N > 3968 (at least 32 output tiles of
+ *     128 x 128), which runs on bf16 matrix cores with fp32 accumulation
+ *     (K % 32 == 0 for both formats).  There the weight operand at (n, k) is the codebook value
  *     plus every sidecar delta at (n, k), summed in fp32 in stored order and
  *     rounded once to bf16 (nearest, ties to even): the sidecar correction is
  *     folded into the operand, so an outlier's corrected weight carries one
@@ -101,9 +102,9 @@ int hxq_linear_fwd_u8(const float* codebook, const uint8_t* indices,
  *             (HXQ whitepaper, "Method", 12-bit index packing; the byte order is this
  *             library's choice).
  *   K must be even.  All other arguments as for hxq_linear_fwd_u8.  bf16 x is
- *   accepted at every M: up to 16 tokens, or when K % 32 != 0, it takes the
- *   fp32 path; past 16 tokens with K % 32 == 0 it runs on the bf16 matrix
- *   cores like the u8 format (weights rounded to bf16 as described above). */
+ *   accepted at every M and takes the fp32 path or the bf16 matrix cores by
+ *   the same rule as the u8 format (weights rounded to bf16 as described
+ *   above); K % 32 != 0 always takes the fp32 path. */
 int hxq_linear_fwd_pk12(const float* codebook2, const uint8_t* packed,
                         const int32_t* sc_rows, const int32_t* sc_cols,
                         const float* sc_deltas, int64_t nnz,

@@ -105,6 +105,13 @@ def test_variant_selection(L):
     assert sel(0, B.HXQ_BF16, 2048, 11008, 2048) == B.HXQ_VARIANT_GEMM_BF16
     assert sel(0, B.HXQ_BF16, 16, 11008, 2048) != B.HXQ_VARIANT_GEMM_BF16
     assert sel(0, B.HXQ_F32, 64, 8512, 2048) != B.HXQ_VARIANT_GEMM_BF16
+    # from 17 to 64 tokens only layers with at least 32 output tiles of 128 x 128 (N > 3968)
+    assert sel(0, B.HXQ_BF16, 64, 8512, 2048) == B.HXQ_VARIANT_GEMM_BF16
+    assert sel(0, B.HXQ_BF16, 17, 3969, 2048) == B.HXQ_VARIANT_GEMM_BF16
+    assert sel(0, B.HXQ_BF16, 64, 3968, 4096) == B.HXQ_VARIANT_GEMV_VALU
+    assert sel(0, B.HXQ_BF16, 17, 2048, 4096) == B.HXQ_VARIANT_GEMV_VALU
+    assert sel(1, B.HXQ_BF16, 64, 2048, 4096) == B.HXQ_VARIANT_GEMV_VALU
+    assert sel(0, B.HXQ_BF16, 65, 2048, 4096) == B.HXQ_VARIANT_GEMM_BF16
     assert sel(1, B.HXQ_BF16, 2048, 11008, 2048) == B.HXQ_VARIANT_GEMM_BF16
     assert sel(1, B.HXQ_BF16, 2048, 11008, 96) == B.HXQ_VARIANT_GEMM_BF16
     assert sel(1, B.HXQ_BF16, 2048, 11008, 80) != B.HXQ_VARIANT_GEMM_BF16

@@ -85,10 +85,11 @@ def test_grouped_token_groups_match_single_calls(fmt, M):
                                       ("u8", 2000, 256), ("pk12", 2000, 256)])
 def test_grouped_prefill_gemm(fmt, M, K):
     # bf16 x past the decode sizes: one matrix-core launch over all layers
-    # (K % 32 == 0), else one call per layer; both equal single-layer calls
-    # bitwise.  At 2000 tokens the grouped launch takes 256-output tiles while
-    # the 1000-output layer alone takes 128-output ones: the tile width does
-    # not change any output's summation order.
+    # (K % 32 == 0), else one call per layer (at 17 tokens these layers are
+    # too narrow for the GEMM and take the fp32 matrix-core GEMV); all equal
+    # single-layer calls bitwise.  At 2000 tokens the grouped launch takes
+    # 256-output tiles while the 1000-output layer alone takes 128-output
+    # ones: the tile width does not change any output's summation order.
     G.say("grouped gemm %s M=%d K=%d" % (fmt, M, K))
     lays, ds = _group(fmt, [1000, 96, 2500], K, seed=M + K)
     x_np = _x(M + 1, M, K, "bf16")
@@ -99,6 +100,29 @@ def test_grouped_prefill_gemm(fmt, M, K):
         tol = G.TOL_BF16 if K % 32 == 0 or fmt == "u8" else G.TOL_FP32
         G.check(y, Y, B, tol, "grouped gemm %s N=%d" % (fmt, lay.N))
         assert G.torch().equal(y, G.run(lay, d, xd)), "grouped and single-layer results differ bitwise"
+
+
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
+@pytest.mark.parametrize("Ns,M", [([4096, 8192], 32), ([1000, 8000], 20), ([2048, 3968], 64)])
+def test_grouped_bf16_narrow_and_wide_layers(fmt, Ns, M):
+    # bf16 x at 17-64 tokens: the GEMM for layers with at least 32 output
+    # tiles of 128 x 128, the fp32 matrix-core GEMV for narrower ones; a
+    # group of both kinds runs its layers one by one.  Each layer equals its
+    # single-layer call bitwise and the oracle within its path's tolerance.
+    G.say("grouped bf16 %s Ns=%s M=%d" % (fmt, Ns, M))
+    K = 2048
+    lays, ds = _group(fmt, Ns, K, seed=M + sum(Ns))
+    x_np = _x(M + 7, M, K, "bf16")
+    xd = G.dev_x(x_np, "bf16")
+    ys = _grouped(fmt, lays, ds, xd)
+    for lay, d, y in zip(lays, ds, ys):
+        Y, B = G.oracle_fwd(lay, x_np, "bf16")
+        G.check(y, Y, B, G.TOL_BF16, "grouped bf16 %s N=%d" % (fmt, lay.N))
+        assert G.torch().equal(y, G.run(lay, d, xd)), "grouped and single-layer results differ bitwise"
+    if all(l.N <= 3968 for l in lays):
+        for lay, y in zip(lays, ys):
+            Y, B = G.oracle_fwd(lay, x_np, "bf16")
+            G.check(y, Y, B, G.TOL_FP32, "grouped bf16 GEMV %s N=%d" % (fmt, lay.N))
 
 
 @pytest.mark.parametrize("fmt,K", [("u8", 11008), ("pk12", 11008), ("u8", 16), ("u8", 4096 + 16)])

@@ -39,9 +39,19 @@ int validate_forward(const void* codebook, const uint8_t* indices, const int32_t
   return HXQ_OK;
 }
 
-int select(bool pk12, bool x_bf16, int64_t M, int64_t K, bool gemv_ok, bool gemm_ok) {
+// bf16 x past 16 tokens: the bf16 GEMM, except up to 64 tokens on a layer
+// with fewer than 32 output tiles of 128 x 128 (N <= 3968), which leaves most
+// CUs idle in the GEMM; there the fp32 matrix-core GEMV (bf16 upcast exactly)
+// is faster.  Decided per layer, so a grouped call picks what single calls do.
+bool bf16_gemm_wanted(int64_t M, int64_t N) {
+  if (M <= 16) return false;
+  if (M > 64) return true;
+  return ((M + 127) / 128) * ((N + 127) / 128) >= 32;
+}
+
+int select(bool pk12, bool x_bf16, int64_t M, int64_t N, int64_t K, bool gemv_ok, bool gemm_ok) {
   if (K == 0) return HXQ_VARIANT_GENERIC;
-  if (x_bf16 && M > 16 && gemm_ok) return HXQ_VARIANT_GEMM_BF16;
+  if (x_bf16 && gemm_ok && M > 16 && (bf16_gemm_wanted(M, N) || !gemv_ok)) return HXQ_VARIANT_GEMM_BF16;
   if (gemv_ok) return HXQ_VARIANT_GEMV_VALU;
   return HXQ_VARIANT_GENERIC;
 }
@@ -83,7 +93,7 @@ int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32
   const bool gemv_ok = K > 0 && hxq::gemv_fast_path_ok(a, pk12);
   const bool gemm_ok = K > 0 && (hxq::gemm5_path_ok(a, pk12) || (pk12 ? hxq::gemm2_path_ok(a, true) : hxq::gemm_path_ok(a)));
   int v = variant;
-  if (v == HXQ_VARIANT_AUTO) v = select(pk12, a.x_bf16, M, K, gemv_ok, gemm_ok);
+  if (v == HXQ_VARIANT_AUTO) v = select(pk12, a.x_bf16, M, N, K, gemv_ok, gemm_ok);
   (void)hipGetLastError();  // start from a clean error state
   switch (v) {
     case HXQ_VARIANT_GEMV_VALU:
@@ -338,11 +348,15 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
   // From 5 to 64 tokens the matrix-core GEMVs, with the kernel a single-layer
   // call would pick for each layer (5 to 8 tokens: the 4x4-block GEMV where it
   // takes the layer, else the 16x16 one; u8 with bf16 x past 16 tokens goes to
-  // the bf16 GEMM instead): one launch when every layer takes the same kernel
-  // and the group fits one workgroup per CU, one launch per layer when they
-  // take the same kernel but do not fit together, else the per-layer calls.
-  const bool bf16_gemm = x_dtype == HXQ_BF16 && M > 16;
-  if (K > 0 && M > 4 && M <= hxq::kGemvMfmaMaxM && !bf16_gemm) {
+  // the bf16 GEMM instead where it wants the layer): one launch when every
+  // layer takes the same kernel and the group fits one workgroup per CU, one
+  // launch per layer when they take the same kernel but do not fit together,
+  // else the per-layer calls.
+  int want_gemm = 0, want_gemv = 0;
+  if (x_dtype == HXQ_BF16 && M > 16)
+    for (int i = 0; i < count; ++i)
+      if (layers[i].N > 0) ++(bf16_gemm_wanted(M, layers[i].N) ? want_gemm : want_gemv);
+  if (K > 0 && M > 4 && M <= hxq::kGemvMfmaMaxM && want_gemm == 0) {
     hxq::GemvSeg gs[hxq::kMaxSegments];
     int ng = 0, n4 = 0, n16 = 0;
     for (int i = 0; i < count; ++i) {
@@ -399,8 +413,9 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
                              : hxq::launch_decode_chunked(segs, nseg, pk12, x, xbf, (int)M, (int)K, stream, err);
     if (done) return status_of(err);
   }
-  // one matrix-core launch for bf16 x past the decode sizes when every layer takes it
-  if (x_dtype == HXQ_BF16 && M > 16 && K > 0) {
+  // one matrix-core launch for bf16 x past the decode sizes when every layer
+  // takes it and wants it
+  if (x_dtype == HXQ_BF16 && M > 16 && K > 0 && want_gemv == 0) {
     hxq::GemmSeg gs[hxq::kMaxSegments];
     int ng = 0;
     bool ok5 = true, ok3 = true, ok = true;
@@ -501,7 +516,7 @@ int hxq_select_variant(int fmt_pk12, int x_dtype, int64_t M, int64_t N, int64_t 
   if (fmt_pk12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
   const bool gemv_ok = K > 0 && K % 16 == 0;
   const bool gemm_ok = x_dtype == HXQ_BF16 && K > 0 && K % 32 == 0;
-  return select(fmt_pk12 != 0, x_dtype == HXQ_BF16, M, K, gemv_ok, gemm_ok);
+  return select(fmt_pk12 != 0, x_dtype == HXQ_BF16, M, N, K, gemv_ok, gemm_ok);
 }
 
 const char* hxq_status_str(int status) {
