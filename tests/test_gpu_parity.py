@@ -109,14 +109,6 @@ def test_pk12_gemm_bf16(N, K, M, variant):
     _case(lay, M, "bf16", variant, G.TOL_BF16, seed=M, what="pk12 gemm")
 
 
-@pytest.mark.parametrize("N,K,nnz,M", [(64, 1024, 8192, 150), (96, 33024, 3000, 130)])
-@pytest.mark.parametrize("variant", GEMMS)
-def test_pk12_gemm_sidecar_paths(N, K, nnz, M, variant):
-    G.say("pk12 gemm sidecar paths N=%d K=%d nnz=%d variant=%d" % (N, K, nnz, variant))
-    lay = gen.random_layer(N + K + 1, N, K, "pk12", nnz=nnz, duplicates=True)
-    _case(lay, M, "bf16", variant, G.TOL_BF16, seed=M, what="pk12 gemm sidecar paths")
-
-
 @pytest.mark.parametrize("M", [1, 5, 16])
 @pytest.mark.parametrize("variant", GEMMS)
 def test_gemm_small_m_forced(M, variant):
@@ -129,9 +121,10 @@ def test_gemm_small_m_forced(M, variant):
     (96, 33024, 3000, 130),   # more stages than the patch bins cover
     (300, 4096, 12000, 200)])  # dense sidecar, patch path in some tiles and walk path in others
 @pytest.mark.parametrize("variant", GEMMS)
-def test_gemm_sidecar_paths(N, K, nnz, M, variant):
-    G.say("gemm sidecar paths N=%d K=%d nnz=%d variant=%d" % (N, K, nnz, variant))
-    lay = gen.random_layer(N + K, N, K, "u8", nnz=nnz, duplicates=True)
+@pytest.mark.parametrize("fmt", ["u8", "pk12"])
+def test_gemm_sidecar_paths(N, K, nnz, M, variant, fmt):
+    G.say("gemm sidecar paths %s N=%d K=%d nnz=%d variant=%d" % (fmt, N, K, nnz, variant))
+    lay = gen.random_layer(N + K, N, K, fmt, nnz=nnz, duplicates=True)
     _case(lay, M, "bf16", variant, G.TOL_BF16, seed=M, what="gemm sidecar paths")
 
 
