@@ -16,19 +16,23 @@
 // from LDS once per wave (64 KB), gathers 8192 codebook entries (each weight
 // once, shared by the tile's 256 tokens) and stores 16 KB of weight tile and
 // 16 KB of x.  Measured with probes on the target: a matrix op takes 33
-// clocks, a 4-byte gather instruction about 2 LDS clocks (conflict-free
-// 32-copy table), so the gathers, not the operand bytes, are the LDS cost
-// that competes with the matrix ops; with one wave per SIMD every stall of
-// the wave also stalls its matrix core, so the stage is ordered by hand.
+// clocks, and the gathers, not the operand bytes, are the LDS cost that
+// competes with the matrix ops; the u8 codebook therefore sits in LDS as 64
+// copies, lane l reading copy l (one bank per lane: 5-8% faster than 32
+// copies, where lanes l and l + 32 share a bank).  With one wave per SIMD
+// every stall of the wave also stalls its matrix core, so the stage is
+// ordered by hand.
 //
 // Pipeline of stage s (one barrier per stage; the operands of s were read
 // during stage s - 1):
 //   - the 32 matrix ops of stage s;
 //   - between them: reads of stage s + 1's operands into the second register
 //     set, gathers and packing of W(s + 2) (from index bytes requested two
-//     stages ago) into the third weight buffer, its sidecar patches, the
-//     store of x(s + 2) (registers requested two stages ago) into the x
-//     ring, and the requests for x and index bytes of stage s + 4.
+//     stages ago) into the weight buffer W(s) used (its reads ended with
+//     stage s - 1), its sidecar patches, the store of x(s + 2) (registers
+//     requested two stages ago) into x(s)'s slot likewise, and the requests
+//     for x and index bytes of stage s + 4.  Two weight buffers and two x
+//     slots suffice.
 // All global loads are ordinary loads the compiler waits for.
 //
 // Sidecar triplets become patches before the main loop (for each distinct
@@ -51,15 +55,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 namespace gemm5 {
 constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int THREADS = 256, WAVES = 4;
-constexpr int XR = 3;          // x stages in LDS
-constexpr int WR = 3;          // weight-tile stages in LDS
+constexpr int XR = 2;          // x stages in LDS
+constexpr int WR = 2;          // weight-tile stages in LDS
 constexpr int MAXST = 384;     // stages on the patch path: K <= 12288
 constexpr int CAP = 4096;      // patches per tile
 constexpr int XS = BM * BK * 2;  // bytes of one x stage (16 blocks of 16 tokens)
 constexpr int WT = BN * BK * 2;  // bytes of one weight stage (8 row blocks x 2 sub-steps)
 template <bool PK12>
 struct Lay {
-  static constexpr int CB = PK12 ? 4096 * 4 : 256 * 128;
+  static constexpr int CB = PK12 ? 4096 * 4 : 256 * 256;
   static constexpr int MAXBINS = MAXST * WAVES;
   static constexpr int OFF_CBF = 0;
   static constexpr int OFF_W = OFF_CBF + (PK12 ? 0 : 1024);
@@ -69,7 +73,7 @@ struct Lay {
   static constexpr int OFF_MISC = OFF_PATCH + CAP * 4;
   static constexpr int LDS = OFF_MISC + 16 + 4 * WAVES;
   static_assert(CAP <= WR * WT, "head flags overlay the weight tiles");
-  static_assert((MAXBINS + 4) * 4 <= XS, "bin counters overlay the third x stage");
+  static_assert(4096 + (MAXBINS + 4) * 4 <= WR * WT, "bin counters overlay the weight tiles after the head flags");
   static_assert(MAXBINS % THREADS == 0, "bin prefix split");
   static_assert(CB + LDS <= 160 * 1024, "LDS");
 };
@@ -165,7 +169,8 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
   load_i(1, ip1);
   load_x(1, xp1);
 
-  // ---- codebook.  u8: 32 copies per entry, lane l reads copy l % 32; pk12:
+  // ---- codebook.  u8: 64 copies per entry (entry e, copy c at byte 256 e + 4 c),
+  // lane l reads copy l; pk12:
   // each component rounded to nearest even on its own
   if (PK12) {
 #pragma unroll
@@ -180,14 +185,14 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
     const float vb = __uint_as_float(f32_to_bf16_rne(cv) << 16);
     const float4 v4 = make_float4(vb, vb, vb, vb);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) *reinterpret_cast<float4*>(cbs + e * 128 + (((q + e) & 7) << 4)) = v4;
+    for (int q = 0; q < 16; ++q) *reinterpret_cast<float4*>(cbs + e * 256 + (((q + e) & 15) << 4)) = v4;
     cbf[e] = cv;
   }
 
   // ---- sidecar: the tile's triplet range [lo, hi)
   const bool long_k = nk > MAXST;
   const int nbins = nk * WAVES;
-  int* cnt32 = reinterpret_cast<int*>(xbuf + 2 * XS);  // third x stage, first written in the loop
+  int* cnt32 = reinterpret_cast<int*>(wbuf + 4096);  // after the head flags; the weight buffers are first written after the set-up
   if (!long_k)
     for (int i = tid; i <= nbins; i += THREADS) cnt32[i] = 0;
   __syncthreads();
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
   // ---- building: lane (h, l32) turns the 16 (12) index bytes of row
   // 32 RB + l32, k = 16 h + [0, 16) (RB = 2 wave + rb) into 8 operand words:
   // block (RB, sub-step h) at bytes 16 l32 (k + [0, 8)) and 512 + 16 l32
-  const uint32_t lanec = (uint32_t)l32 << 2;
+  const uint32_t lane4 = (uint32_t)lane << 2;
   auto wofs = [&](int rb) { return (2 * (2 * wave + rb) + h) * 1024 + l32 * 16; };
   auto build = [&](const u32x4 iq, unsigned char* wt, int rb) {
     uint32_t w[8];
@@ -306,10 +311,10 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
         w[2 * d + 1] = lds_load<uint32_t>((v >> 12) << 2, cbs);
       } else {
         const uint32_t wd = iq[d];
-        const uint32_t f0 = lds_load<uint32_t>(((wd << 7) & 0x7f80u) | lanec, cbs);
-        const uint32_t f1 = lds_load<uint32_t>(((wd >> 1) & 0x7f80u) | lanec, cbs);
-        const uint32_t f2 = lds_load<uint32_t>(((wd >> 9) & 0x7f80u) | lanec, cbs);
-        const uint32_t f3 = lds_load<uint32_t>(((wd >> 17) & 0x7f80u) | lanec, cbs);
+        const uint32_t f0 = lds_load<uint32_t>(byte_addr256<0>(wd, lane4), cbs);
+        const uint32_t f1 = lds_load<uint32_t>(byte_addr256<1>(wd, lane4), cbs);
+        const uint32_t f2 = lds_load<uint32_t>(byte_addr256<2>(wd, lane4), cbs);
+        const uint32_t f3 = lds_load<uint32_t>(byte_addr256<3>(wd, lane4), cbs);
         w[2 * d] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
         w[2 * d + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
       }
@@ -407,11 +412,11 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
         } else {
           const uint32_t wd = iq[d];
           if (half == 0) {
-            gw[rb][4 * d] = lds_load<uint32_t>(((wd << 7) & 0x7f80u) | lanec, cbs);
-            gw[rb][4 * d + 1] = lds_load<uint32_t>(((wd >> 1) & 0x7f80u) | lanec, cbs);
+            gw[rb][4 * d] = lds_load<uint32_t>(byte_addr256<0>(wd, lane4), cbs);
+            gw[rb][4 * d + 1] = lds_load<uint32_t>(byte_addr256<1>(wd, lane4), cbs);
           } else {
-            gw[rb][4 * d + 2] = lds_load<uint32_t>(((wd >> 9) & 0x7f80u) | lanec, cbs);
-            gw[rb][4 * d + 3] = lds_load<uint32_t>(((wd >> 17) & 0x7f80u) | lanec, cbs);
+            gw[rb][4 * d + 2] = lds_load<uint32_t>(byte_addr256<2>(wd, lane4), cbs);
+            gw[rb][4 * d + 3] = lds_load<uint32_t>(byte_addr256<3>(wd, lane4), cbs);
           }
         }
       };
