@@ -16,7 +16,8 @@ move: indices, codebooks, sidecar triplets, x once per launch, bias, y) over
 the GPU time of the timed steps.  Also reported: the same step issued as seven
 single-layer calls, the M = 8 step, the bf16 prefill GEMM at M = 2048
 (TFLOP/s; u8 layer set and two pk12 layers), the input gradient dx = dy W of
-the layer set (M = 1 fp32 in GB/s, M = 2048 bf16 in TFLOP/s), the read
+the layer set, one grouped call per shared input like the forward (M = 1
+fp32 in GB/s, M = 2048 bf16 in TFLOP/s), the read
 bandwidth of a plain streaming kernel over the same rotated buffers, the
 roofline of the dominant launch (gate|up) and the CPU oracle baseline.
 
@@ -156,27 +157,71 @@ class BwdCall:
             raise RuntimeError("hxq_linear_bwd_x failed with status %d" % st)
 
 
+class BwdGroupCall:
+    """One pre-marshalled hxq_linear_bwd_x_grouped call: dx = sum_i dy_i W_i
+    over layers that share their input."""
+
+    def __init__(self, L, B, ds, dys, dx, M, K, stream, ws):
+        self.fn = L.hxq_linear_bwd_x_grouped
+        self.arr = (B.HxqBwdLayer * len(ds))()
+        for i, (d, dy) in enumerate(zip(ds, dys)):
+            self.arr[i] = B.HxqBwdLayer(d["codebook"].data_ptr(), d["indices"].data_ptr(), d["rows"].data_ptr(),
+                                        d["cols"].data_ptr(), d["deltas"].data_ptr(), d["rows"].numel(),
+                                        dy.data_ptr(), d["indices"].shape[0])
+        self.dyt = B.HXQ_BF16 if dys[0].element_size() == 2 else B.HXQ_F32
+        self.need = L.hxq_linear_bwd_x_grouped_workspace(B.HXQ_FMT_U8, self.dyt, self.arr, len(ds), M, K)
+        self.args = (B.HXQ_FMT_U8, self.arr, len(ds), self.dyt, dx.data_ptr(), M, K,
+                     ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, stream)
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError("hxq_linear_bwd_x_grouped failed with status %d" % st)
+
+
 def bwd_bytes(l, M, dy_bytes):
     """Bytes the input gradient of one u8 layer must move: index storage,
     codebook, sidecar triplets, dy once and the fp32 dx."""
     return l.N * l.K + 256 * 4 + 12 * l.nnz + M * l.N * dy_bytes + 4 * M * l.K
 
 
+def bwd_group_bytes(ls, M, dy_bytes):
+    """The same for layers sharing their input: one dx for the group."""
+    return sum(bwd_bytes(l, M, dy_bytes) - 4 * M * l.K for l in ls) + 4 * M * ls[0].K
+
+
 def input_gradient(torch, L, B, layers, devs, M, dtype, steps, warmup, stream):
-    """dx = dy W for every layer of the set, one call per layer (devs[r][i]:
-    copy r of layer i).  Returns per-layer averages and the seven-layer step."""
+    """dx = dy W through the layer set (devs[r][i]: copy r of layer i): the
+    step is one grouped call per input the layers share (q|k|v, o, gate|up,
+    down: each input's gradient summed over its layers); per-layer averages
+    come from single-layer calls."""
     import numpy as np
 
     rng = np.random.Generator(np.random.PCG64(77))
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     dys = [torch.from_numpy(rng.standard_normal((M, l.N)).astype(np.float32)).cuda().to(tdt) for l in layers]
     dxs = [torch.empty((M, l.K), dtype=torch.float32, device="cuda") for l in layers]
+    by_name = {l.name: i for i, l in enumerate(layers)}
+    gidx = [[by_name[n] for n in g] for g in GROUPS]
+    gdx = [torch.empty((M, layers[ix[0]].K), dtype=torch.float32, device="cuda") for ix in gidx]
     need = max(L.hxq_linear_bwd_x_workspace(B.HXQ_FMT_U8, B.HXQ_F32 if dtype == "f32" else B.HXQ_BF16, M, l.N,
                                             l.K, l.nnz) for l in layers)
+    for ix, dx in zip(gidx, gdx):
+        probe = BwdGroupCall(L, B, [devs[0][i] for i in ix], [dys[i] for i in ix], dx, M, layers[ix[0]].K,
+                             stream, None)
+        if probe.need < 0:
+            raise RuntimeError("hxq_linear_bwd_x_grouped_workspace failed with status %d" % probe.need)
+        need = max(need, probe.need)
     ws = torch.empty(max(int(need), 16), dtype=torch.uint8, device="cuda")
     calls = [[BwdCall(L, B, row[i], dys[i], dxs[i], M, l.N, l.K, stream, ws) for i, l in enumerate(layers)]
              for row in devs]
-    total = time_steps(torch, calls, steps, warmup)
+    gcalls = [[BwdGroupCall(L, B, [row[i] for i in ix], [dys[i] for i in ix], dx, M, layers[ix[0]].K, stream, ws)
+               for ix, dx in zip(gidx, gdx)] for row in devs]
+    total = time_steps(torch, gcalls, steps, warmup)
+    per_group = []
+    for g in range(len(GROUPS)):
+        tg = time_steps(torch, [[row[g]] for row in gcalls], steps, 1)
+        per_group.append(round(tg / steps * 1e3, 2))
     avg = []
     for i in range(len(layers)):
         ti = time_steps(torch, [[row[i]] for row in calls], steps, 1)
@@ -191,18 +236,19 @@ def input_gradient(torch, L, B, layers, devs, M, dtype, steps, warmup, stream):
             r["tflops"] = round(2.0 * M * l.N * l.K / (m * 1e-3) / 1e12, 1)
         rows.append(r)
     step_us = total / steps * 1e3
-    out = dict(M=M, dy_dtype=dtype, step_us=round(step_us, 2), layers=rows, workspace_bytes=int(need))
+    out = dict(M=M, dy_dtype=dtype, step_us=round(step_us, 2), layers=rows, workspace_bytes=int(need),
+               launches=dict(zip(["qkv", "o", "gateup", "down"], per_group)))
     if M == 1:
-        gbs = sum(bwd_bytes(l, M, xb) for l in layers) / (step_us * 1e-6) / 1e9
-        out.update(workload="input gradient dx = dy W of the Qwen2.5-3B-shaped u8 layer set, M=1, fp32 dy, "
-                            "one call per layer, rotating copies", gbs=round(gbs, 1),
-                   frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+        gbs = sum(bwd_group_bytes([layers[i] for i in ix], M, xb) for ix in gidx) / (step_us * 1e-6) / 1e9
+        out.update(workload="input gradient of the Qwen2.5-3B-shaped u8 layer set, M=1, fp32 dy: one grouped "
+                            "call per shared input (q|k|v, o, gate|up, down; dx = sum of dy_i W_i), rotating copies",
+                   gbs=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
     else:
         tfs = sum(2.0 * M * l.N * l.K for l in layers) / (step_us * 1e-6) / 1e12
-        out.update(workload="input gradient dx = dy W of the Qwen2.5-3B-shaped u8 layer set, M=%d, bf16 dy "
-                            "(bf16 matrix cores), one call per layer" % M, tflops=round(tfs, 1),
-                   frac_of_mfma_peak=round(tfs / MFMA_BF16_PEAK_TFS, 4))
-    del dys, dxs, ws
+        out.update(workload="input gradient of the Qwen2.5-3B-shaped u8 layer set, M=%d, bf16 dy (bf16 matrix "
+                            "cores): one grouped call per shared input (q|k|v, o, gate|up, down)" % M,
+                   tflops=round(tfs, 1), frac_of_mfma_peak=round(tfs / MFMA_BF16_PEAK_TFS, 4))
+    del dys, dxs, gdx, ws
     return out
 
 

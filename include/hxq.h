@@ -273,6 +273,59 @@ int hxq_linear_bwd_x_noalloc(int fmt, const float* codebook, const uint8_t* indi
 int64_t hxq_linear_bwd_x_workspace(int fmt, int dy_dtype, int64_t M, int64_t N,
                                    int64_t K, int64_t nnz);
 
+/* The input gradient of several layers that read the same activations (the
+ * query, key and value projections; the gate and up projections), their
+ * contributions summed:
+ *
+ *     dx[m][k] = sum over layers i of sum_n dy_i[m][n] * W_i[n][k]
+ *
+ * which is the gradient with respect to the shared x of what
+ * hxq_linear_fwd_grouped computes (each layer's W as for hxq_linear_bwd_x).
+ *   fmt        HXQ_FMT_U8 or HXQ_FMT_PK12.
+ *   layers     host array of `count` descriptors, 1 <= count <= HXQ_MAX_GROUP,
+ *              read during the call only: codebook, indices, sidecar and N as
+ *              for hxq_linear_bwd_x, dy the layer's [M][N] gradient
+ *              (dy_dtype).  A layer with N == 0 adds nothing.
+ *   dy_dtype, dx, M, K, stream  as for hxq_linear_bwd_x; dx receives the sum.
+ *   workspace  caller-owned device memory, 16-byte aligned, of at least the
+ *              size hxq_linear_bwd_x_grouped_workspace gives (which assumes
+ *              16-byte aligned dy, dx and indices); contents on entry ignored
+ *              and on return unspecified.  It holds a partial sum of dx for
+ *              every run of rows the layers are split into.
+ * Arithmetic: as hxq_linear_bwd_x for every layer (the bf16 matrix-core
+ * products when every layer's shape and pointers allow them, else fp32
+ * products for all); the partial sums are added in a fixed order (layer
+ * order, then row order).  With a single layer of N > 0 the result is that of
+ * hxq_linear_bwd_x with the same workspace.  Work is one or two launches on
+ * `stream` (the product over all layers, the sum), or with bf16 matrix-core
+ * products one or two per layer (sidecar binning, product) and the sum.
+ * Errors: HXQ_ERR_SHAPE for count out of range or an unknown fmt, HXQ_ERR_NULL
+ * for NULL layers, otherwise the first error hxq_linear_bwd_x would return for
+ * any layer; HXQ_ERR_UNSUPPORTED when the workspace is smaller than the call
+ * needs; nothing is launched when an error is returned. */
+typedef struct hxq_bwd_layer {
+  const void* codebook;     /* u8: float[256]; pk12: float[4096][2] */
+  const uint8_t* indices;   /* u8: [N][K]; pk12: [N][3*ceil(K/4)] */
+  const int32_t* sc_rows;
+  const int32_t* sc_cols;
+  const float* sc_deltas;
+  int64_t nnz;
+  const void* dy;           /* [M][N] float32 or bf16 bits */
+  int64_t N;
+} hxq_bwd_layer;
+
+int hxq_linear_bwd_x_grouped(int fmt, const hxq_bwd_layer* layers, int count,
+                             int dy_dtype, float* dx, int64_t M, int64_t K,
+                             void* workspace, int64_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Bytes of workspace hxq_linear_bwd_x_grouped needs on the current device for
+ * these layers (only their N and nnz are read) with 16-byte aligned pointers,
+ * or a negative hxq_status for arguments it would reject (HXQ_ERR_SHAPE,
+ * HXQ_ERR_DTYPE, HXQ_ERR_NULL).  Host only. */
+int64_t hxq_linear_bwd_x_grouped_workspace(int fmt, int dy_dtype, const hxq_bwd_layer* layers,
+                                           int count, int64_t M, int64_t K);
+
 /* The same with the kernel family forced: HXQ_VARIANT_AUTO;
  * HXQ_VARIANT_GEMV_VALU, the vector-FMA kernel (any shape); or
  * HXQ_VARIANT_GEMM_BF16, the bf16 matrix-core kernel (bf16 dy, N % 32 == 0,

@@ -295,3 +295,58 @@ def test_noalloc_bwd_rejects_oversize_before_any_hip_call(L):
     # M == 0 does nothing
     assert L.hxq_linear_bwd_x_noalloc(B.HXQ_FMT_U8, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, B.HXQ_F32, FAKE, 0, N, K,
                                       None) == B.HXQ_OK
+
+
+def _bwd_layers(specs):
+    """hxq_bwd_layer array of (N, nnz) with stand-in pointers (never dereferenced)."""
+    arr = (B.HxqBwdLayer * len(specs))()
+    for i, (N, nnz) in enumerate(specs):
+        arr[i] = B.HxqBwdLayer(FAKE, FAKE, FAKE, FAKE, FAKE, nnz, FAKE, N)
+    return arr
+
+
+def test_bwd_x_grouped_workspace_query(L):
+    q = L.hxq_linear_bwd_x_grouped_workspace
+    F32, BF, U8 = B.HXQ_F32, B.HXQ_BF16, B.HXQ_FMT_U8
+    two = _bwd_layers([(2048, 10), (256, 3)])
+    assert q(9, F32, two, 2, 1, 2048) == B.HXQ_ERR_SHAPE
+    assert q(U8, 5, two, 2, 1, 2048) == B.HXQ_ERR_DTYPE
+    assert q(U8, F32, two, 0, 1, 2048) == B.HXQ_ERR_SHAPE
+    assert q(U8, F32, two, B.HXQ_MAX_GROUP + 1, 1, 2048) == B.HXQ_ERR_SHAPE
+    assert q(U8, F32, None, 2, 1, 2048) == B.HXQ_ERR_NULL
+    assert q(B.HXQ_FMT_PK12, F32, two, 2, 1, 2047) == B.HXQ_ERR_SHAPE
+    assert q(U8, F32, _bwd_layers([(-1, 0), (8, 0)]), 2, 1, 64) == B.HXQ_ERR_SHAPE
+    assert q(U8, F32, two, 2, 0, 2048) == 0
+    assert q(U8, F32, _bwd_layers([(0, 0), (0, 0)]), 2, 4, 64) == 0
+    # one layer with rows: what the single-layer call asks for
+    for M, dt in ((1, F32), (256, BF)):
+        assert q(U8, dt, _bwd_layers([(0, 0), (2048, 40)]), 2, M, 2048) == \
+            L.hxq_linear_bwd_x_workspace(U8, dt, M, 2048, 2048, 40)
+    # vector path: one partial sum of [M][K] fp32 per run of rows, at least one per layer
+    for M in (1, 3, 8):
+        n = q(U8, F32, _bwd_layers([(2048, 10), (256, 3), (256, 3)]), 3, M, 2048)
+        assert n >= 3 * M * 2048 * 4 and n % (M * 2048 * 4) == 0
+    # matrix-core path: the sidecar bins come on top of the partial sums
+    assert q(U8, BF, _bwd_layers([(2048, 4096), (256, 400)]), 2, 256, 2048) > \
+        q(U8, BF, _bwd_layers([(2048, 0), (256, 0)]), 2, 256, 2048)
+
+
+def test_bwd_x_grouped_rejects_before_any_hip_call(L):
+    g = L.hxq_linear_bwd_x_grouped
+    F32, U8 = B.HXQ_F32, B.HXQ_FMT_U8
+    two = _bwd_layers([(300, 5), (200, 5)])
+    M, K = 2, 1024
+    assert g(9, two, 2, F32, FAKE, M, K, FAKE, 1 << 20, None) == B.HXQ_ERR_SHAPE
+    assert g(U8, two, 0, F32, FAKE, M, K, FAKE, 1 << 20, None) == B.HXQ_ERR_SHAPE
+    assert g(U8, None, 2, F32, FAKE, M, K, FAKE, 1 << 20, None) == B.HXQ_ERR_NULL
+    assert g(U8, two, 2, 7, FAKE, M, K, FAKE, 1 << 20, None) == B.HXQ_ERR_DTYPE
+    assert g(U8, two, 2, F32, None, M, K, FAKE, 1 << 20, None) == B.HXQ_ERR_NULL
+    assert g(U8, two, 2, F32, FAKE, M, K, FAKE + 8, 1 << 20, None) == B.HXQ_ERR_ALIGN
+    assert g(U8, _bwd_layers([(300, 5), (-2, 0)]), 2, F32, FAKE, M, K, FAKE, 1 << 20, None) == B.HXQ_ERR_SHAPE
+    # too little workspace for two layers: refused, nothing launched
+    need = L.hxq_linear_bwd_x_grouped_workspace(U8, F32, two, 2, M, K)
+    assert need > 0
+    assert g(U8, two, 2, F32, FAKE, M, K, FAKE, need - 256, None) == B.HXQ_ERR_UNSUPPORTED
+    assert g(U8, two, 2, F32, FAKE, M, K, None, 0, None) == B.HXQ_ERR_UNSUPPORTED
+    # nothing to compute
+    assert g(U8, two, 2, F32, FAKE, 0, K, None, 0, None) == B.HXQ_OK

@@ -19,10 +19,12 @@ from ._binding import (  # noqa: F401
     HXQ_VARIANT_GEMV_VALU,
     HXQ_VARIANT_GENERIC,
     VARIANT_NAMES,
+    HxqBwdLayer,
     HxqError,
     HxqLayer,
     hxq_dequant_bf16,
     hxq_linear_bwd_x,
+    hxq_linear_bwd_x_grouped,
     hxq_linear_bwd_x_noalloc,
     hxq_linear_bwd_x_workspace,
     hxq_linear_fwd_grouped,

@@ -75,6 +75,15 @@ class HxqLayer(ctypes.Structure):
                 ("bias", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64)]
 
 
+class HxqBwdLayer(ctypes.Structure):
+    """struct hxq_bwd_layer of include/hxq.h."""
+
+    _fields_ = [("codebook", ctypes.c_void_p), ("indices", ctypes.c_void_p),
+                ("sc_rows", ctypes.c_void_p), ("sc_cols", ctypes.c_void_p),
+                ("sc_deltas", ctypes.c_void_p), ("nnz", ctypes.c_int64),
+                ("dy", ctypes.c_void_p), ("N", ctypes.c_int64)]
+
+
 _FWD_ARGS = [_P, _P, _P, _P, _P, _I64, _P, _INT, _P, _P, _I64, _I64, _I64, _P]
 SIGNATURES = {
     "hxq_linear_fwd_u8": (_INT, _FWD_ARGS),
@@ -90,6 +99,9 @@ SIGNATURES = {
                                    _INT]),
     "hxq_linear_bwd_x_noalloc": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P]),
     "hxq_linear_bwd_x_workspace": (_I64, [_INT, _INT, _I64, _I64, _I64, _I64]),
+    "hxq_linear_bwd_x_grouped": (_INT, [_INT, ctypes.POINTER(HxqBwdLayer), _INT, _INT, _P, _I64, _I64, _P, _I64,
+                                        _P]),
+    "hxq_linear_bwd_x_grouped_workspace": (_I64, [_INT, _INT, ctypes.POINTER(HxqBwdLayer), _INT, _I64, _I64]),
     "hxq_select_variant": (_INT, [_INT, _INT, _I64, _I64, _I64]),
     "hxq_status_str": (ctypes.c_char_p, [_INT]),
     "hxq_version": (_INT, []),
@@ -392,6 +404,63 @@ def hxq_linear_fwd_grouped(fmt: int, layers, x, stream=None) -> None:
     st = lib().hxq_linear_fwd_grouped(fmt, arr, len(layers), _ptr(x), _x_dtype(x), M, K, _stream(stream, dev))
     if st != HXQ_OK:
         raise HxqError(st, "hxq_linear_fwd_grouped")
+
+
+def grouped_bwd_layers(fmt: int, layers, M: int, K: int, dy_dtype: int):
+    """HxqBwdLayer array for hxq_linear_bwd_x_grouped from dicts holding the
+    tensors codebook, indices, sc_rows, sc_cols, sc_deltas (or None) and dy.
+    Checks dtypes and shapes like hxq_linear_bwd_x."""
+    torch = _torch()
+    if not 1 <= len(layers) <= HXQ_MAX_GROUP:
+        raise ValueError("between 1 and %d layers per call" % HXQ_MAX_GROUP)
+    arr = (HxqBwdLayer * len(layers))()
+    for i, l in enumerate(layers):
+        cb, idx, dy = l["codebook"], l["indices"], l["dy"]
+        if cb.dtype != torch.float32 or cb.numel() != (256 if fmt == HXQ_FMT_U8 else 8192):
+            raise ValueError("layer %d: wrong codebook size or dtype" % i)
+        if idx.dtype != torch.uint8 or idx.dim() != 2 or not idx.is_contiguous():
+            raise ValueError("layer %d: indices must be a contiguous uint8 matrix" % i)
+        N = idx.shape[0]
+        row = K if fmt == HXQ_FMT_U8 else 3 * ((K + 3) // 4)
+        if idx.shape[1] != row:
+            raise ValueError("layer %d: index rows hold %d bytes, expected %d" % (i, idx.shape[1], row))
+        if dy.dim() != 2 or not dy.is_contiguous() or tuple(dy.shape) != (M, N) or _x_dtype(dy) != dy_dtype:
+            raise ValueError("layer %d: dy must be a contiguous [M, N] tensor of the group's dtype" % i)
+        nnz = _check_sidecar(l.get("sc_rows"), l.get("sc_cols"), l.get("sc_deltas"))
+        _check_device(cb, idx, l.get("sc_rows"), l.get("sc_cols"), l.get("sc_deltas"), dy)
+        arr[i] = HxqBwdLayer(_ptr(cb), _ptr(idx), _ptr(l.get("sc_rows")), _ptr(l.get("sc_cols")),
+                             _ptr(l.get("sc_deltas")), nnz, _ptr(dy), N)
+    return arr
+
+
+def hxq_linear_bwd_x_grouped(fmt: int, layers, dx, stream=None, workspace=None) -> None:
+    """dx <- sum over layers of dy_i (C_i[indices_i] + S_i): the input gradient
+    of layers that share their input (each dict as for grouped_bwd_layers).
+    dx is a contiguous float32 [M, K] tensor.  ``workspace`` (a device tensor)
+    holds the partial sums; when None, one of the size the library asks for
+    is taken from torch's caching allocator."""
+    torch = _torch()
+    if dx.dtype != torch.float32 or dx.dim() != 2 or not dx.is_contiguous():
+        raise ValueError("dx must be a contiguous float32 [M, K] tensor")
+    M, K = dx.shape
+    if not layers:
+        raise ValueError("between 1 and %d layers per call" % HXQ_MAX_GROUP)
+    dyt = _x_dtype(layers[0]["dy"])
+    arr = grouped_bwd_layers(fmt, layers, M, K, dyt)
+    dev = _check_device(dx, workspace if workspace is not None and workspace.numel() > 0 else None)
+    if workspace is None:
+        need = lib().hxq_linear_bwd_x_grouped_workspace(fmt, dyt, arr, len(layers), M, K)
+        if need < 0:
+            raise HxqError(int(need), "hxq_linear_bwd_x_grouped_workspace")
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dx.device) if need > 0 else None
+    if workspace is None or workspace.numel() == 0:
+        wptr, wbytes = None, 0
+    else:
+        wptr, wbytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = lib().hxq_linear_bwd_x_grouped(fmt, arr, len(layers), dyt, _ptr(dx), M, K, wptr, wbytes,
+                                        _stream(stream, dev))
+    if st != HXQ_OK:
+        raise HxqError(st, "hxq_linear_bwd_x_grouped")
 
 
 def hxq_linear_bwd_x_workspace(fmt: int, dy_dtype: int, M: int, N: int, K: int, nnz: int) -> int:

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cstdint>
@@ -189,6 +190,132 @@ int backward_x(int fmt, const float* codebook, const uint8_t* indices, const int
   return status_of(hxq::launch_bwdx_valu(a, pk12, stream));
 }
 
+// ---- grouped input gradient: dx = sum over layers of dy_i W_i
+
+hxq::BwdArgs bwd_args_of(const hxq_bwd_layer& l, bool dy_bf16, float* dx, int64_t M, int64_t K) {
+  hxq::BwdArgs a = {};
+  a.codebook = static_cast<const float*>(l.codebook);
+  a.indices = l.indices;
+  a.sc_rows = l.sc_rows;
+  a.sc_cols = l.sc_cols;
+  a.sc_deltas = l.sc_deltas;
+  a.nnz = l.nnz;
+  a.dy = l.dy;
+  a.dy_bf16 = dy_bf16;
+  a.dx = dx;
+  a.M = (int)M;
+  a.N = (int)l.N;
+  a.K = (int)K;
+  return a;
+}
+
+// The path of a call over n >= 2 layers with N > 0 and the workspace it
+// needs: with matrix-core products the sidecar bins of one layer at a time
+// (the layers run in turn) and then every layer's row splits; on the vector
+// path the splits of its single launch.  aligned: plan for 16-byte aligned
+// pointers (the workspace query) instead of the layers' own.
+struct BwdGroupWs {
+  bool mfma;
+  int64_t bin_bytes;  // a multiple of 256: the split slots follow
+  int slots;
+  int64_t bytes;
+};
+
+BwdGroupWs plan_group(bool pk12, bool dy_bf16, const hxq_bwd_layer* act, int n, int64_t M, int64_t K, float* dx,
+                      bool aligned) {
+  const int64_t per = M * K * 4;
+  bool mfma = dy_bf16 && M >= kBwdMfmaMinM;
+  for (int i = 0; i < n && mfma; ++i) {
+    hxq::BwdArgs a = bwd_args_of(act[i], dy_bf16, dx, M, K);
+    if (aligned) {
+      a.indices = reinterpret_cast<const uint8_t*>(uintptr_t(256));
+      a.dy = reinterpret_cast<const void*>(uintptr_t(256));
+      a.dx = reinterpret_cast<float*>(uintptr_t(256));
+    }
+    mfma = hxq::bwdx_mfma_ok(a, pk12);
+  }
+  BwdGroupWs w = {};
+  w.mfma = mfma;
+  if (mfma) {
+    for (int i = 0; i < n; ++i) {
+      const hxq::BwdMPlan p = hxq::bwdx_mfma_plan((int)M, (int)act[i].N, (int)K, act[i].nnz);
+      w.bin_bytes = std::max(w.bin_bytes, p.bin_bytes);
+      w.slots += p.S;
+    }
+  } else {
+    int Ns[hxq::kMaxSegments];
+    for (int i = 0; i < n; ++i) Ns[i] = (int)act[i].N;
+    w.slots = hxq::bwdx_group_plan((int)M, Ns, n, (int)K).slots_total;
+  }
+  w.bytes = w.bin_bytes + (int64_t)w.slots * per;
+  return w;
+}
+
+int check_group(int fmt, const hxq_bwd_layer* layers, int count, int dy_dtype) {
+  if (fmt != HXQ_FMT_U8 && fmt != HXQ_FMT_PK12) return HXQ_ERR_SHAPE;
+  if (count < 1 || count > HXQ_MAX_GROUP) return HXQ_ERR_SHAPE;
+  if (dy_dtype != HXQ_F32 && dy_dtype != HXQ_BF16) return HXQ_ERR_DTYPE;
+  if (!layers) return HXQ_ERR_NULL;
+  return HXQ_OK;
+}
+
+int backward_x_grouped(int fmt, const hxq_bwd_layer* layers, int count, int dy_dtype, float* dx, int64_t M,
+                       int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  int st = check_group(fmt, layers, count, dy_dtype);
+  if (st != HXQ_OK) return st;
+  for (int i = 0; i < count; ++i) {
+    const hxq_bwd_layer& l = layers[i];
+    st = validate_bwd(fmt, static_cast<const float*>(l.codebook), l.indices, l.sc_rows, l.sc_cols, l.sc_deltas,
+                      l.nnz, l.dy, dy_dtype, dx, M, l.N, K, workspace, workspace_bytes, HXQ_VARIANT_AUTO);
+    if (st != HXQ_OK) return st;
+  }
+  if (misaligned(workspace, 16)) return HXQ_ERR_ALIGN;
+  if (M == 0 || K == 0) return HXQ_OK;
+  hxq_bwd_layer act[HXQ_MAX_GROUP];
+  int n = 0;
+  for (int i = 0; i < count; ++i)
+    if (layers[i].N > 0) act[n++] = layers[i];
+  if (n <= 1) {
+    if (n == 0) {
+      (void)hipGetLastError();
+      return status_of(hxq::launch_fill_zero(dx, M * K, stream));
+    }
+    const hxq_bwd_layer& l = act[0];
+    return backward_x(fmt, static_cast<const float*>(l.codebook), l.indices, l.sc_rows, l.sc_cols, l.sc_deltas,
+                      l.nnz, l.dy, dy_dtype, dx, M, l.N, K, workspace, workspace_bytes, stream, HXQ_VARIANT_AUTO);
+  }
+  const bool pk12 = fmt == HXQ_FMT_PK12, dy_bf16 = dy_dtype == HXQ_BF16;
+  const BwdGroupWs w = plan_group(pk12, dy_bf16, act, n, M, K, dx, false);
+  if (workspace == nullptr || workspace_bytes < w.bytes) return HXQ_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  unsigned char* wb = static_cast<unsigned char*>(workspace);
+  if (w.mfma) {
+    float* slots = reinterpret_cast<float*>(wb + w.bin_bytes);
+    int slot0 = 0;
+    for (int i = 0; i < n; ++i) {
+      hxq::BwdArgs a = bwd_args_of(act[i], dy_bf16, dx, M, K);
+      a.ws = reinterpret_cast<float*>(wb);
+      a.ws_bytes = w.bin_bytes;
+      a.slots = slots;
+      a.slot0 = slot0;
+      const hipError_t e = hxq::launch_bwdx_mfma(a, pk12, stream);
+      if (e != hipSuccess) return status_of(e);
+      slot0 += hxq::bwdx_mfma_plan(a.M, a.N, a.K, a.nnz).S;
+    }
+    return status_of(hxq::launch_bwdx_reduce(slots, dx, M * K, slot0, stream));
+  }
+  hxq::BwdArgs a = bwd_args_of(act[0], dy_bf16, dx, M, K);
+  a.ws = reinterpret_cast<float*>(wb);
+  a.ws_bytes = workspace_bytes;
+  a.nseg = n;
+  for (int i = 0; i < n; ++i) {
+    const hxq_bwd_layer& l = act[i];
+    a.seg[i] = {static_cast<const float*>(l.codebook), l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz, l.dy,
+                (int)l.N, 0, 0};
+  }
+  return status_of(hxq::launch_bwdx_valu_grouped(a, pk12, stream));
+}
+
 // ---- device scratch of the allocation-free input gradient.  One array per
 // GPU (each device holds its own copy of this module's globals), kept until
 // the process ends.  In host code `scratch` only names the symbol: its
@@ -271,6 +398,29 @@ int64_t hxq_linear_bwd_x_workspace(int fmt, int dy_dtype, int64_t M, int64_t N, 
     return p.split_bytes + p.bin_bytes;
   }
   return hxq::bwdx_workspace_bytes((int)M, (int)N, (int)K);
+}
+
+int hxq_linear_bwd_x_grouped(int fmt, const hxq_bwd_layer* layers, int count, int dy_dtype, float* dx, int64_t M,
+                             int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return backward_x_grouped(fmt, layers, count, dy_dtype, dx, M, K, workspace, workspace_bytes, stream);
+}
+
+int64_t hxq_linear_bwd_x_grouped_workspace(int fmt, int dy_dtype, const hxq_bwd_layer* layers, int count, int64_t M,
+                                           int64_t K) {
+  const int st = check_group(fmt, layers, count, dy_dtype);
+  if (st != HXQ_OK) return st;
+  if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return HXQ_ERR_SHAPE;
+  if (fmt == HXQ_FMT_PK12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
+  hxq_bwd_layer act[HXQ_MAX_GROUP];
+  int n = 0;
+  for (int i = 0; i < count; ++i) {
+    const hxq_bwd_layer& l = layers[i];
+    if (l.N < 0 || l.N > kMaxDim || l.nnz < 0 || l.nnz > kMaxDim) return HXQ_ERR_SHAPE;
+    if (l.N > 0) act[n++] = l;
+  }
+  if (M == 0 || K == 0 || n == 0) return 0;
+  if (n == 1) return hxq_linear_bwd_x_workspace(fmt, dy_dtype, M, act[0].N, K, act[0].nnz);
+  return plan_group(fmt == HXQ_FMT_PK12, dy_dtype == HXQ_BF16, act, n, M, K, nullptr, true).bytes;
 }
 
 int hxq_linear_bwd_x_ex(int fmt, const float* codebook, const uint8_t* indices, const int32_t* sc_rows,

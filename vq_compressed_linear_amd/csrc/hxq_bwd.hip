@@ -140,11 +140,17 @@ __global__ __launch_bounds__(bx::THREADS) void bwdx_valu(BwdArgs ba) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int M = ba.M, N = ba.N, K = ba.K;
   const int b = blockIdx.x;
   const int ct = b % ba.CT, rest = b / ba.CT, s = rest % ba.S, mt = rest / ba.S;
+  // the layer of split s (one layer unless the call is grouped)
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSegments; ++i)
+    if (i < ba.nseg && s >= ba.seg[i].split0) si = i;
+  const BwdSeg& sg = ba.seg[si];
+  const int M = ba.M, N = sg.N, K = ba.K;
   const int c0 = ct * CW, m0 = mt * MT;
-  const int n_lo = s * ba.R, n_hi = min(N, n_lo + ba.R);
+  const int n_lo = (s - sg.split0) * sg.R, n_hi = min(N, n_lo + sg.R);
   const int rw = wave * (64 / LPR) + lane / LPR;  // the lane's row position
   const int cl = c0 + 8 * (lane % LPR);            // the lane's first column
   const uint32_t lane4 = (uint32_t)lane << 2;
@@ -156,9 +162,9 @@ __global__ __launch_bounds__(bx::THREADS) void bwdx_valu(BwdArgs ba) {
   if (VEC) {
     // lanes past the last column read column 0 (never stored)
     const int q = cl < K ? cl >> 3 : 0;
-    il.base = ba.indices + (PK12 ? (int64_t)(6 * q - 2 * (q & 1)) : (int64_t)(cl < K ? cl : 0));
+    il.base = sg.indices + (PK12 ? (int64_t)(6 * q - 2 * (q & 1)) : (int64_t)(cl < K ? cl : 0));
   } else {
-    il.base = ba.indices;
+    il.base = sg.indices;
   }
   const bool odd = (cl >> 3) & 1;
 
@@ -176,23 +182,23 @@ __global__ __launch_bounds__(bx::THREADS) void bwdx_valu(BwdArgs ba) {
 #pragma unroll
     for (int v = 0; v < DYV; ++v) {
       const int e = tid + THREADS * v, i = e / MT, m = e % MT;
-      dyv[v] = (i < rc && m0 + m < M) ? load_dy<DYBF>(ba.dy, (int64_t)(m0 + m) * N + r0 + i) : 0.f;
+      dyv[v] = (i < rc && m0 + m < M) ? load_dy<DYBF>(sg.dy, (int64_t)(m0 + m) * N + r0 + i) : 0.f;
     }
   };
   load_chunk();
   WindowProbe probe;
   const int target = wave == 0 ? n_lo : n_hi;
-  if (ba.nnz > 0 && wave < 2)
-    window_issue(probe, ba.sc_rows, ba.nnz, (int64_t)((double)ba.nnz * (double)target / (double)N));
+  if (sg.nnz > 0 && wave < 2)
+    window_issue(probe, sg.sc_rows, sg.nnz, (int64_t)((double)sg.nnz * (double)target / (double)N));
   if (PK12) {
     // (4-byte loads: the codebook is only required to be 4-byte aligned)
 #pragma unroll
     for (int i = 0; i < 8192 / THREADS; ++i) {
       const int e = tid + THREADS * i;
-      reinterpret_cast<float*>(cbs)[e] = ba.codebook[e];
+      reinterpret_cast<float*>(cbs)[e] = sg.codebook[e];
     }
   } else {
-    const float v = ba.codebook[tid];
+    const float v = sg.codebook[tid];
     const float4 v4 = make_float4(v, v, v, v);
 #pragma unroll
     for (int q = 0; q < 16; ++q) *reinterpret_cast<float4*>(cbs + tid * 256 + (((q + tid) & 15) << 4)) = v4;
@@ -206,8 +212,8 @@ __global__ __launch_bounds__(bx::THREADS) void bwdx_valu(BwdArgs ba) {
 
   // the run's triplets: resolved before the first barrier, then loaded (up
   // to SCQ per thread) while the rows are processed
-  if (ba.nnz > 0 && wave < 2) {
-    const int64_t v = window_resolve(probe, ba.sc_rows, ba.nnz, target);
+  if (sg.nnz > 0 && wave < 2) {
+    const int64_t v = window_resolve(probe, sg.sc_rows, sg.nnz, target);
     if (lane == 0) lohi[wave] = v;
   }
   int64_t lo = 0, hi = 0;
@@ -221,15 +227,15 @@ __global__ __launch_bounds__(bx::THREADS) void bwdx_valu(BwdArgs ba) {
       if (e < RPAD * MT) dys[e] = dyv[v];
     }
     __syncthreads();
-    if (first && ba.nnz > 0) {
+    if (first && sg.nnz > 0) {
       lo = lohi[0];
       hi = lohi[1];
 #pragma unroll
       for (int q = 0; q < SCQ; ++q) {
-        const int64_t e = min(lo + tid + THREADS * q, ba.nnz - 1);
-        tr[q] = ba.sc_rows[e];
-        tc[q] = ba.sc_cols[e];
-        td[q] = ba.sc_deltas[e];
+        const int64_t e = min(lo + tid + THREADS * q, sg.nnz - 1);
+        tr[q] = sg.sc_rows[e];
+        tc[q] = sg.sc_cols[e];
+        td[q] = sg.sc_deltas[e];
       }
     }
     first = false;
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(bx::THREADS) void bwdx_valu(BwdArgs ba) {
 
   // ---- sidecar terms of the run's triplets in these columns (LDS atomics):
   // the prefetched ones first, dy from LDS when the run was one chunk
-  if (ba.nnz > 0) {
+  if (sg.nnz > 0) {
     const bool one_chunk = n_hi - n_lo <= RC;
 #pragma unroll
     for (int q = 0; q < SCQ; ++q) {
@@ -318,26 +324,26 @@ __global__ __launch_bounds__(bx::THREADS) void bwdx_valu(BwdArgs ba) {
         for (int m = 0; m < MT; ++m)
           if (m0 + m < M) {
             const float g = one_chunk ? dys[(tr[q] - n_lo) * MT + m]
-                                      : load_dy<DYBF>(ba.dy, (int64_t)(m0 + m) * N + tr[q]);
+                                      : load_dy<DYBF>(sg.dy, (int64_t)(m0 + m) * N + tr[q]);
             atomicAdd(&red[m * CW + (tc[q] - c0)], td[q] * g);
           }
       }
     }
     for (int64_t e = lo + tid + THREADS * SCQ; e < hi; e += THREADS) {
-      const int c = ba.sc_cols[e];
+      const int c = sg.sc_cols[e];
       if (c >= c0 && c < c0 + CW) {
-        const int r = ba.sc_rows[e];
-        const float d = ba.sc_deltas[e];
+        const int r = sg.sc_rows[e];
+        const float d = sg.sc_deltas[e];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          if (m0 + m < M) atomicAdd(&red[m * CW + (c - c0)], d * load_dy<DYBF>(ba.dy, (int64_t)(m0 + m) * N + r));
+          if (m0 + m < M) atomicAdd(&red[m * CW + (c - c0)], d * load_dy<DYBF>(sg.dy, (int64_t)(m0 + m) * N + r));
       }
     }
     __syncthreads();
   }
 
   // ---- store: into dx when the rows are not split, else into split s of
-  // the workspace
+  // the workspace (in a grouped call the splits of all layers)
   float* out = ba.S > 1 ? ba.ws + (int64_t)s * M * K : ba.dx;
   for (int e = tid; e < MT * CW; e += THREADS) {
     const int m = e / CW, col = e % CW;
@@ -411,10 +417,12 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-bool bwdx_vec_ok(const BwdArgs& a, bool pk12) {
-  const uintptr_t ip = reinterpret_cast<uintptr_t>(a.indices);
-  return pk12 ? (a.K % 16 == 0 && ip % 4 == 0) : (a.K % 8 == 0 && ip % 8 == 0);
+static bool vec_ok(const uint8_t* indices, int K, bool pk12) {
+  const uintptr_t ip = reinterpret_cast<uintptr_t>(indices);
+  return pk12 ? (K % 16 == 0 && ip % 4 == 0) : (K % 8 == 0 && ip % 8 == 0);
 }
+
+bool bwdx_vec_ok(const BwdArgs& a, bool pk12) { return vec_ok(a.indices, a.K, pk12); }
 
 template <bool PK12, bool DYBF, bool VEC, int LPR>
 static hipError_t launch_bx(const BwdArgs& a, int mt, dim3 grid, hipStream_t stream) {
@@ -456,7 +464,7 @@ BwdPlan bwdx_plan(int M, int N, int K) {
   const int group_rows = bx::WAVES * (64 / p.lpr) * (p.mt >= 8 ? 4 : 8);
   if (N <= 2 * group_rows) smax = 1;
   if (S > smax) S = smax;
-  if (S > 64) S = 64;  // the reduction kernel sums at most 64 splits
+  if (S > 64) S = 64;  // at most 64 splits (each M K floats of workspace)
   if (S < 1) S = 1;
   p.S = (int)S;
   return p;
@@ -471,6 +479,18 @@ int64_t bwdx_workspace_bytes(int M, int N, int K) {
 // One launch of the main kernel, then the reduction over the row splits when
 // there are several (their partial sums go to the workspace; a workspace too
 // small for the planned splits gets fewer).
+static hipError_t launch_bx_any(const BwdArgs& a, const BwdPlan& p, bool pk12, bool vec, int64_t S,
+                                hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.ct * p.mtiles * S;
+  if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks);
+  if (pk12)
+    return a.dy_bf16 ? launch_bx_v<true, true>(a, p.mt, vec, p.lpr, grid, stream)
+                     : launch_bx_v<true, false>(a, p.mt, vec, p.lpr, grid, stream);
+  return a.dy_bf16 ? launch_bx_v<false, true>(a, p.mt, vec, p.lpr, grid, stream)
+                   : launch_bx_v<false, false>(a, p.mt, vec, p.lpr, grid, stream);
+}
+
 hipError_t launch_bwdx_valu(const BwdArgs& a0, bool pk12, hipStream_t stream) {
   BwdArgs a = a0;
   const BwdPlan p = bwdx_plan(a.M, a.N, a.K);
@@ -484,19 +504,53 @@ hipError_t launch_bwdx_valu(const BwdArgs& a0, bool pk12, hipStream_t stream) {
   a.CT = p.ct;
   a.S = (int)S;
   a.R = (int)R;
-  const int64_t blocks = (int64_t)p.ct * p.mtiles * S;
-  if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
-  const bool vec = bwdx_vec_ok(a, pk12);
-  const dim3 grid((unsigned)blocks);
-  hipError_t e;
-  if (pk12)
-    e = a.dy_bf16 ? launch_bx_v<true, true>(a, p.mt, vec, p.lpr, grid, stream)
-                  : launch_bx_v<true, false>(a, p.mt, vec, p.lpr, grid, stream);
-  else
-    e = a.dy_bf16 ? launch_bx_v<false, true>(a, p.mt, vec, p.lpr, grid, stream)
-                  : launch_bx_v<false, false>(a, p.mt, vec, p.lpr, grid, stream);
+  a.nseg = 1;
+  a.seg[0] = {a.codebook, a.indices, a.sc_rows, a.sc_cols, a.sc_deltas, a.nnz, a.dy, a.N, 0, (int)R};
+  const hipError_t e = launch_bx_any(a, p, pk12, bwdx_vec_ok(a, pk12), S, stream);
   if (e != hipSuccess || S == 1) return e;
   return launch_bwdx_reduce(a.ws, a.dx, (int64_t)a.M * a.K, (int)S, stream);
+}
+
+// Every layer is split into runs of one length R, chosen as for a single
+// layer of all the group's rows (so a group of small layers still fills the
+// GPU); a run never crosses into the next layer.  Ns[i] > 0.
+BwdGroupPlan bwdx_group_plan(int M, const int* Ns, int nseg, int K) {
+  BwdGroupPlan g;
+  int64_t total = 0;
+  for (int i = 0; i < nseg; ++i) total += Ns[i];
+  g.p = bwdx_plan(M, (int)total, K);
+  g.R = (int)((total + g.p.S - 1) / g.p.S);
+  g.slots_total = 0;
+  for (int i = 0; i < nseg; ++i) {
+    g.S[i] = (Ns[i] + g.R - 1) / g.R;
+    g.slots_total += g.S[i];
+  }
+  return g;
+}
+
+// One launch over the layers in a.seg (their fields set by the caller, split0
+// and R set here), then the sum of all their splits into dx.  a.ws holds the
+// plan's slots.
+hipError_t launch_bwdx_valu_grouped(const BwdArgs& a0, bool pk12, hipStream_t stream) {
+  BwdArgs a = a0;
+  int Ns[kMaxSegments];
+  for (int i = 0; i < a.nseg; ++i) Ns[i] = a.seg[i].N;
+  const BwdGroupPlan g = bwdx_group_plan(a.M, Ns, a.nseg, a.K);
+  if (a.ws == nullptr || a.ws_bytes < (int64_t)g.slots_total * a.M * a.K * 4) return hipErrorInvalidValue;
+  bool vec = true;
+  int split0 = 0;
+  for (int i = 0; i < a.nseg; ++i) {
+    vec = vec && vec_ok(a.seg[i].indices, a.K, pk12);
+    a.seg[i].split0 = split0;
+    a.seg[i].R = g.R;
+    split0 += g.S[i];
+  }
+  a.CT = g.p.ct;
+  a.S = g.slots_total;
+  a.R = g.R;
+  const hipError_t e = launch_bx_any(a, g.p, pk12, vec, g.slots_total, stream);
+  if (e != hipSuccess) return e;
+  return launch_bwdx_reduce(a.ws, a.dx, (int64_t)a.M * a.K, g.slots_total, stream);
 }
 
 hipError_t launch_bwdx_reduce(const float* ws, float* dx, int64_t n, int S, hipStream_t stream) {
@@ -504,7 +558,7 @@ hipError_t launch_bwdx_reduce(const float* ws, float* dx, int64_t n, int S, hipS
   const bool vec = n % 4 == 0 && reinterpret_cast<uintptr_t>(dx) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(ws) % 16 == 0 && n / 1024 >= device_cu_count();
   const int64_t rb = (n + (vec ? 1023 : 255)) / (vec ? 1024 : 256);
-  if (rb > INT_MAX || S > 64) return hipErrorInvalidConfiguration;
+  if (rb > INT_MAX || S < 1 || S > 1024) return hipErrorInvalidConfiguration;
   if (vec)
     hipLaunchKernelGGL(bwdx_reduce<true>, dim3((unsigned)rb), dim3(256), 0, stream, ws, dx, n, S);
   else

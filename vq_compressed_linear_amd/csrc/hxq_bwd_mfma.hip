@@ -481,7 +481,7 @@ BwdMPlan bwdx_mfma_plan(int M, int N, int K, int64_t nnz) {
   int64_t S = (cus + tiles - 1) / tiles;
   const int64_t smax = N / 256 > 0 ? N / 256 : 1;  // at least 8 steps per split
   if (S > smax) S = smax;
-  if (S > 64) S = 64;  // the reduction kernel sums at most 64 splits
+  if (S > 64) S = 64;  // at most 64 splits (each M K floats of workspace)
   const int64_t smin = (N / bm::STEP + bm::MAXST - 1) / bm::MAXST;  // bin starts of a split fit LDS
   if (S < smin) S = smin;
   if (S < 1) S = 1;
@@ -496,16 +496,20 @@ BwdMPlan bwdx_mfma_plan(int M, int N, int K, int64_t nnz) {
   return p;
 }
 
+// a.slots set (grouped calls): the splits go to slots a.slot0 .. + S - 1 and
+// are not summed here; the workspace then holds only the sidecar bins.
 hipError_t launch_bwdx_mfma(const BwdArgs& a, bool pk12, hipStream_t stream) {
   const BwdMPlan p = bwdx_mfma_plan(a.M, a.N, a.K, a.nnz);
-  if (a.ws_bytes < p.split_bytes + p.bin_bytes || (p.split_bytes + p.bin_bytes > 0 && a.ws == nullptr))
+  const bool grouped = a.slots != nullptr;
+  const int64_t split_bytes = grouped ? 0 : p.split_bytes;
+  if (a.ws_bytes < split_bytes + p.bin_bytes || (split_bytes + p.bin_bytes > 0 && a.ws == nullptr))
     return hipErrorInvalidValue;
   unsigned char* w = reinterpret_cast<unsigned char*>(a.ws);
   BwdMArgs m = {};
   m.codebook = a.codebook;
   m.indices = a.indices;
   m.dy = static_cast<const uint16_t*>(a.dy);
-  m.out = p.S > 1 ? reinterpret_cast<float*>(w) : a.dx;
+  m.out = grouped ? a.slots + (int64_t)a.slot0 * a.M * a.K : p.S > 1 ? reinterpret_cast<float*>(w) : a.dx;
   m.M = a.M;
   m.N = a.N;
   m.K = a.K;
@@ -518,7 +522,7 @@ hipError_t launch_bwdx_mfma(const BwdArgs& a, bool pk12, hipStream_t stream) {
   if (a.nnz > 0) {
     const int nsteps = a.N / bm::STEP;
     auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
-    unsigned char* q = w + p.split_bytes;
+    unsigned char* q = w + split_bytes;
     int* binstart = reinterpret_cast<int*>(q);
     q += al((int64_t)nsteps * (p.CT + 1) * 4);
     uint32_t* bpat = reinterpret_cast<uint32_t*>(q);
@@ -540,7 +544,7 @@ hipError_t launch_bwdx_mfma(const BwdArgs& a, bool pk12, hipStream_t stream) {
   else
     hipLaunchKernelGGL(bwdx_mfma<false>, dim3((unsigned)blocks), dim3(bm::THREADS), 0, stream, m);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.S == 1) return e;
+  if (e != hipSuccess || p.S == 1 || grouped) return e;
   return launch_bwdx_reduce(m.out, a.dx, (int64_t)a.M * a.K, p.S, stream);
 }
 

@@ -176,6 +176,19 @@ hipError_t launch_sidecar_add(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream);
 
 // ---- input gradient dx = dy W (hxq_bwd.hip, hxq_bwd_mfma.hip)
+// One layer of a vector-kernel launch: its rows split into runs of R rows,
+// the first of them split `split0` of the launch.
+struct BwdSeg {
+  const float* codebook;
+  const uint8_t* indices;
+  const int32_t* sc_rows;
+  const int32_t* sc_cols;
+  const float* sc_deltas;
+  int64_t nnz;
+  const void* dy;            // [M][N] fp32 or bf16 bits
+  int N, split0, R;
+};
+
 struct BwdArgs {
   const float* codebook;     // u8: float[256]; pk12: float[4096][2]
   const uint8_t* indices;    // u8: [N][K]; pk12: [N][3*ceil(K/4)]
@@ -190,6 +203,14 @@ struct BwdArgs {
   float* ws;                 // workspace for the partial sums of row splits, or nullptr
   int64_t ws_bytes;
   int CT, S, R;              // set by the launcher: column tiles, row splits, rows per split
+  // grouped calls (dx = the sum over layers of dy_i W_i): the matrix-core
+  // launcher writes this layer's splits into slots + slot0 (M K floats each)
+  // and leaves the sum to the caller; the vector kernel reads its layers
+  // from seg (nseg of them; the launcher fills seg[0] for one layer)
+  float* slots;
+  int slot0;
+  int nseg;
+  BwdSeg seg[kMaxSegments];
 };
 
 struct BwdPlan {
@@ -201,6 +222,16 @@ bool bwdx_vec_ok(const BwdArgs& a, bool pk12);
 BwdPlan bwdx_plan(int M, int N, int K);
 int64_t bwdx_workspace_bytes(int M, int N, int K);
 hipError_t launch_bwdx_valu(const BwdArgs& a, bool pk12, hipStream_t stream);
+// Several layers sharing dy's tokens and K: dx = sum_i dy_i W_i.  The group
+// plan splits every layer into runs of one common length; slots_total is the
+// number of partial sums (M K floats each) the workspace must hold.
+struct BwdGroupPlan {
+  BwdPlan p;
+  int R, slots_total;
+  int S[kMaxSegments];
+};
+BwdGroupPlan bwdx_group_plan(int M, const int* Ns, int nseg, int K);
+hipError_t launch_bwdx_valu_grouped(const BwdArgs& a, bool pk12, hipStream_t stream);
 hipError_t launch_bwdx_reduce(const float* ws, float* dx, int64_t n, int S, hipStream_t stream);
 
 struct BwdMPlan {
