@@ -327,12 +327,14 @@ int64_t hxq_linear_bwd_x_grouped_workspace(int fmt, int dy_dtype, const hxq_bwd_
                                            int count, int64_t M, int64_t K);
 
 /* The same with the kernel family forced: HXQ_VARIANT_AUTO;
- * HXQ_VARIANT_GEMV_VALU, the vector-FMA kernel (any shape); or
- * HXQ_VARIANT_GEMM_BF16, the bf16 matrix-core kernel (bf16 dy, N % 32 == 0,
- * K % 128 == 0, K <= 16384, dy and dx 16-byte and indices 8-byte (u8) or
- * 4-byte (pk12) aligned, and the workspace the query gives), which returns
- * HXQ_ERR_UNSUPPORTED when it cannot take the call; any other value returns
- * HXQ_ERR_UNSUPPORTED. */
+ * HXQ_VARIANT_GEMV_VALU, the vector-FMA kernel (any shape);
+ * HXQ_VARIANT_GEMM_BF16, the 64-token bf16 matrix-core kernel (bf16 dy,
+ * N % 32 == 0, K % 128 == 0, K <= 16384, dy and dx 16-byte and indices
+ * 8-byte (u8) or 4-byte (pk12) aligned, and the workspace the query gives);
+ * or HXQ_VARIANT_GEMM_BF16_T256, the 256 x 256 tile bf16 matrix-core kernel
+ * (u8 only; the same shapes, indices 4-byte aligned), which AUTO takes from
+ * 128 tokens.  A forced kernel that cannot take the call returns
+ * HXQ_ERR_UNSUPPORTED; any other value returns HXQ_ERR_UNSUPPORTED. */
 int hxq_linear_bwd_x_ex(int fmt, const float* codebook, const uint8_t* indices,
                         const int32_t* sc_rows, const int32_t* sc_cols,
                         const float* sc_deltas, int64_t nnz,

@@ -9,7 +9,7 @@ stores) and the empty cases.  Tolerance: 1e-5 * (|dY| |W|) for the fp32 path,
 8e-3 * (|dY| |W|) for the bf16 matrix-core kernel (bf16 dy from 16 tokens),
 which is also run forced on its own shapes: the MLP widths, K not a multiple
 of its 512-column workgroup tile, token tails, the smallest and largest K, and
-sidecar bins longer than a wave.
+sidecar bins longer than a wave; likewise the 256 x 256 tile kernel (u8).
 """
 
 import numpy as np
@@ -236,6 +236,63 @@ def test_bwd_x_mfma_needs_its_workspace():
     with pytest.raises(hx.HxqError):
         hx.hxq_linear_bwd_x(hx.HXQ_FMT_U8, d["codebook"], d["indices"], d["rows"], d["cols"], d["deltas"], dy, dx,
                             K, variant=hx.HXQ_VARIANT_GEMM_BF16, workspace=t.zeros(4, dtype=t.uint8, device="cuda"))
+
+
+G5_CASES = [
+    # (N, K, M) on the 256 x 256 tile kernel (u8): row splits, token tails,
+    # K with a half-empty last column tile, one and three stages, the
+    # narrowest and widest K
+    (2048, 2048, 256),
+    (11008, 2048, 300),
+    (2048, 11008, 200),
+    (32, 384, 17),
+    (96, 1152, 520),
+    (4096, 128, 64),
+    (64, 16384, 130),
+]
+
+
+@pytest.mark.parametrize("N,K,M", G5_CASES)
+def test_bwd_x_g5_matches_oracle(N, K, M):
+    G.say("bwd_x g5 N=%d K=%d M=%d" % (N, K, M))
+    lay = gen.random_layer(9000 + N + 3 * K + 7 * M, N, K, "u8", nnz=max(1, N * K // 1000), duplicates=True)
+    d = G.dev_layer(lay)
+    dy_np = _dy(9500 + N + K + M, M, N, "bf16")
+    dx = _run(lay, d, G.dev_x(dy_np, "bf16"), variant=hx.HXQ_VARIANT_GEMM_BF16_T256)
+    G.torch().cuda.synchronize()
+    Y, B = _oracle(lay, dy_np, "bf16")
+    G.check(dx, Y, B, G.TOL_BF16, "bwd_x g5 N=%d K=%d M=%d" % (N, K, M))
+
+
+def test_bwd_x_g5_dense_sidecar_and_repeats():
+    # bins of several hundred patch words (past the 64 a wave reads at once)
+    # with repeated coordinates, rows in every stage; the same layer without
+    # its sidecar; and, without it, the same bits on a second call
+    t = G.torch()
+    N, K, M = 96, 1024, 256
+    G.say("bwd_x g5 dense sidecar")
+    lay = gen.random_layer(111, N, K, "u8", nnz=N * K // 8, duplicates=True)
+    d = G.dev_layer(lay)
+    dy_np = _dy(112, M, N, "bf16")
+    dyd = G.dev_x(dy_np, "bf16")
+    for sidecar in (True, False):
+        dx = _run(lay, d, dyd, sidecar=sidecar, variant=hx.HXQ_VARIANT_GEMM_BF16_T256)
+        Y, B = _oracle(lay, dy_np, "bf16", sidecar=sidecar)
+        G.check(dx, Y, B, G.TOL_BF16, "bwd_x g5 dense sidecar=%s" % sidecar)
+    again = _run(lay, d, dyd, sidecar=False, variant=hx.HXQ_VARIANT_GEMM_BF16_T256)
+    assert t.equal(dx, again)
+
+
+def test_bwd_x_g5_rejects_pk12():
+    t = G.torch()
+    N, K, M = 256, 512, 256
+    lay = gen.random_layer(113, N, K, "pk12", nnz=100)
+    d = G.dev_layer(lay)
+    dy = G.dev_x(_dy(114, M, N, "bf16"), "bf16")
+    dx = t.zeros((M, K), dtype=t.float32, device="cuda")
+    with pytest.raises(hx.HxqError):
+        hx.hxq_linear_bwd_x(hx.HXQ_FMT_PK12, d["codebook"], d["indices"], d["rows"], d["cols"], d["deltas"], dy,
+                            dx, K, variant=hx.HXQ_VARIANT_GEMM_BF16_T256)
 
 
 @pytest.mark.parametrize("fmt", ["u8", "pk12"])

@@ -24,7 +24,7 @@ OUT = os.path.join(HERE, "libhxq.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["hxq_gemv.hip", "hxq_gemv_mfma.hip", "hxq_gemv_mfma4.hip", "hxq_dequant.hip", "hxq_decode.hip", "hxq_decode1.hip", "hxq_gemm.hip", "hxq_gemm5.hip", "hxq_bwd.hip", "hxq_bwd_mfma.hip", "hxq_api.cpp"]
+SOURCES = ["hxq_gemv.hip", "hxq_gemv_mfma.hip", "hxq_gemv_mfma4.hip", "hxq_dequant.hip", "hxq_decode.hip", "hxq_decode1.hip", "hxq_gemm.hip", "hxq_gemm5.hip", "hxq_bwd.hip", "hxq_bwd_mfma.hip", "hxq_bwd_g5.hip", "hxq_api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

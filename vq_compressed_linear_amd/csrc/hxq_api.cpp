@@ -17,6 +17,7 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)INT32_MAX - 65536;  // room for tile rounding in int32
 constexpr int64_t kBwdMfmaMinM = 16;                       // input gradient: matrix cores from here
+constexpr int64_t kBwdG5MinM = 128;                        // and the 256 x 256 tile kernel (u8) from here
 
 bool misaligned(const void* p, uintptr_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
@@ -137,7 +138,8 @@ int validate_bwd(int fmt, const float* codebook, const uint8_t* indices, const i
   if (M < 0 || N < 0 || K < 0 || nnz < 0 || workspace_bytes < 0) return HXQ_ERR_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim || nnz > kMaxDim) return HXQ_ERR_SHAPE;
   if (pk12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
-  if (variant != HXQ_VARIANT_AUTO && variant != HXQ_VARIANT_GEMV_VALU && variant != HXQ_VARIANT_GEMM_BF16)
+  if (variant != HXQ_VARIANT_AUTO && variant != HXQ_VARIANT_GEMV_VALU && variant != HXQ_VARIANT_GEMM_BF16 &&
+      variant != HXQ_VARIANT_GEMM_BF16_T256)
     return HXQ_ERR_UNSUPPORTED;
   if (M == 0 || K == 0) return HXQ_OK;
   if (!dx) return HXQ_ERR_NULL;
@@ -176,18 +178,35 @@ int backward_x(int fmt, const float* codebook, const uint8_t* indices, const int
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
-  // the bf16 matrix-core kernel past 16 tokens, when the shape, the pointers
-  // and the workspace (row splits and sidecar bins) allow it
-  bool mfma = hxq::bwdx_mfma_ok(a, pk12);
-  if (mfma) {
-    const hxq::BwdMPlan p = hxq::bwdx_mfma_plan(a.M, a.N, a.K, nnz);
+  // the bf16 matrix-core kernels past 16 tokens (256 x 256 tiles from 128
+  // tokens, u8), when the shape, the pointers and the workspace (row splits
+  // and sidecar bins) allow them
+  auto fits = [&](const hxq::BwdMPlan& p) {
     const int64_t need = p.split_bytes + p.bin_bytes;
-    mfma = need == 0 || (workspace && workspace_bytes >= need);
+    return need == 0 || (workspace && workspace_bytes >= need);
+  };
+  const bool g5 = hxq::bwdx_g5_ok(a, pk12) && fits(hxq::bwdx_g5_plan(a.M, a.N, a.K, nnz));
+  const bool mfma = hxq::bwdx_mfma_ok(a, pk12) && fits(hxq::bwdx_mfma_plan(a.M, a.N, a.K, nnz));
+  if (variant == HXQ_VARIANT_GEMM_BF16_T256)
+    return g5 ? status_of(hxq::launch_bwdx_g5(a, stream)) : HXQ_ERR_UNSUPPORTED;
+  if (variant == HXQ_VARIANT_GEMM_BF16)
+    return mfma ? status_of(hxq::launch_bwdx_mfma(a, pk12, stream)) : HXQ_ERR_UNSUPPORTED;
+  if (variant == HXQ_VARIANT_AUTO && M >= kBwdMfmaMinM) {
+    if (g5 && M >= kBwdG5MinM) return status_of(hxq::launch_bwdx_g5(a, stream));
+    if (mfma) return status_of(hxq::launch_bwdx_mfma(a, pk12, stream));
   }
-  if (variant == HXQ_VARIANT_GEMM_BF16 && !mfma) return HXQ_ERR_UNSUPPORTED;
-  if (variant == HXQ_VARIANT_GEMM_BF16 || (variant == HXQ_VARIANT_AUTO && mfma && M >= kBwdMfmaMinM))
-    return status_of(hxq::launch_bwdx_mfma(a, pk12, stream));
   return status_of(hxq::launch_bwdx_valu(a, pk12, stream));
+}
+
+// The matrix-core kernel AUTO runs for one layer from kBwdMfmaMinM tokens
+// (0: none takes it): 2 = 256 x 256 tiles, 1 = the 64-token kernel.
+int bwd_mm_kernel(const hxq::BwdArgs& a, bool pk12) {
+  if (a.M >= kBwdG5MinM && hxq::bwdx_g5_ok(a, pk12)) return 2;
+  return hxq::bwdx_mfma_ok(a, pk12) ? 1 : 0;
+}
+
+hxq::BwdMPlan bwd_mm_plan(int kernel, const hxq::BwdArgs& a) {
+  return kernel == 2 ? hxq::bwdx_g5_plan(a.M, a.N, a.K, a.nnz) : hxq::bwdx_mfma_plan(a.M, a.N, a.K, a.nnz);
 }
 
 // ---- grouped input gradient: dx = sum over layers of dy_i W_i
@@ -216,7 +235,8 @@ hxq::BwdArgs bwd_args_of(const hxq_bwd_layer& l, bool dy_bf16, float* dx, int64_
 // pointers (the workspace query) instead of the layers' own.
 struct BwdGroupWs {
   bool mfma;
-  int64_t bin_bytes;  // a multiple of 256: the split slots follow
+  int kernel[HXQ_MAX_GROUP];  // per layer, with matrix cores: as bwd_mm_kernel
+  int64_t bin_bytes;          // a multiple of 256: the split slots follow
   int slots;
   int64_t bytes;
 };
@@ -225,6 +245,7 @@ BwdGroupWs plan_group(bool pk12, bool dy_bf16, const hxq_bwd_layer* act, int n, 
                       bool aligned) {
   const int64_t per = M * K * 4;
   bool mfma = dy_bf16 && M >= kBwdMfmaMinM;
+  BwdGroupWs w = {};
   for (int i = 0; i < n && mfma; ++i) {
     hxq::BwdArgs a = bwd_args_of(act[i], dy_bf16, dx, M, K);
     if (aligned) {
@@ -232,13 +253,13 @@ BwdGroupWs plan_group(bool pk12, bool dy_bf16, const hxq_bwd_layer* act, int n, 
       a.dy = reinterpret_cast<const void*>(uintptr_t(256));
       a.dx = reinterpret_cast<float*>(uintptr_t(256));
     }
-    mfma = hxq::bwdx_mfma_ok(a, pk12);
+    w.kernel[i] = bwd_mm_kernel(a, pk12);
+    mfma = w.kernel[i] != 0;
   }
-  BwdGroupWs w = {};
   w.mfma = mfma;
   if (mfma) {
     for (int i = 0; i < n; ++i) {
-      const hxq::BwdMPlan p = hxq::bwdx_mfma_plan((int)M, (int)act[i].N, (int)K, act[i].nnz);
+      const hxq::BwdMPlan p = bwd_mm_plan(w.kernel[i], bwd_args_of(act[i], dy_bf16, dx, M, K));
       w.bin_bytes = std::max(w.bin_bytes, p.bin_bytes);
       w.slots += p.S;
     }
@@ -298,9 +319,9 @@ int backward_x_grouped(int fmt, const hxq_bwd_layer* layers, int count, int dy_d
       a.ws_bytes = w.bin_bytes;
       a.slots = slots;
       a.slot0 = slot0;
-      const hipError_t e = hxq::launch_bwdx_mfma(a, pk12, stream);
+      const hipError_t e = w.kernel[i] == 2 ? hxq::launch_bwdx_g5(a, stream) : hxq::launch_bwdx_mfma(a, pk12, stream);
       if (e != hipSuccess) return status_of(e);
-      slot0 += hxq::bwdx_mfma_plan(a.M, a.N, a.K, a.nnz).S;
+      slot0 += bwd_mm_plan(w.kernel[i], a).S;
     }
     return status_of(hxq::launch_bwdx_reduce(slots, dx, M * K, slot0, stream));
   }
@@ -393,8 +414,10 @@ int64_t hxq_linear_bwd_x_workspace(int fmt, int dy_dtype, int64_t M, int64_t N, 
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
-  if (M >= kBwdMfmaMinM && hxq::bwdx_mfma_ok(a, fmt == HXQ_FMT_PK12)) {
-    const hxq::BwdMPlan p = hxq::bwdx_mfma_plan(a.M, a.N, a.K, nnz);
+  a.nnz = nnz;
+  const int kernel = M >= kBwdMfmaMinM ? bwd_mm_kernel(a, fmt == HXQ_FMT_PK12) : 0;
+  if (kernel != 0) {
+    const hxq::BwdMPlan p = bwd_mm_plan(kernel, a);
     return p.split_bytes + p.bin_bytes;
   }
   return hxq::bwdx_workspace_bytes((int)M, (int)N, (int)K);

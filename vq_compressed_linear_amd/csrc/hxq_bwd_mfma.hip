@@ -496,6 +496,17 @@ BwdMPlan bwdx_mfma_plan(int M, int N, int K, int64_t nnz) {
   return p;
 }
 
+hipError_t launch_bwdx_bin(const BwdArgs& a, bool pk12, int CT, int* binstart, uint32_t* bpat, hipStream_t stream) {
+  const int nsteps = a.N / bm::STEP;
+  if (pk12)
+    hipLaunchKernelGGL(bwdx_bin<true>, dim3((unsigned)nsteps), dim3(256), 0, stream, a.codebook, a.indices, a.sc_rows,
+                       a.sc_cols, a.sc_deltas, a.nnz, a.N, a.K, CT, binstart, bpat);
+  else
+    hipLaunchKernelGGL(bwdx_bin<false>, dim3((unsigned)nsteps), dim3(256), 0, stream, a.codebook, a.indices, a.sc_rows,
+                       a.sc_cols, a.sc_deltas, a.nnz, a.N, a.K, CT, binstart, bpat);
+  return hipGetLastError();
+}
+
 // a.slots set (grouped calls): the splits go to slots a.slot0 .. + S - 1 and
 // are not summed here; the workspace then holds only the sidecar bins.
 hipError_t launch_bwdx_mfma(const BwdArgs& a, bool pk12, hipStream_t stream) {
@@ -526,13 +537,7 @@ hipError_t launch_bwdx_mfma(const BwdArgs& a, bool pk12, hipStream_t stream) {
     int* binstart = reinterpret_cast<int*>(q);
     q += al((int64_t)nsteps * (p.CT + 1) * 4);
     uint32_t* bpat = reinterpret_cast<uint32_t*>(q);
-    if (pk12)
-      hipLaunchKernelGGL(bwdx_bin<true>, dim3((unsigned)nsteps), dim3(256), 0, stream, a.codebook, a.indices, a.sc_rows,
-                         a.sc_cols, a.sc_deltas, a.nnz, a.N, a.K, p.CT, binstart, bpat);
-    else
-      hipLaunchKernelGGL(bwdx_bin<false>, dim3((unsigned)nsteps), dim3(256), 0, stream, a.codebook, a.indices, a.sc_rows,
-                         a.sc_cols, a.sc_deltas, a.nnz, a.N, a.K, p.CT, binstart, bpat);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_bwdx_bin(a, pk12, p.CT, binstart, bpat, stream);
     if (e != hipSuccess) return e;
     m.binstart = binstart;
     m.bpat = bpat;

@@ -241,5 +241,26 @@ struct BwdMPlan {
 bool bwdx_mfma_ok(const BwdArgs& a, bool pk12);
 BwdMPlan bwdx_mfma_plan(int M, int N, int K, int64_t nnz);
 hipError_t launch_bwdx_mfma(const BwdArgs& a, bool pk12, hipStream_t stream);
+// The sidecar patch words of every 32-row step, binned by 128-column bin
+// (CT = K / 128 bins per step; binstart [N / 32][CT + 1], bpat [nnz]).
+hipError_t launch_bwdx_bin(const BwdArgs& a, bool pk12, int CT, int* binstart, uint32_t* bpat, hipStream_t stream);
+
+// 256-token x 256-column tiles (hxq_bwd_g5.hip), u8 only
+struct BwdG5Args {
+  const float* codebook;
+  const uint8_t* indices;
+  const uint16_t* dy;        // [M][N] bf16
+  float* out;                // dx, or the first of the slots split s stores into
+  int64_t slot_stride;       // floats between the splits' slots (0: one split into dx)
+  int M, N, K;
+  int tiles_m, tiles_k, R;   // token tiles, column tiles, rows per split
+  int CT;                    // sidecar bins per step (K / 128); 0 = no sidecar
+  int nnz;                   // patch words (at most the triplets)
+  const int* binstart;
+  const uint32_t* bpat;
+};
+bool bwdx_g5_ok(const BwdArgs& a, bool pk12);
+BwdMPlan bwdx_g5_plan(int M, int N, int K, int64_t nnz);
+hipError_t launch_bwdx_g5(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace hxq
