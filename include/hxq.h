@@ -258,7 +258,7 @@ int hxq_linear_bwd_x(int fmt, const float* codebook, const uint8_t* indices,
  *   device current (HXQ_ERR_HIP if that fails).
  * Errors: those of hxq_linear_bwd_x, and HXQ_ERR_SCRATCH (nothing launched)
  * when the workspace query exceeds HXQ_SCRATCH_BYTES. */
-#define HXQ_SCRATCH_BYTES (48 * 1024 * 1024)
+#define HXQ_SCRATCH_BYTES (96 * 1024 * 1024)
 
 int hxq_linear_bwd_x_noalloc(int fmt, const float* codebook, const uint8_t* indices,
                              const int32_t* sc_rows, const int32_t* sc_cols,

@@ -69,3 +69,10 @@ def test_noalloc_two_calls_second_smaller(fmt, dtype):
 def test_noalloc_one_token():
     _case("u8", 11008, 2048, 1, "f32", seed=13)
     _case("u8", 2048, 11008, 1, "f32", seed=14)
+
+
+def test_noalloc_256_tile_kernel():
+    # from 128 tokens (u8, bf16 dy) the 256 x 256 tile kernel: row splits and
+    # sidecar bins in the scratch, then a smaller call of the same kernel
+    _case("u8", 2048, 2048, 256, "bf16", seed=15)
+    _case("u8", 512, 1024, 128, "bf16", seed=16)

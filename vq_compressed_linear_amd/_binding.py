@@ -28,7 +28,7 @@ HXQ_ERR_ALIGN = -4
 HXQ_ERR_UNSUPPORTED = -5
 HXQ_ERR_HIP = -6
 HXQ_ERR_SCRATCH = -7
-HXQ_SCRATCH_BYTES = 48 * 1024 * 1024
+HXQ_SCRATCH_BYTES = 96 * 1024 * 1024
 
 HXQ_F32 = 0
 HXQ_BF16 = 1
