@@ -5,8 +5,10 @@ of each layer's fp64 dY_i @ W_i, with the bound the sum of the layers' bounds.
 Cases: the Qwen2.5-3B decode shapes (q|k|v, gate|up at one token), token
 tails, the byte-load path, a group with an empty layer, both kernel families
 (fp32 vector products; bf16 matrix cores from 16 tokens on shapes they
-take), a single active layer (the single-layer call, bitwise), repeat
-determinism without a sidecar, and a workspace that is too small.
+take, a launch per layer, or from 128 tokens (u8) one 256 x 256 tile
+launch for the whole group, also with a dense sidecar in one layer only),
+a single active layer (the single-layer call, bitwise), repeat determinism
+without a sidecar, and a workspace that is too small.
 Tolerances as for the single-layer input gradient.
 """
 
@@ -49,10 +51,10 @@ def _oracle_one(lay, dy_np, dtype, sidecar=True):
                                         lay.N, lay.K)
 
 
-def _group(fmt, Ns, K, M, dtype, seed):
+def _group(fmt, Ns, K, M, dtype, seed, den=1000):
     lays, devs, dys, dy_nps = [], [], [], []
     for i, N in enumerate(Ns):
-        lay = gen.random_layer(seed * 13 + i, N, K, fmt, nnz=max(1, N * K // 1000) if N else 0,
+        lay = gen.random_layer(seed * 13 + i, N, K, fmt, nnz=max(1, N * K // den) if N else 0,
                                duplicates=True)
         dy_np = _dy(seed * 17 + i, M, N, dtype)
         lays.append(lay)
@@ -96,8 +98,9 @@ CASES = [
     ([300, 97, 5], 522, 2),        # byte-load path, ragged column tile
     ([700, 300], 2048, 8),
     ([700, 300, 5], 1024, 37),
-    ([2048, 256, 256], 2048, 64),  # bf16: matrix cores
-    ([512, 1024], 1024, 300),
+    ([2048, 256, 256], 2048, 64),  # bf16: matrix cores, a launch per layer
+    ([512, 1024], 1024, 300),      # bf16 (u8): one 256 x 256 tile launch for both
+    ([2048, 256, 256], 2048, 256),
 ]
 
 
@@ -162,3 +165,17 @@ def test_bwd_x_grouped_needs_its_workspace():
                                     workspace=t.zeros(16, dtype=t.uint8, device="cuda"))
     t.cuda.synchronize()
     assert bool(t.isnan(dx).all())
+
+
+def test_bwd_x_grouped_256_tiles_dense_sidecar():
+    # one 256 x 256 tile launch for the group with stages of several hundred
+    # patch words in one layer and none in the other
+    K, M = 1024, 256
+    lays, devs, dys, dy_nps = _group("u8", [96, 128], K, M, "bf16", 36, den=8)
+    lays[1].rows = lays[1].rows[:0]
+    lays[1].cols = lays[1].cols[:0]
+    lays[1].deltas = lays[1].deltas[:0]
+    devs[1] = G.dev_layer(lays[1])
+    dx = _run("u8", devs, dys, M, K)
+    Y, B = _oracle(lays, dy_nps, "bf16", K)
+    G.check(dx, Y, B, G.TOL_BF16, "bwd_x grouped 256 tiles dense sidecar")

@@ -235,6 +235,7 @@ hxq::BwdArgs bwd_args_of(const hxq_bwd_layer& l, bool dy_bf16, float* dx, int64_
 // pointers (the workspace query) instead of the layers' own.
 struct BwdGroupWs {
   bool mfma;
+  bool g5group;               // every layer on the 256 x 256 tile kernel: one launch for all
   int kernel[HXQ_MAX_GROUP];  // per layer, with matrix cores: as bwd_mm_kernel
   int64_t bin_bytes;          // a multiple of 256: the split slots follow
   int slots;
@@ -257,7 +258,19 @@ BwdGroupWs plan_group(bool pk12, bool dy_bf16, const hxq_bwd_layer* act, int n, 
     mfma = w.kernel[i] != 0;
   }
   w.mfma = mfma;
-  if (mfma) {
+  w.g5group = mfma;
+  for (int i = 0; i < n && mfma; ++i) w.g5group = w.g5group && w.kernel[i] == 2;
+  if (w.g5group) {
+    int Ns[hxq::kMaxSegments];
+    int64_t nnzs[hxq::kMaxSegments];
+    for (int i = 0; i < n; ++i) {
+      Ns[i] = (int)act[i].N;
+      nnzs[i] = act[i].nnz;
+    }
+    const hxq::BwdG5Group g = hxq::bwdx_g5_group_plan((int)M, (int)K, Ns, nnzs, n);
+    w.bin_bytes = g.bin_total;
+    w.slots = g.slots;
+  } else if (mfma) {
     for (int i = 0; i < n; ++i) {
       const hxq::BwdMPlan p = bwd_mm_plan(w.kernel[i], bwd_args_of(act[i], dy_bf16, dx, M, K));
       w.bin_bytes = std::max(w.bin_bytes, p.bin_bytes);
@@ -310,6 +323,14 @@ int backward_x_grouped(int fmt, const hxq_bwd_layer* layers, int count, int dy_d
   if (workspace == nullptr || workspace_bytes < w.bytes) return HXQ_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   unsigned char* wb = static_cast<unsigned char*>(workspace);
+  if (w.g5group) {
+    hxq::BwdArgs ls[HXQ_MAX_GROUP];
+    for (int i = 0; i < n; ++i) ls[i] = bwd_args_of(act[i], dy_bf16, dx, M, K);
+    float* slots = reinterpret_cast<float*>(wb + w.bin_bytes);
+    const hipError_t e = hxq::launch_bwdx_g5_grouped(ls, n, slots, wb, stream);
+    if (e != hipSuccess) return status_of(e);
+    return status_of(hxq::launch_bwdx_reduce(slots, dx, M * K, w.slots, stream));
+  }
   if (w.mfma) {
     float* slots = reinterpret_cast<float*>(wb + w.bin_bytes);
     int slot0 = 0;

@@ -88,16 +88,22 @@ __global__ __launch_bounds__(256, 1) void bwdx_g5(BwdG5Args a) {
   const int G = gridDim.x, bx = blockIdx.x;
   const int per = G / 8, full = per * 8;
   const int L = (bx < full) ? (bx % 8) * per + bx / 8 : bx;
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSegments; ++i)
+    if (i < a.nseg && L >= a.seg[i].wg0) si = i;
+  const BwdG5Seg& sg = a.seg[si];
   const int tiles = a.tiles_m * a.tiles_k;
-  const int s = L / tiles, tl = L - s * tiles;
+  const int Ls = L - sg.wg0;
+  const int s = Ls / tiles, tl = Ls - s * tiles;
   const int m0 = (tl % a.tiles_m) * BM, k0 = (tl / a.tiles_m) * BN;
-  const int M = a.M, N = a.N, K = a.K;
-  const int n_lo = s * a.R;
-  const int nst = (min(N, n_lo + a.R) - n_lo) / BK;  // N and R are multiples of 32
+  const int M = a.M, N = sg.N, K = a.K;
+  const int n_lo = s * sg.R;
+  const int nst = (min(N, n_lo + sg.R) - n_lo) / BK;  // N and R are multiples of 32
 
   // dy piece j of this wave: block 4 wave + j (16 tokens), lane i: token
   // m0 + 16 (4 wave + j) + i % 16, rows n_lo + 32 stage + 8 (i / 16) + [0, 8)
-  const unsigned char* dyb = reinterpret_cast<const unsigned char*>(a.dy);
+  const unsigned char* dyb = reinterpret_cast<const unsigned char*>(sg.dy);
   const unsigned char* xsrc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(256, 1) void bwdx_g5(BwdG5Args a) {
   };
   // index bytes: rows n_lo + 32 stage + 8 wave + j (j < 8), columns 4 lane .. + 3
   // of the tile (past K: the row's last four, never stored)
-  const uint8_t* isrc = a.indices + (int64_t)(n_lo + 8 * wave) * K + min(k0 + 4 * lane, K - 4);
+  const uint8_t* isrc = sg.indices + (int64_t)(n_lo + 8 * wave) * K + min(k0 + 4 * lane, K - 4);
   auto load_i = [&](int st, uint32_t (&q)[8]) {
     const int sc = min(st, nst - 1);
     const uint8_t* p = isrc + (int64_t)(sc * BK) * K;
@@ -132,19 +138,19 @@ __global__ __launch_bounds__(256, 1) void bwdx_g5(BwdG5Args a) {
   // 4 c, the value in the upper half), lane l reads copy l
   {
     const int e = tid;
-    const float vb = __uint_as_float(f32_to_bf16_rne(a.codebook[e]) << 16);
+    const float vb = __uint_as_float(f32_to_bf16_rne(sg.codebook[e]) << 16);
     const float4 v4 = make_float4(vb, vb, vb, vb);
 #pragma unroll
     for (int q = 0; q < 16; ++q) *reinterpret_cast<float4*>(cbs + e * 256 + (((q + e) & 15) << 4)) = v4;
   }
   // ---- the word ranges of the tile's two sidecar bins per stage: [bs0, bs1)
   // columns k0 .. + 127, [bs1, bs2) the next 128
-  const bool side = a.CT > 0;
+  const bool side = sg.CT > 0;
   {
     const int step0 = n_lo / BK, b0 = k0 / 128;
     for (int i = tid; i < nst * 3; i += THREADS) {
       const int st = i / 3, c = i - 3 * st;
-      bsl[i] = side ? a.binstart[(int64_t)(step0 + st) * (a.CT + 1) + min(b0 + c, a.CT)] : 0;
+      bsl[i] = side ? sg.binstart[(int64_t)(step0 + st) * (sg.CT + 1) + min(b0 + c, sg.CT)] : 0;
     }
   }
   load_i(2, iq0);
@@ -192,7 +198,7 @@ __global__ __launch_bounds__(256, 1) void bwdx_g5(BwdG5Args a) {
   };
   auto patch_range = [&](int q0, int q1, int q2, unsigned char* wt) {  // every word of [q0, q2)
     for (int q = q0 + lane; q < q2; q += 64) {
-      const uint32_t wd = a.bpat[q];
+      const uint32_t wd = sg.bpat[q];
       const int p = patch_pos(wd, q >= q1 ? 128 : 0);
       if (p >= 0) *reinterpret_cast<uint16_t*>(wt + p) = (uint16_t)(wd >> 16);
     }
@@ -286,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void bwdx_g5(BwdG5Args a) {
         // (unconditional, so that the compiler's counter waits stay exact;
         // clamped: an empty last bin starts at nnz, and without a sidecar
         // the ranges are 0 and bpat a stand-in word)
-        if (i == 0) pe = a.bpat[max(min(q0 + lane, a.nnz - 1), 0)];
+        if (i == 0) pe = sg.bpat[max(min(q0 + lane, sg.nnz - 1), 0)];
         if (i == 4) {  // word ranges of W(s + 3), used next stage (past the end: unused)
           const int b = 3 * min(s + 3, nst - 1);
           pq0 = bsl[b];
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(256, 1) void bwdx_g5(BwdG5Args a) {
         // counter waits after it cover every load in flight), each waited
         // for in its own asm block
         for (int q = q0 + 64; q < q2; ++q) {
-          const uint32_t* wp = a.bpat + q;
+          const uint32_t* wp = sg.bpat + q;
           uint32_t wd;
           asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(wd) : "s"(wp) : "memory");
           const int p = patch_pos(wd, q >= q1 ? 128 : 0);
@@ -347,7 +353,7 @@ __global__ __launch_bounds__(256, 1) void bwdx_g5(BwdG5Args a) {
   // and stores 512-byte row pieces (chunk c of row t at 16 ((c ^ t) % 32))
   {
     unsigned char* reg = cbs + wave * RS;
-    float* out = a.out + (int64_t)s * a.slot_stride;
+    float* out = a.out + (int64_t)(sg.slot0 + s) * a.slot_stride;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
@@ -413,12 +419,44 @@ BwdMPlan bwdx_g5_plan(int M, int N, int K, int64_t nnz) {
   return p;
 }
 
-// As launch_bwdx_mfma: sidecar binning, the product, the sum of the splits
-// (a.slots set: the splits go to slots a.slot0 .. + S - 1, not summed).
-hipError_t launch_bwdx_g5(const BwdArgs& a, hipStream_t stream) {
+static hipError_t launch_g5(const BwdG5Args& g, int64_t blocks, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwdx_g5),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, bg5::LDS);
   if (attr != hipSuccess) return attr;
+  if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(bwdx_g5, dim3((unsigned)blocks), dim3(bg5::THREADS), bg5::LDS, stream, g);
+  return hipGetLastError();
+}
+
+// A layer's segment: its bins into `bins` first when it has a sidecar
+// (without one the kernel reads a stand-in word: its first index bytes).
+static hipError_t g5_segment(const BwdArgs& a, int R, int CT, unsigned char* bins, BwdG5Seg& sg,
+                             hipStream_t stream) {
+  sg.codebook = a.codebook;
+  sg.indices = a.indices;
+  sg.dy = static_cast<const uint16_t*>(a.dy);
+  sg.N = a.N;
+  sg.R = R;
+  sg.CT = a.nnz > 0 ? CT : 0;
+  sg.nnz = a.nnz > 0 ? (int)a.nnz : 1;
+  sg.binstart = nullptr;
+  sg.bpat = reinterpret_cast<const uint32_t*>(a.indices);
+  if (a.nnz > 0) {
+    const int nsteps = a.N / bg5::BK;
+    auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+    int* binstart = reinterpret_cast<int*>(bins);
+    uint32_t* bpat = reinterpret_cast<uint32_t*>(bins + al((int64_t)nsteps * (CT + 1) * 4));
+    const hipError_t e = launch_bwdx_bin(a, false, CT, binstart, bpat, stream);
+    if (e != hipSuccess) return e;
+    sg.binstart = binstart;
+    sg.bpat = bpat;
+  }
+  return hipSuccess;
+}
+
+// As launch_bwdx_mfma: sidecar binning, the product, the sum of the splits
+// (a.slots set: the splits go to slots a.slot0 .. + S - 1, not summed).
+hipError_t launch_bwdx_g5(const BwdArgs& a, hipStream_t stream) {
   const BwdMPlan p = bwdx_g5_plan(a.M, a.N, a.K, a.nnz);
   const bool grouped = a.slots != nullptr;
   const int64_t split_bytes = grouped ? 0 : p.split_bytes;
@@ -426,37 +464,82 @@ hipError_t launch_bwdx_g5(const BwdArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;
   unsigned char* w = reinterpret_cast<unsigned char*>(a.ws);
   BwdG5Args g = {};
-  g.codebook = a.codebook;
-  g.indices = a.indices;
-  g.dy = static_cast<const uint16_t*>(a.dy);
   g.out = grouped ? a.slots + (int64_t)a.slot0 * a.M * a.K : p.S > 1 ? reinterpret_cast<float*>(w) : a.dx;
   g.slot_stride = (grouped || p.S > 1) ? (int64_t)a.M * a.K : 0;
   g.M = a.M;
-  g.N = a.N;
   g.K = a.K;
   g.tiles_m = p.mtiles;
   g.tiles_k = p.ctw;
-  g.R = p.R;
-  g.CT = p.CT;
-  // without a sidecar the kernel still reads one stand-in word per stage
-  g.nnz = a.nnz > 0 ? (int)a.nnz : 1;
-  g.bpat = reinterpret_cast<const uint32_t*>(a.indices);
-  if (a.nnz > 0) {
-    const int nsteps = a.N / bg5::BK;
-    auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
-    int* binstart = reinterpret_cast<int*>(w + split_bytes);
-    uint32_t* bpat = reinterpret_cast<uint32_t*>(w + split_bytes + al((int64_t)nsteps * (p.CT + 1) * 4));
-    const hipError_t e = launch_bwdx_bin(a, false, p.CT, binstart, bpat, stream);
-    if (e != hipSuccess) return e;
-    g.binstart = binstart;
-    g.bpat = bpat;
-  }
-  const int64_t blocks = (int64_t)p.ctw * p.mtiles * p.S;
-  if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(bwdx_g5, dim3((unsigned)blocks), dim3(bg5::THREADS), bg5::LDS, stream, g);
-  hipError_t e = hipGetLastError();
+  g.nseg = 1;
+  hipError_t e = g5_segment(a, p.R, a.K / 128, w + split_bytes, g.seg[0], stream);
+  if (e != hipSuccess) return e;
+  g.seg[0].wg0 = 0;
+  g.seg[0].slot0 = 0;
+  e = launch_g5(g, (int64_t)p.ctw * p.mtiles * p.S, stream);
   if (e != hipSuccess || p.S == 1 || grouped) return e;
   return launch_bwdx_reduce(g.out, a.dx, (int64_t)a.M * a.K, p.S, stream);
+}
+
+BwdG5Group bwdx_g5_group_plan(int M, int K, const int* Ns, const int64_t* nnzs, int n) {
+  BwdG5Group g = {};
+  const int64_t tiles = (int64_t)((M + bg5::BM - 1) / bg5::BM) * ((K + bg5::BN - 1) / bg5::BN);
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) total += Ns[i] / bg5::BK;
+  int64_t target = (device_cu_count() + tiles - 1) / tiles;
+  if (target > 64) target = 64;
+  int64_t R = (total + target - 1) / target;  // stages per run
+  if (R < 8) R = 8;
+  if (R > bg5::MAXST) R = bg5::MAXST;
+  auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+  for (int i = 0; i < n; ++i) {
+    const int steps = Ns[i] / bg5::BK;
+    int S = (int)((steps + R / 2) / R);
+    if (S < 1) S = 1;
+    const int smin = (steps + bg5::MAXST - 1) / bg5::MAXST;
+    if (S < smin) S = smin;
+    const int spp = (steps + S - 1) / S;
+    g.S[i] = (steps + spp - 1) / spp;
+    g.R[i] = spp * bg5::BK;
+    g.slots += g.S[i];
+    g.bins[i] = nnzs[i] > 0 ? al((int64_t)steps * (K / 128 + 1) * 4) + al(nnzs[i] * 4) : 0;
+    g.bin_total += g.bins[i];
+  }
+  return g;
+}
+
+hipError_t launch_bwdx_g5_grouped(const BwdArgs* ls, int n, float* slots, unsigned char* bins, hipStream_t stream) {
+  if (n < 1 || n > kMaxSegments) return hipErrorInvalidValue;
+  int Ns[kMaxSegments];
+  int64_t nnzs[kMaxSegments];
+  for (int i = 0; i < n; ++i) {
+    Ns[i] = ls[i].N;
+    nnzs[i] = ls[i].nnz;
+  }
+  const int M = ls[0].M, K = ls[0].K;
+  const BwdG5Group p = bwdx_g5_group_plan(M, K, Ns, nnzs, n);
+  BwdG5Args g = {};
+  g.out = slots;
+  g.slot_stride = (int64_t)M * K;
+  g.M = M;
+  g.K = K;
+  g.tiles_m = (M + bg5::BM - 1) / bg5::BM;
+  g.tiles_k = (K + bg5::BN - 1) / bg5::BN;
+  g.nseg = n;
+  const int64_t tiles = (int64_t)g.tiles_m * g.tiles_k;
+  int64_t wg = 0;
+  int slot = 0;
+  for (int i = 0; i < n; ++i) {
+    const hipError_t e = g5_segment(ls[i], p.R[i], K / 128, bins, g.seg[i], stream);
+    if (e != hipSuccess) return e;
+    bins += p.bins[i];
+    if (wg > INT_MAX) return hipErrorInvalidConfiguration;
+    g.seg[i].wg0 = (int)wg;
+    g.seg[i].slot0 = slot;
+    wg += tiles * p.S[i];
+    slot += p.S[i];
+  }
+  for (int i = n; i < kMaxSegments; ++i) g.seg[i] = g.seg[0];
+  return launch_g5(g, wg, stream);
 }
 
 }  // namespace hxq

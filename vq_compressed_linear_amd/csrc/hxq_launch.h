@@ -245,22 +245,38 @@ hipError_t launch_bwdx_mfma(const BwdArgs& a, bool pk12, hipStream_t stream);
 // (CT = K / 128 bins per step; binstart [N / 32][CT + 1], bpat [nnz]).
 hipError_t launch_bwdx_bin(const BwdArgs& a, bool pk12, int CT, int* binstart, uint32_t* bpat, hipStream_t stream);
 
-// 256-token x 256-column tiles (hxq_bwd_g5.hip), u8 only
-struct BwdG5Args {
+// 256-token x 256-column tiles (hxq_bwd_g5.hip), u8 only.  One launch can
+// take several layers of a grouped call (all with the same M and K): layer
+// i owns workgroups wg0 .. and stores its split s into slot slot0 + s.
+struct BwdG5Seg {
   const float* codebook;
   const uint8_t* indices;
   const uint16_t* dy;        // [M][N] bf16
-  float* out;                // dx, or the first of the slots split s stores into
-  int64_t slot_stride;       // floats between the splits' slots (0: one split into dx)
-  int M, N, K;
-  int tiles_m, tiles_k, R;   // token tiles, column tiles, rows per split
-  int CT;                    // sidecar bins per step (K / 128); 0 = no sidecar
-  int nnz;                   // patch words (at most the triplets)
-  const int* binstart;
-  const uint32_t* bpat;
+  const int* binstart;       // sidecar bins (CT > 0)
+  const uint32_t* bpat;      // patch words, or a stand-in word when nnz == 0
+  int N, nnz, CT, R;         // rows, words (>= 1), bins per step (K / 128; 0 = no sidecar), rows per split
+  int wg0, slot0;
+};
+struct BwdG5Args {
+  float* out;                // dx, or slot 0
+  int64_t slot_stride;       // floats between slots (0: one split into dx)
+  int M, K, tiles_m, tiles_k, nseg;
+  BwdG5Seg seg[kMaxSegments];
 };
 bool bwdx_g5_ok(const BwdArgs& a, bool pk12);
 BwdMPlan bwdx_g5_plan(int M, int N, int K, int64_t nnz);
+// Several layers in one launch: one run length for all (about one workgroup
+// per CU over the group's rows), each layer's splits and sidecar bins.
+struct BwdG5Group {
+  int S[kMaxSegments], R[kMaxSegments];
+  int64_t bins[kMaxSegments];  // workspace bytes of each layer's bins (multiples of 256)
+  int slots;
+  int64_t bin_total;
+};
+BwdG5Group bwdx_g5_group_plan(int M, int K, const int* Ns, const int64_t* nnzs, int n);
+// Bins into `bins` (bin_total bytes), then one launch whose splits go to
+// slots 0 .. slots - 1 (M K floats each) of `slots`; not summed here.
+hipError_t launch_bwdx_g5_grouped(const BwdArgs* ls, int n, float* slots, unsigned char* bins, hipStream_t stream);
 hipError_t launch_bwdx_g5(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace hxq
