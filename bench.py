@@ -125,6 +125,24 @@ class GroupCall:
             raise RuntimeError("hxq_linear_fwd_grouped failed with status %d" % st)
 
 
+class WsCall:
+    """One pre-marshalled hxq_linear_fwd_ws call: a single layer with a
+    workspace for its k split (the prefill steps' o and down launches)."""
+
+    def __init__(self, L, B, d, y, x, M, N, K, stream, ws):
+        self.fn = L.hxq_linear_fwd_ws
+        xdt = B.HXQ_BF16 if x.element_size() == 2 else B.HXQ_F32
+        self.args = (B.HXQ_FMT_U8, d["codebook"].data_ptr(), d["indices"].data_ptr(), d["rows"].data_ptr(),
+                     d["cols"].data_ptr(), d["deltas"].data_ptr(), d["rows"].numel(), x.data_ptr(), xdt,
+                     d["bias"].data_ptr(), y.data_ptr(), M, N, K,
+                     ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, stream)
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError("hxq_linear_fwd_ws failed with status %d" % st)
+
+
 class LayerCall:
     """One pre-marshalled single-layer call."""
 
@@ -283,6 +301,9 @@ class LayerSet:
     """Device copies of the layer set, activations and outputs for one M."""
 
     def __init__(self, torch, L, B, layers, M, xdt, cfg_x, copies, stream):
+        """Launches that share x go through hxq_linear_fwd_grouped; with bf16
+        x (the prefill steps) a layer alone goes through hxq_linear_fwd_ws
+        with a workspace for its k split."""
         import numpy as np
 
         from hxq_synth import gen
@@ -301,12 +322,24 @@ class LayerSet:
             self.ys.append(torch.empty((M, lay.N), dtype=torch.float32, device="cuda"))
         self.grouped = []
         self.single = []
+        self.ws = None
+        if xdt == "bf16":
+            need = max(L.hxq_linear_fwd_workspace(B.HXQ_FMT_U8, B.HXQ_BF16, M, l.N, l.K) for l in layers)
+            if need < 0:
+                raise RuntimeError("hxq_linear_fwd_workspace failed with status %d" % need)
+            if need > 0:
+                self.ws = torch.empty(int(need), dtype=torch.uint8, device="cuda")
         for r in range(copies):
             row = []
             for g in GROUPS:
                 idx = [self.by_name[n] for n in g]
-                row.append(GroupCall(L, B, [self.devs[r][i] for i in idx], [self.ys[i] for i in idx],
-                                     self.xs[idx[0]], M, layers[idx[0]].K, stream))
+                if len(idx) == 1 and xdt == "bf16":
+                    i = idx[0]
+                    row.append(WsCall(L, B, self.devs[r][i], self.ys[i], self.xs[i], M, layers[i].N, layers[i].K,
+                                      stream, self.ws))
+                else:
+                    row.append(GroupCall(L, B, [self.devs[r][i] for i in idx], [self.ys[i] for i in idx],
+                                         self.xs[idx[0]], M, layers[idx[0]].K, stream))
             self.grouped.append(row)
             self.single.append([LayerCall(L, B, self.devs[r][i], self.ys[i], self.xs[i], M, l.N, l.K, stream)
                                 for i, l in enumerate(layers)])
@@ -464,7 +497,9 @@ def prefill_big(torch, L, B, layers, stream, steps):
     x_dn = torch.from_numpy(gen.to_bf16_bits(gen.synth_x(4, 6, M, 11008)).view(np.int16)).cuda().view(torch.bfloat16)
     ys = [torch.empty((M, l.N), dtype=torch.float32, device="cuda") for l in sel]
     gu = GroupCall(L, B, devs[:2], ys[:2], x_gu, M, 2048, stream)
-    dn = LayerCall(L, B, devs[2], ys[2], x_dn, M, sel[2].N, sel[2].K, stream)
+    need = L.hxq_linear_fwd_workspace(B.HXQ_FMT_U8, B.HXQ_BF16, M, sel[2].N, sel[2].K)
+    ws = torch.empty(int(need), dtype=torch.uint8, device="cuda") if need > 0 else None
+    dn = WsCall(L, B, devs[2], ys[2], x_dn, M, sel[2].N, sel[2].K, stream, ws)
     t_gu = time_steps(torch, [[gu]], steps, 1) / steps * 1e3
     t_dn = time_steps(torch, [[dn]], steps, 1) / steps * 1e3
     f_gu = 2.0 * 2.0 * M * 11008 * 2048
@@ -476,7 +511,7 @@ def prefill_big(torch, L, B, layers, stream, steps):
     r_dn = dict(launch="down", avg_us=round(t_dn, 2))
     r_dn.update(roof(b_dn, f_dn, t_dn, "bf16"))
     tf = (f_gu + f_dn) / ((t_gu + t_dn) * 1e-6) / 1e12
-    del devs, x_gu, x_dn, ys
+    del devs, x_gu, x_dn, ys, ws
     torch.cuda.empty_cache()
     return dict(workload="gate|up and down of the Qwen2.5-3B-shaped u8 set at M=25600 (50 x 512 tokens), bf16 x",
                 M=M, step_us=round(t_gu + t_dn, 2), tflops=round(tf, 1),

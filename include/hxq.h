@@ -111,6 +111,37 @@ int hxq_linear_fwd_pk12(const float* codebook2, const uint8_t* packed,
                         const void* x, int x_dtype, const float* bias, float* y,
                         int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/* The forward of either format (fmt: HXQ_FMT_U8 or HXQ_FMT_PK12; codebook
+ * and indices as for hxq_linear_fwd_u8 / hxq_linear_fwd_pk12) with a caller
+ * workspace.  A layer with bf16 x that the matrix-core GEMM takes but whose
+ * 256 x 256 output tiles are too few to fill the GPU while K is long (the
+ * 2048 -> 11008 -> 2048 down projection at 512 or 2048 tokens) then splits
+ * its sum over k into runs of at least 48 32-deep stages: each run's partial
+ * sums go to the workspace, and a second launch adds them into y in run
+ * order (the bias and, on the sidecar's walk path, its terms in the first
+ * run).  The result is within the bf16 tolerance of the single-launch
+ * product, not bitwise the same (another summation order).  Any other call,
+ * or a workspace smaller than hxq_linear_fwd_workspace gives, computes
+ * exactly what hxq_linear_fwd_u8 / hxq_linear_fwd_pk12 compute.
+ *   workspace  caller-owned device memory, 16-byte aligned, workspace_bytes
+ *              long (NULL with 0: none); contents on entry ignored and on
+ *              return unspecified; two calls in flight at once need separate
+ *              workspaces.
+ * Errors: those of hxq_linear_fwd_u8 / _pk12, HXQ_ERR_SHAPE for an unknown fmt
+ * or negative workspace_bytes, HXQ_ERR_ALIGN for a misaligned workspace. */
+int hxq_linear_fwd_ws(int fmt, const void* codebook, const uint8_t* indices,
+                      const int32_t* sc_rows, const int32_t* sc_cols,
+                      const float* sc_deltas, int64_t nnz,
+                      const void* x, int x_dtype, const float* bias, float* y,
+                      int64_t M, int64_t N, int64_t K,
+                      void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace hxq_linear_fwd_ws uses on the current device for these
+ * sizes with 16-byte aligned pointers (0 when it would not split), or a
+ * negative hxq_status for arguments it would reject (HXQ_ERR_SHAPE,
+ * HXQ_ERR_DTYPE).  Host only. */
+int64_t hxq_linear_fwd_workspace(int fmt, int x_dtype, int64_t M, int64_t N, int64_t K);
+
 /* The sidecar term alone, accumulated into y:
  *     y[m][r] += sum over triplets (r, c, d) of d * x[m][c]      (fp32)
  * (HXQ whitepaper, "Method", sidecar outlier correction, applied to the

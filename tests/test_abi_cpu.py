@@ -350,3 +350,35 @@ def test_bwd_x_grouped_rejects_before_any_hip_call(L):
     assert g(U8, two, 2, F32, FAKE, M, K, None, 0, None) == B.HXQ_ERR_UNSUPPORTED
     # nothing to compute
     assert g(U8, two, 2, F32, FAKE, 0, K, None, 0, None) == B.HXQ_OK
+
+
+def test_fwd_workspace_query(L):
+    q = L.hxq_linear_fwd_workspace
+    U8, PK, BF, F32 = B.HXQ_FMT_U8, B.HXQ_FMT_PK12, B.HXQ_BF16, B.HXQ_F32
+    assert q(9, BF, 1, 8, 8) == B.HXQ_ERR_SHAPE
+    assert q(U8, 5, 1, 8, 8) == B.HXQ_ERR_DTYPE
+    assert q(U8, BF, -1, 8, 8) == B.HXQ_ERR_SHAPE
+    assert q(PK, BF, 8, 8, 7) == B.HXQ_ERR_SHAPE
+    assert q(U8, BF, 0, 8, 8) == 0
+    # the down projection at 512 and 2048 tokens splits its k (whole [M][N] fp32 partial sums)
+    for M in (512, 2048):
+        n = q(U8, BF, M, 2048, 11008)
+        assert n >= 2 * M * 2048 * 4 and n % (M * 2048 * 4) == 0
+    # no split: fp32 x, enough output tiles, short K, or too few tokens for the GEMM
+    assert q(U8, F32, 2048, 2048, 11008) == 0
+    assert q(U8, BF, 2048, 11008, 2048) == 0
+    assert q(U8, BF, 2048, 2048, 2048) == 0
+    assert q(U8, BF, 17, 2048, 11008) == 0
+
+
+def test_fwd_ws_rejects_before_any_hip_call(L):
+    f = L.hxq_linear_fwd_ws
+    U8, BF = B.HXQ_FMT_U8, B.HXQ_BF16
+    args = lambda **k: (k.get("fmt", U8), FAKE, FAKE, None, None, None, 0, FAKE, BF, None, FAKE, 4, 64, 64,
+                        k.get("ws", None), k.get("wsb", 0), None)
+    assert f(*args(fmt=7)) == B.HXQ_ERR_SHAPE
+    assert f(*args(wsb=-1)) == B.HXQ_ERR_SHAPE
+    assert f(*args(ws=FAKE + 4, wsb=64)) == B.HXQ_ERR_ALIGN
+    assert f(U8, FAKE, FAKE, None, None, None, 0, FAKE, 9, None, FAKE, 4, 64, 64, None, 0, None) == B.HXQ_ERR_DTYPE
+    assert f(U8, FAKE, FAKE, None, None, None, 0, FAKE, BF, None, None, 4, 64, 64, None, 0, None) == B.HXQ_ERR_NULL
+    assert f(U8, FAKE, FAKE, None, None, None, 0, FAKE, BF, None, FAKE, 0, 64, 64, None, 0, None) == B.HXQ_OK

@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     hxq_linear_fwd_grouped,
     hxq_linear_fwd_pk12,
     hxq_linear_fwd_u8,
+    hxq_linear_fwd_ws,
     hxq_select_variant,
     hxq_sidecar_add,
     hxq_version,

@@ -91,6 +91,8 @@ SIGNATURES = {
     "hxq_linear_fwd_u8_ex": (_INT, _FWD_ARGS + [_INT]),
     "hxq_linear_fwd_pk12_ex": (_INT, _FWD_ARGS + [_INT]),
     "hxq_sidecar_add": (_INT, [_P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P]),
+    "hxq_linear_fwd_ws": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _INT, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
+    "hxq_linear_fwd_workspace": (_I64, [_INT, _INT, _I64, _I64, _I64]),
     "hxq_linear_fwd_grouped": (_INT, [_INT, ctypes.POINTER(HxqLayer), _INT, _P, _INT, _I64, _I64, _P]),
     "hxq_stream_read": (_INT, [_P, _I64, _P, _INT, _P]),
     "hxq_dequant_bf16": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _I64, _I64, _P]),
@@ -259,6 +261,47 @@ def hxq_linear_fwd_pk12(codebook2, packed, sc_rows, sc_cols, sc_deltas, x, bias,
         _ptr(x), _x_dtype(x), _ptr(bias), _ptr(y), M, N, K, _stream(stream, dev), variant)
     if st != HXQ_OK:
         raise HxqError(st, "hxq_linear_fwd_pk12")
+
+
+def hxq_linear_fwd_ws(fmt: int, codebook, indices, sc_rows, sc_cols, sc_deltas, x, bias, y, K: int,
+                      stream=None, workspace=None) -> None:
+    """The forward of either format with a workspace for the k split of
+    layers with few output tiles (see include/hxq.h).  K is the layer's input
+    width (pk12 rows hold 3*ceil(K/4) bytes).  ``workspace`` (a device
+    tensor): when None, one of the size the library asks for is taken from
+    torch's caching allocator; an empty tensor means none."""
+    torch = _torch()
+    if fmt == HXQ_FMT_U8:
+        if codebook.dtype != torch.float32 or codebook.numel() != 256:
+            raise ValueError("codebook must be 256 float32 values")
+        row = K
+    else:
+        if codebook.dtype != torch.float32 or codebook.numel() != 4096 * 2:
+            raise ValueError("codebook2 must be 4096 x 2 float32 values")
+        row = 3 * ((K + 3) // 4)
+    if indices.dtype != torch.uint8 or indices.dim() != 2 or not indices.is_contiguous() or indices.shape[1] != row:
+        raise ValueError("indices must be a contiguous uint8 [N, %d] tensor" % row)
+    N = indices.shape[0]
+    M, Kx = _check_common(x, bias, y, N)
+    if Kx != K:
+        raise ValueError("x has K=%d, the layer K=%d" % (Kx, K))
+    nnz = _check_sidecar(sc_rows, sc_cols, sc_deltas)
+    dev = _check_device(codebook, indices, sc_rows, sc_cols, sc_deltas, x, bias, y,
+                        workspace if workspace is not None and workspace.numel() > 0 else None)
+    if workspace is None:
+        need = lib().hxq_linear_fwd_workspace(fmt, _x_dtype(x), M, N, K)
+        if need < 0:
+            raise HxqError(int(need), "hxq_linear_fwd_workspace")
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=y.device) if need > 0 else None
+    if workspace is None or workspace.numel() == 0:
+        wptr, wbytes = None, 0
+    else:
+        wptr, wbytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = lib().hxq_linear_fwd_ws(fmt, _ptr(codebook), _ptr(indices), _ptr(sc_rows), _ptr(sc_cols),
+                                 _ptr(sc_deltas), nnz, _ptr(x), _x_dtype(x), _ptr(bias), _ptr(y), M, N, K,
+                                 wptr, wbytes, _stream(stream, dev))
+    if st != HXQ_OK:
+        raise HxqError(st, "hxq_linear_fwd_ws")
 
 
 def hxq_sidecar_add(sc_rows, sc_cols, sc_deltas, x, y, stream=None) -> None:

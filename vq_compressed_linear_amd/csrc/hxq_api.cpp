@@ -209,6 +209,55 @@ hxq::BwdMPlan bwd_mm_plan(int kernel, const hxq::BwdArgs& a) {
   return kernel == 2 ? hxq::bwdx_g5_plan(a.M, a.N, a.K, a.nnz) : hxq::bwdx_mfma_plan(a.M, a.N, a.K, a.nnz);
 }
 
+// ---- forward with a workspace: the k split of the 256 x 256 tile GEMM
+
+// The split plan AUTO would use for this layer with a workspace (S < 2: none).
+hxq::Gemm5Split fwd_split_plan(bool pk12, const hxq::LayerArgs& a) {
+  const hxq::Gemm5Split none = {1, 0, 0};
+  if (!a.x_bf16 || a.K <= 0 || !hxq::gemm5_path_ok(a, pk12)) return none;
+  const bool gemv_ok = hxq::gemv_fast_path_ok(a, pk12);
+  if (select(pk12, true, a.M, a.N, a.K, gemv_ok, true) != HXQ_VARIANT_GEMM_BF16) return none;
+  return hxq::gemm5_split_plan(a.M, a.N, a.K);
+}
+
+int forward_ws(int fmt, const void* codebook, const uint8_t* indices, const int32_t* sc_rows, const int32_t* sc_cols,
+               const float* sc_deltas, int64_t nnz, const void* x, int x_dtype, const float* bias, float* y, int64_t M,
+               int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (fmt != HXQ_FMT_U8 && fmt != HXQ_FMT_PK12) return HXQ_ERR_SHAPE;
+  const bool pk12 = fmt == HXQ_FMT_PK12;
+  const int st = validate_forward(codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, x, x_dtype, bias, y, M, N, K,
+                                  pk12);
+  if (st != HXQ_OK) return st;
+  if (workspace_bytes < 0) return HXQ_ERR_SHAPE;
+  if (misaligned(workspace, 16)) return HXQ_ERR_ALIGN;
+  if (M > 0 && N > 0 && K > 0) {
+    hxq::LayerArgs a = {};
+    a.codebook = codebook;
+    a.indices = indices;
+    a.sc_rows = sc_rows;
+    a.sc_cols = sc_cols;
+    a.sc_deltas = sc_deltas;
+    a.nnz = nnz;
+    a.x = x;
+    a.x_bf16 = x_dtype == HXQ_BF16;
+    a.bias = bias;
+    a.y = y;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    const hxq::Gemm5Split p = fwd_split_plan(pk12, a);
+    if (p.S >= 2 && workspace && workspace_bytes >= p.bytes) {
+      (void)hipGetLastError();
+      const hxq::GemmSeg sg = {static_cast<const float*>(codebook), indices, sc_rows, sc_cols, sc_deltas, nnz, bias, y,
+                               (int)N, 0};
+      return status_of(hxq::launch_gemm5_split(sg, pk12, x, (int)M, (int)K, static_cast<float*>(workspace),
+                                               workspace_bytes, stream));
+    }
+  }
+  return forward(pk12, codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, x, x_dtype, bias, y, M, N, K, stream,
+                 HXQ_VARIANT_AUTO);
+}
+
 // ---- grouped input gradient: dx = sum over layers of dy_i W_i
 
 hxq::BwdArgs bwd_args_of(const hxq_bwd_layer& l, bool dy_bf16, float* dx, int64_t M, int64_t K) {
@@ -489,6 +538,34 @@ int hxq_linear_fwd_pk12_ex(const float* codebook2, const uint8_t* packed, const 
                            int64_t N, int64_t K, hipStream_t stream, int variant) {
   return forward(true, codebook2, packed, sc_rows, sc_cols, sc_deltas, nnz, x, x_dtype, bias, y, M,
                  N, K, stream, variant);
+}
+
+int hxq_linear_fwd_ws(int fmt, const void* codebook, const uint8_t* indices, const int32_t* sc_rows,
+                      const int32_t* sc_cols, const float* sc_deltas, int64_t nnz, const void* x, int x_dtype,
+                      const float* bias, float* y, int64_t M, int64_t N, int64_t K, void* workspace,
+                      int64_t workspace_bytes, hipStream_t stream) {
+  return forward_ws(fmt, codebook, indices, sc_rows, sc_cols, sc_deltas, nnz, x, x_dtype, bias, y, M, N, K, workspace,
+                    workspace_bytes, stream);
+}
+
+int64_t hxq_linear_fwd_workspace(int fmt, int x_dtype, int64_t M, int64_t N, int64_t K) {
+  if (fmt != HXQ_FMT_U8 && fmt != HXQ_FMT_PK12) return HXQ_ERR_SHAPE;
+  if (x_dtype != HXQ_F32 && x_dtype != HXQ_BF16) return HXQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return HXQ_ERR_SHAPE;
+  if (fmt == HXQ_FMT_PK12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
+  if (M == 0 || N == 0 || K == 0) return 0;
+  // the plan for 16-byte aligned pointers
+  hxq::LayerArgs a = {};
+  a.indices = reinterpret_cast<const uint8_t*>(uintptr_t(256));
+  a.codebook = reinterpret_cast<const void*>(uintptr_t(256));
+  a.x = reinterpret_cast<const void*>(uintptr_t(256));
+  a.y = reinterpret_cast<float*>(uintptr_t(256));
+  a.x_bf16 = x_dtype == HXQ_BF16;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  const hxq::Gemm5Split p = fwd_split_plan(fmt == HXQ_FMT_PK12, a);
+  return p.S >= 2 ? p.bytes : 0;
 }
 
 int hxq_linear_fwd_u8(const float* codebook, const uint8_t* indices, const int32_t* sc_rows,

@@ -114,9 +114,17 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
     if (i < ga.nseg && L >= ga.seg[i].tile0) si = i;
   const GemmSeg& sg = ga.seg[si];
   const int M = ga.M, N = sg.N, K = ga.K;
-  const int tl = L - sg.tile0;
+  int tl = L - sg.tile0;
+  // a split launch (one layer): run `split` of the tile's k stages
+  int split = 0;
+  if (ga.S > 1) {
+    const int tiles = ga.tiles_m * ((N + BN - 1) / BN);
+    split = tl / tiles;
+    tl -= split * tiles;
+  }
   const int m0 = (tl % ga.tiles_m) * BM, n0 = (tl / ga.tiles_m) * BN;
-  const int nk = K / BK;
+  const int kb = split * ga.sst;                // the run's first stage
+  const int nk = min(K / BK - kb, ga.sst);      // and its stages
   const int64_t row_bytes = PK12 ? (int64_t)(K / 4) * 3 : (int64_t)K;
 
   // x piece j of this wave: block 4 wave + j (16 tokens), lane i: token
@@ -126,7 +134,8 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
   const unsigned char* xsrc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    xsrc[j] = xb + (int64_t)min(m0 + 16 * (4 * wave + j) + (lane & 15), M - 1) * (K * 2) + 16 * (lane >> 4);
+    xsrc[j] = xb + (int64_t)min(m0 + 16 * (4 * wave + j) + (lane & 15), M - 1) * (K * 2) + 16 * (lane >> 4) +
+              kb * (BK * 2);
   auto load_x = [&](int st, u32x4 (&v)[4]) {
     const int sc = min(st, nk - 1);
 #pragma unroll
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
   const uint8_t* isrc[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
-    isrc[rb] = sg.indices + (int64_t)min(n0 + 64 * wave + 32 * rb + l32, N - 1) * row_bytes + UB * h;
+    isrc[rb] = sg.indices + (int64_t)min(n0 + 64 * wave + 32 * rb + l32, N - 1) * row_bytes + UB * h + kb * IS;
   auto load_i = [&](int st, u32x4 (&q)[2]) {
     const int sc = min(st, nk - 1);
 #pragma unroll
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
     constexpr int QMAX = CAP / THREADS;
     unsigned char* hflag = wbuf;  // the weight buffers are first written after the set-up
     int tr[QMAX], tc[QMAX];
-    bool head[QMAX];
+    bool head[QMAX], inr[QMAX];  // inr: in this run's stages
 #pragma unroll
     for (int q = 0; q < QMAX; ++q) {
       const int64_t e = lo + tid + (int64_t)THREADS * q;
@@ -220,8 +229,9 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
       tc[q] = sg.sc_cols[ec];
       const int pr = sg.sc_rows[ep], pc = sg.sc_cols[ep];
       head[q] = e < hi && (e == lo || pr != tr[q] || pc != tc[q]);
+      inr[q] = (unsigned)(tc[q] / BK - kb) < (unsigned)nk;
       if (e < hi) hflag[e - lo] = head[q] ? 1 : 0;
-      if (head[q]) atomicAdd(&cnt32[1 + (tc[q] / BK) * WAVES + ((tr[q] - n0) >> 6)], 1);
+      if (head[q] && inr[q]) atomicAdd(&cnt32[1 + (tc[q] / BK - kb) * WAVES + ((tr[q] - n0) >> 6)], 1);
     }
     __syncthreads();
     {
@@ -258,7 +268,7 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < QMAX; ++q) {
-      if (!head[q]) continue;
+      if (!head[q] || !inr[q]) continue;
       const int64_t e = lo + tid + (int64_t)THREADS * q;
       float v = sg.sc_deltas[e];
       if (PK12) {
@@ -275,7 +285,7 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
       const int nl = tr[q] - n0, kl = tc[q] % BK;
       const uint32_t pos = (uint32_t)(((nl >> 5) * 2 + (kl >> 4)) * 1024 + ((((kl >> 3) & 1) * 32 + (nl & 31)) * 16) +
                                       (kl & 7) * 2);
-      patch[atomicAdd(&cnt32[1 + (tc[q] / BK) * WAVES + (nl >> 6)], 1)] = pos | (f32_to_bf16_rne(v) << 16);
+      patch[atomicAdd(&cnt32[1 + (tc[q] / BK - kb) * WAVES + (nl >> 6)], 1)] = pos | (f32_to_bf16_rne(v) << 16);
     }
   } else if (!walk) {
     for (int i = tid; i <= nbins; i += THREADS) bins[i] = 0;
@@ -506,7 +516,7 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int n = n0 + 32 * (4 * wn + f) + 8 * q + 4 * h + r;
-          bv[f][q][r] = (sg.bias && n < N) ? sg.bias[n] : 0.f;
+          bv[f][q][r] = (sg.bias && n < N && split == 0) ? sg.bias[n] : 0.f;  // once per output
         }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -529,8 +539,8 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
         const int t = 2 * i + h;
         v[i] = *reinterpret_cast<const float4*>(reg + t * 512 + ((l32 ^ t) & 31) * 16);
       }
-      if (walk) {
-        // the sidecar of the lane's outputs: for each distinct (row, col),
+      if (walk && split == 0) {
+        // the sidecar of the lane's outputs (all of k, in the first run): for each distinct (row, col),
         // x times (bf16(C[idx] + deltas) - bf16(C[idx])), both bf16 values exact in fp32
         const uint16_t* xh = static_cast<const uint16_t*>(ga.x);
         const int mb = m0 + 128 * wm + 32 * g + h;
@@ -572,7 +582,7 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
         const int t = 2 * i + h;
         const int m = m0 + 128 * wm + 32 * g + t;
         if (m >= M || n >= N) continue;
-        float* yp = sg.y + (int64_t)m * N + n;
+        float* yp = (ga.S > 1 ? ga.ws + (int64_t)split * ga.slot_stride : sg.y) + (int64_t)m * N + n;
         if (vec_ok) {
           *reinterpret_cast<float4*>(yp) = v[i];
         } else {
@@ -590,7 +600,7 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
 }
 
 template <bool PK12>
-static hipError_t launch_gemm5(GemmArgs& ga, hipStream_t stream) {
+static hipError_t launch_gemm5(GemmArgs& ga, hipStream_t stream, int grid = 0) {
   using Ly = gemm5::Lay<PK12>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm5_bf16<PK12>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, Ly::LDS);
@@ -601,6 +611,7 @@ static hipError_t launch_gemm5(GemmArgs& ga, hipStream_t stream) {
     tiles += (int64_t)ga.tiles_m * ((ga.seg[i].N + gemm5::BN - 1) / gemm5::BN);
     if (tiles > INT_MAX) return hipErrorInvalidValue;
   }
+  if (grid > 0) tiles = grid;
   hipLaunchKernelGGL((gemm5_bf16<PK12>), dim3((unsigned)tiles), dim3(gemm5::THREADS), Ly::LDS, stream, ga);
   return hipGetLastError();
 }
@@ -632,7 +643,55 @@ hipError_t launch_gemm5_grouped(const GemmSeg* segs, int nseg, bool pk12, const 
   ga.nseg = nseg;
   for (int i = 0; i < nseg; ++i) ga.seg[i] = segs[i];
   for (int i = nseg; i < kMaxSegments; ++i) ga.seg[i] = segs[0];
+  ga.S = 1;
+  ga.sst = K / gemm5::BK;
+  ga.ws = nullptr;
+  ga.slot_stride = 0;
   return pk12 ? launch_gemm5<true>(ga, stream) : launch_gemm5<false>(ga, stream);
+}
+
+// Runs of at least MINST stages (shorter ones spend more on their partial
+// sums' traffic than they gain), about one workgroup per CU, at most MAXST
+// stages each (the patch bins), at most 64 runs.
+Gemm5Split gemm5_split_plan(int M, int N, int K) {
+  constexpr int MINST = 48;
+  Gemm5Split p = {1, K / gemm5::BK, 0};
+  const int64_t tiles = (int64_t)((M + gemm5::BM - 1) / gemm5::BM) * ((N + gemm5::BN - 1) / gemm5::BN);
+  const int nk = K / gemm5::BK;
+  int64_t S = (device_cu_count() + tiles - 1) / tiles;
+  if (S > nk / MINST) S = nk / MINST;
+  if (S > 64) S = 64;
+  const int smin = (nk + gemm5::MAXST - 1) / gemm5::MAXST;
+  if (S < 2 || S < smin) return p;
+  p.sst = (int)((nk + S - 1) / S);
+  p.S = (nk + p.sst - 1) / p.sst;
+  p.bytes = p.S > 1 ? (int64_t)p.S * M * N * 4 : 0;
+  if (p.S < 2) p = {1, nk, 0};
+  return p;
+}
+
+hipError_t launch_gemm5_split(const GemmSeg& sg, bool pk12, const void* x, int M, int K, float* ws, int64_t ws_bytes,
+                              hipStream_t stream) {
+  const Gemm5Split p = gemm5_split_plan(M, sg.N, K);
+  if (p.S < 2 || ws == nullptr || ws_bytes < p.bytes) return hipErrorInvalidValue;
+  GemmArgs ga;
+  ga.x = x;
+  ga.M = M;
+  ga.K = K;
+  ga.tiles_m = (M + gemm5::BM - 1) / gemm5::BM;
+  ga.nseg = 1;
+  for (int i = 0; i < kMaxSegments; ++i) ga.seg[i] = sg;
+  ga.S = p.S;
+  ga.sst = p.sst;
+  ga.ws = ws;
+  ga.slot_stride = (int64_t)M * sg.N;
+  const int64_t tiles = (int64_t)ga.tiles_m * ((sg.N + gemm5::BN - 1) / gemm5::BN);
+  if (tiles * p.S > INT_MAX) return hipErrorInvalidValue;
+  // the launcher counts one run's tiles; the grid covers all runs
+  hipError_t e = pk12 ? launch_gemm5<true>(ga, stream, (int)(tiles * p.S))
+                      : launch_gemm5<false>(ga, stream, (int)(tiles * p.S));
+  if (e != hipSuccess) return e;
+  return launch_bwdx_reduce(ws, sg.y, (int64_t)M * sg.N, p.S, stream);
 }
 
 }  // namespace hxq

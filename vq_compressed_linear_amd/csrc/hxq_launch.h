@@ -156,6 +156,11 @@ struct GemmArgs {
   int tiles_m;
   int nseg;
   GemmSeg seg[kMaxSegments];
+  // the 256 x 256 tile kernel's split of k (one layer only): S runs of sst
+  // stages, run s storing into ws + s * slot_stride (S == 1: into y)
+  int S, sst;
+  float* ws;
+  int64_t slot_stride;
 };
 hipError_t launch_gemm_grouped(const GemmSeg* segs, int nseg, bool pk12, const void* x, int M, int K,
                                hipStream_t stream);
@@ -167,6 +172,16 @@ bool gemm5_path_ok(const LayerArgs& a, bool pk12);
 int64_t gemm5_tiles(const GemmSeg* segs, int nseg, int M);
 hipError_t launch_gemm5_grouped(const GemmSeg* segs, int nseg, bool pk12, const void* x, int M, int K,
                                 hipStream_t stream);
+// One layer with its sum over k split into S runs (S >= 2 when the layer has
+// too few tiles to fill the CUs and K is long enough), the runs' partial
+// sums in a workspace of S M N floats, added into y in run order.
+struct Gemm5Split {
+  int S, sst;
+  int64_t bytes;
+};
+Gemm5Split gemm5_split_plan(int M, int N, int K);
+hipError_t launch_gemm5_split(const GemmSeg& sg, bool pk12, const void* x, int M, int K, float* ws, int64_t ws_bytes,
+                              hipStream_t stream);
 
 // y += S x.
 hipError_t launch_sidecar_add(const LayerArgs& a, hipStream_t stream);
