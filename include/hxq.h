@@ -114,12 +114,12 @@ int hxq_linear_fwd_pk12(const float* codebook2, const uint8_t* packed,
 /* The forward of either format (fmt: HXQ_FMT_U8 or HXQ_FMT_PK12; codebook
  * and indices as for hxq_linear_fwd_u8 / hxq_linear_fwd_pk12) with a caller
  * workspace.  A layer with bf16 x that the matrix-core GEMM takes but whose
- * 256 x 256 output tiles are too few to fill the GPU while K is long (the
- * 2048 -> 11008 -> 2048 down projection at 512 or 2048 tokens) then splits
- * its sum over k into runs of at least 48 32-deep stages: each run's partial
- * sums go to the workspace, and a second launch adds them into y in run
- * order (the bias and, on the sidecar's walk path, its terms in the first
- * run).  The result is within the bf16 tolerance of the single-launch
+ * 256 x 256 output tiles are too few to fill the GPU while K is long
+ * (K >= 4096: the 11008 -> 2048 down projection at 512 or 2048 tokens) then
+ * splits its sum over k into runs of at least 24 32-deep stages: each run's
+ * partial sums go to the workspace, and a second launch adds them into y in
+ * run order (the bias and, on the sidecar's walk path, its terms in the
+ * first run).  The result is within the bf16 tolerance of the single-launch
  * product, not bitwise the same (another summation order).  Any other call,
  * or a workspace smaller than hxq_linear_fwd_workspace gives, computes
  * exactly what hxq_linear_fwd_u8 / hxq_linear_fwd_pk12 compute.

@@ -650,14 +650,16 @@ hipError_t launch_gemm5_grouped(const GemmSeg* segs, int nseg, bool pk12, const 
   return pk12 ? launch_gemm5<true>(ga, stream) : launch_gemm5<false>(ga, stream);
 }
 
-// Runs of at least MINST stages (shorter ones spend more on their partial
-// sums' traffic than they gain), about one workgroup per CU, at most MAXST
-// stages each (the patch bins), at most 64 runs.
+// Layers of at least 128 stages (K >= 4096: shorter ones spend more on
+// their partial sums' traffic than the split gains; o at 2048 tokens 45 ->
+// 67 us in two runs), in runs of at least MINST stages, about one workgroup
+// per CU, at most MAXST stages each (the patch bins), at most 64 runs.
 Gemm5Split gemm5_split_plan(int M, int N, int K) {
-  constexpr int MINST = 48;
+  constexpr int MINST = 24;
   Gemm5Split p = {1, K / gemm5::BK, 0};
   const int64_t tiles = (int64_t)((M + gemm5::BM - 1) / gemm5::BM) * ((N + gemm5::BN - 1) / gemm5::BN);
   const int nk = K / gemm5::BK;
+  if (nk < 128) return p;
   int64_t S = (device_cu_count() + tiles - 1) / tiles;
   if (S > nk / MINST) S = nk / MINST;
   if (S > 64) S = 64;
