@@ -385,7 +385,8 @@ enum hxq_variant {
   HXQ_VARIANT_GENERIC = 4,    /* any shape or alignment, one wave per output row */
   HXQ_VARIANT_GEMM_BF16_T256 = 5  /* the bf16 matrix-core GEMM with 256 x 256 tiles (bf16 x only,
                                      K % 32 == 0); AUTO and HXQ_VARIANT_GEMM_BF16 take it for
-                                     launches of at least two rounds of such tiles over the CUs */
+                                     launches whose tiles fill their rounds over the CUs to at
+                                     least 59% */
 };
 
 int hxq_linear_fwd_u8_ex(const float* codebook, const uint8_t* indices,

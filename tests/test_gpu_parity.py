@@ -211,10 +211,10 @@ def test_dense_sidecar_rows(fmt, variant, M, xdt):
 
 @pytest.mark.parametrize("fmt", ["u8", "pk12"])
 def test_gemm_wide_tiles_ragged(fmt):
-    """2000 tokens x 4100 outputs: 256-output tiles take fewer rounds over the
-    CUs than 128-output ones, so the wide tiles run, with a 4-output last
-    tile and an 80-token last tile row."""
-    N, K, M = 4100, 128, 2000
+    """2000 tokens x 5124 outputs: 168 tiles of 256 x 256 fill most of a
+    round over the CUs, so the wide tiles run, with a 4-output last tile and
+    an 80-token last tile row."""
+    N, K, M = 5124, 128, 2000
     G.say("gemm wide tiles ragged %s" % fmt)
     lay = gen.random_layer(57, N, K, fmt, nnz=N * K // 1000, duplicates=True)
     for variant in GEMMS:

@@ -63,10 +63,16 @@ int status_of(hipError_t e) { return e == hipSuccess ? HXQ_OK : HXQ_ERR_HIP; }
 // The 256 x 256 tile GEMM (gemm5) against the 128-token one (gemm3): per
 // tile it does more work per LDS byte and per gather, but a launch with few
 // tiles leaves CUs idle (the prefill layers at 2048 tokens: q|k|v, o and down
-// have 64 to 80 such tiles, gate|up 688).  It takes a launch of at least two
-// rounds of tiles over the CUs, and the shapes only it can take.
+// have 64 to 80 such tiles, gate|up 688).  A round of gemm5 tiles over the
+// CUs takes about as long as gemm3 needs for 0.59 CUs' worth of tiles
+// (measured at K = 2048: one round 78-85 us; gemm3 54 us for 86 tiles, 102
+// us for 172), so gemm5 takes a launch whose tiles fill its rounds to at
+// least that (gate|up at 512 tokens: 172 tiles), and the shapes only it can
+// take.
 bool gemm5_preferred(const hxq::GemmSeg* segs, int nseg, int M) {
-  return hxq::gemm5_tiles(segs, nseg, M) >= 2 * (int64_t)hxq::device_cu_count();
+  const int64_t t = hxq::gemm5_tiles(segs, nseg, M), cus = hxq::device_cu_count();
+  const int64_t rounds = (t + cus - 1) / cus;
+  return 100 * t >= 59 * cus * rounds;
 }
 
 int forward(bool pk12, const void* codebook, const uint8_t* indices, const int32_t* sc_rows,
