@@ -35,8 +35,10 @@
  *   - bias may be NULL (no bias).
  *   - M == 0 or N == 0: nothing is launched, HXQ_OK.  K == 0: y = bias (or 0).
  *   - Arithmetic: fp32 activations are multiplied in fp32 with fp32
- *     accumulation (vector FMAs up to 4 tokens, fp32 matrix-core products
- *     beyond, which are exact fp32 products summed in fp32); bf16 activations
+ *     accumulation (vector FMAs for one token, fp32 matrix-core products
+ *     from two, which are exact fp32 products summed in fp32; up to 4 tokens
+ *     vector FMAs again where the matrix-core GEMV does not take the layer:
+ *     K % 256 != 0 or misaligned pointers); bf16 activations
  *     are upcast exactly and take the same fp32 path, except with M > 64, or
  *     17 <= M <= 64 on a layer with N > 3968 (at least 32 output tiles of
  *     128 x 128), which runs on bf16 matrix cores with fp32 accumulation
@@ -379,7 +381,8 @@ int hxq_linear_bwd_x_ex(int fmt, const float* codebook, const uint8_t* indices,
  * HXQ_ERR_UNSUPPORTED when it cannot take the call. */
 enum hxq_variant {
   HXQ_VARIANT_AUTO = 0,
-  HXQ_VARIANT_GEMV_VALU = 1,  /* fp32 GEMV family: vector FMAs up to 4 tokens, fp32 matrix cores beyond */
+  HXQ_VARIANT_GEMV_VALU = 1,  /* fp32 GEMV family: vector FMAs for one token (and up to 4 where the
+                                 matrix-core GEMV does not fit), fp32 matrix cores beyond */
   HXQ_VARIANT_GEMV_MFMA = 2,  /* fp32 matrix-core GEMV (16x16x4 fp32 MFMA) at any M; needs K % 64 == 0 */
   HXQ_VARIANT_GEMM_BF16 = 3,  /* bf16 matrix-core GEMM (bf16 x only; K % 32 == 0) */
   HXQ_VARIANT_GENERIC = 4,    /* any shape or alignment, one wave per output row */

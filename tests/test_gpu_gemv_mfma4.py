@@ -1,4 +1,4 @@
-"""GPU parity of the 4x4-block matrix-core GEMV (5 to 8 tokens, u8 and pk12,
+"""GPU parity of the 4x4-block matrix-core GEMV (2 to 8 tokens, u8 and pk12,
 K % 256 == 0) against the CPU oracle, through the C ABI."""
 
 import numpy as np
@@ -38,7 +38,7 @@ def _case(fmt, x_dtype, M, N, K, seed, nnz_den=1000):
 
 @pytest.mark.parametrize("fmt", ["u8", "pk12"])
 @pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("M", [5, 6, 7, 8])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("N,K", [(97, 2048), (2048, 11008), (11008, 2048), (1000, 768), (5, 256)])
 def test_gemv_mfma4_matches_oracle(fmt, x_dtype, M, N, K):
     # ragged last fragment, one to 43 chunks (waves without chunks at K < 2048),
@@ -48,10 +48,12 @@ def test_gemv_mfma4_matches_oracle(fmt, x_dtype, M, N, K):
 
 
 @pytest.mark.parametrize("N", [24576, 24580])
-def test_gemv_mfma4_fragment_limit(N):
-    # 24 fragments per workgroup on 256 CUs fit; four rows more take the 16x16 kernel
-    G.say("gemv mfma4 limit N=%d" % N)
-    _case("u8", "f32", 8, N, 256, seed=N)
+@pytest.mark.parametrize("M", [3, 8])
+def test_gemv_mfma4_fragment_limit(N, M):
+    # 24 fragments per workgroup on 256 CUs fit; four rows more take the 16x16
+    # kernel (8 tokens) or the decode kernel (3)
+    G.say("gemv mfma4 limit N=%d M=%d" % (N, M))
+    _case("u8", "f32", M, N, 256, seed=N + M)
 
 
 def test_gemv_mfma4_dense_sidecar():

@@ -622,9 +622,10 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
     segs[nseg++] = {l.codebook, l.indices, l.sc_rows, l.sc_cols, l.sc_deltas, l.nnz, l.bias, l.y, (int)l.N, 0, 0, 0.f};
   }
   if (fast && nseg == 0) return HXQ_OK;
-  // From 5 to 64 tokens the matrix-core GEMVs, with the kernel a single-layer
-  // call would pick for each layer (5 to 8 tokens: the 4x4-block GEMV where it
-  // takes the layer, else the 16x16 one; u8 with bf16 x past 16 tokens goes to
+  // From 2 to 64 tokens the matrix-core GEMVs, with the kernel a single-layer
+  // call would pick for each layer (2 to 8 tokens: the 4x4-block GEMV where it
+  // takes the layer, else the 16x16 one from 5 tokens and the decode kernel up
+  // to 4; u8 with bf16 x past 16 tokens goes to
   // the bf16 GEMM instead where it wants the layer): one launch when every
   // layer takes the same kernel and the group fits one workgroup per CU, one
   // launch per layer when they take the same kernel but do not fit together,
@@ -633,7 +634,7 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
   if (x_dtype == HXQ_BF16 && M > 16)
     for (int i = 0; i < count; ++i)
       if (layers[i].N > 0) ++(bf16_gemm_wanted(M, layers[i].N) ? want_gemm : want_gemv);
-  if (K > 0 && M > 4 && M <= hxq::kGemvMfmaMaxM && want_gemm == 0) {
+  if (K > 0 && M >= 2 && M <= hxq::kGemvMfmaMaxM && want_gemm == 0) {
     hxq::GemvSeg gs[hxq::kMaxSegments];
     int ng = 0, n4 = 0, n16 = 0;
     for (int i = 0; i < count; ++i) {
@@ -652,7 +653,7 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
       if (hxq::gemv_fast_path_ok(a, pk12)) {
         if (M <= 8 && hxq::gemv_mfma4_ok(a, pk12) && hxq::gemv_mfma4_group_fits(&gs[ng], 1))
           ++n4;
-        else if (hxq::gemv_mfma_ok(a, pk12))
+        else if (M > 4 && hxq::gemv_mfma_ok(a, pk12))
           ++n16;
       }
       ++ng;
