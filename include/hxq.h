@@ -332,9 +332,10 @@ int64_t hxq_linear_bwd_x_workspace(int fmt, int dy_dtype, int64_t M, int64_t N,
  * hxq_linear_bwd_x with the same workspace.  Work is one or two launches on
  * `stream` (the product over all layers, the sum), or with bf16 matrix-core
  * products one or two per layer (sidecar binning, product) and the sum.
- * Errors: HXQ_ERR_SHAPE for count out of range or an unknown fmt, HXQ_ERR_NULL
- * for NULL layers, otherwise the first error hxq_linear_bwd_x would return for
- * any layer; HXQ_ERR_UNSUPPORTED when the workspace is smaller than the call
+ * Errors: HXQ_ERR_SHAPE for count out of range, an unknown fmt or layers
+ * with more than INT32_MAX - 65536 rows together, HXQ_ERR_NULL for NULL
+ * layers, otherwise the first error hxq_linear_bwd_x would return for any
+ * layer; HXQ_ERR_UNSUPPORTED when the workspace is smaller than the call
  * needs; nothing is launched when an error is returned. */
 typedef struct hxq_bwd_layer {
   const void* codebook;     /* u8: float[256]; pk12: float[4096][2] */

@@ -382,3 +382,11 @@ def test_fwd_ws_rejects_before_any_hip_call(L):
     assert f(U8, FAKE, FAKE, None, None, None, 0, FAKE, 9, None, FAKE, 4, 64, 64, None, 0, None) == B.HXQ_ERR_DTYPE
     assert f(U8, FAKE, FAKE, None, None, None, 0, FAKE, BF, None, None, 4, 64, 64, None, 0, None) == B.HXQ_ERR_NULL
     assert f(U8, FAKE, FAKE, None, None, None, 0, FAKE, BF, None, FAKE, 0, 64, 64, None, 0, None) == B.HXQ_OK
+
+
+def test_bwd_x_grouped_total_rows_limit(L):
+    # the layers' rows are split as one range: their total must fit int32
+    big = _bwd_layers([(2**31 - 2**17, 0), (2**17, 0)])
+    assert L.hxq_linear_bwd_x_grouped_workspace(B.HXQ_FMT_U8, B.HXQ_F32, big, 2, 1, 64) == B.HXQ_ERR_SHAPE
+    assert L.hxq_linear_bwd_x_grouped(B.HXQ_FMT_U8, big, 2, B.HXQ_F32, FAKE, 1, 64, FAKE, 1 << 20,
+                                      None) == B.HXQ_ERR_SHAPE

@@ -359,6 +359,9 @@ int backward_x_grouped(int fmt, const hxq_bwd_layer* layers, int count, int dy_d
     if (st != HXQ_OK) return st;
   }
   if (misaligned(workspace, 16)) return HXQ_ERR_ALIGN;
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) rows += layers[i].N;
+  if (rows > kMaxDim) return HXQ_ERR_SHAPE;  // the layers' rows are split as one range
   if (M == 0 || K == 0) return HXQ_OK;
   hxq_bwd_layer act[HXQ_MAX_GROUP];
   int n = 0;
@@ -512,11 +515,14 @@ int64_t hxq_linear_bwd_x_grouped_workspace(int fmt, int dy_dtype, const hxq_bwd_
   if (fmt == HXQ_FMT_PK12 && (K % 2) != 0) return HXQ_ERR_SHAPE;
   hxq_bwd_layer act[HXQ_MAX_GROUP];
   int n = 0;
+  int64_t rows = 0;
   for (int i = 0; i < count; ++i) {
     const hxq_bwd_layer& l = layers[i];
     if (l.N < 0 || l.N > kMaxDim || l.nnz < 0 || l.nnz > kMaxDim) return HXQ_ERR_SHAPE;
+    rows += l.N;
     if (l.N > 0) act[n++] = l;
   }
+  if (rows > kMaxDim) return HXQ_ERR_SHAPE;
   if (M == 0 || K == 0 || n == 0) return 0;
   if (n == 1) return hxq_linear_bwd_x_workspace(fmt, dy_dtype, M, act[0].N, K, act[0].nnz);
   return plan_group(fmt == HXQ_FMT_PK12, dy_dtype == HXQ_BF16, act, n, M, K, nullptr, true).bytes;
