@@ -440,3 +440,16 @@ def test_helix_linear_layer_object():
     assert tuple(y.shape) == (2, 3, 128)
     Y, B = G.oracle_fwd(lay, x_np, "f32")
     G.check(y.reshape(6, 128), Y, B, G.TOL_FP32, "layer object")
+
+
+def test_helix_linear_layer_bf16_split():
+    # bf16 activations on a down-shaped layer: the layer object's forward
+    # takes the workspace entry point, which splits the sum over k here
+    lay = gen.random_layer(43, 2048, 11008, "u8", nnz=2048 * 11008 // 1000)
+    m = hx.HelixLinear.from_layer(lay)
+    assert hx.lib().hxq_linear_fwd_workspace(hx.HXQ_FMT_U8, hx.HXQ_BF16, 512, 2048, 11008) > 0
+    x_np = _x(11, 512, 11008, "bf16")
+    y = m(G.dev_x(x_np, "bf16").view(2, 256, 11008))
+    assert tuple(y.shape) == (2, 256, 2048)
+    Y, B = G.oracle_fwd(lay, x_np, "bf16")
+    G.check(y.reshape(512, 2048), Y, B, G.TOL_BF16, "layer object bf16 split")

@@ -66,9 +66,17 @@ class HelixLinear:
         x2 = x.reshape(-1, self.in_features).contiguous()
         y = out if out is not None else torch.empty((x2.shape[0], self.out_features),
                                                     dtype=torch.float32, device=x.device)
-        fn = B.hxq_linear_fwd_u8 if self.fmt == "u8" else B.hxq_linear_fwd_pk12
-        fn(self.codebook, self.indices, self.sc_rows, self.sc_cols, self.sc_deltas, x2,
-           self.bias, y, stream=stream, variant=variant)
+        if variant == B.HXQ_VARIANT_AUTO and x2.dtype == torch.bfloat16:
+            # bf16 activations: the entry point with a workspace (from torch's
+            # caching allocator), which splits the sum over k of layers with
+            # too few output tiles to fill the GPU
+            fmt = B.HXQ_FMT_U8 if self.fmt == "u8" else B.HXQ_FMT_PK12
+            B.hxq_linear_fwd_ws(fmt, self.codebook, self.indices, self.sc_rows, self.sc_cols, self.sc_deltas, x2,
+                                self.bias, y, self.in_features, stream=stream)
+        else:
+            fn = B.hxq_linear_fwd_u8 if self.fmt == "u8" else B.hxq_linear_fwd_pk12
+            fn(self.codebook, self.indices, self.sc_rows, self.sc_cols, self.sc_deltas, x2,
+               self.bias, y, stream=stream, variant=variant)
         return y.reshape(*lead, self.out_features)
 
     __call__ = forward
