@@ -179,3 +179,28 @@ def test_bwd_x_grouped_256_tiles_dense_sidecar():
     dx = _run("u8", devs, dys, M, K)
     Y, B = _oracle(lays, dy_nps, "bf16", K)
     G.check(dx, Y, B, G.TOL_BF16, "bwd_x grouped 256 tiles dense sidecar")
+
+
+@pytest.mark.parametrize("names", [("q", "k", "v"), ("gate", "up"), ("o",), ("down",)])
+def test_bwd_x_grouped_workload_2048_tokens_sampled(names):
+    # the bench's input-gradient step at 2048 tokens (bf16 dy), each shared
+    # input's grouped call on the Qwen2.5-3B-shaped layers of the workload:
+    # every column of dx for one token row in every 128-token block, the last
+    # of every 256-token block and 64 more
+    by = {l.name: l for l in gen.config_layers(1)}
+    lays = [by[n] for n in names]
+    M, K = 2048, lays[0].K
+    G.say("bwd_x grouped workload %s M=%d" % ("|".join(names), M))
+    devs = [G.dev_layer(l) for l in lays]
+    dy_nps = [_dy(900 + i, M, l.N, "bf16") for i, l in enumerate(lays)]
+    dys = [G.dev_x(d, "bf16") for d in dy_nps]
+    dx = _run("u8", devs, dys, M, K)
+    rows = G.tile_rows(M)
+    Y = np.zeros((len(rows), K))
+    B = np.zeros((len(rows), K))
+    for lay, dy_np in zip(lays, dy_nps):
+        y, b = oracle.hxq_linear_bwd_x_u8(lay.codebook, lay.indices, lay.rows, lay.cols, lay.deltas, dy_np,
+                                          "bf16", m_rows=rows)
+        Y += y
+        B += b
+    G.check(dx, Y, B, G.TOL_BF16, "bwd_x grouped workload %s" % "|".join(names), m_rows=rows)
