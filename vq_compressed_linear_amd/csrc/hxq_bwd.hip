@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void bwdx_reduce(const float* __restrict__ ws,
 #pragma unroll
     for (int u = 0; u < B; ++u)
       if (s + u < S) v = make_float4(v.x + t[u].x, v.y + t[u].y, v.z + t[u].z, v.w + t[u].w);
-    *reinterpret_cast<float4*>(dx + i) = v;
+    __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(dx + i));
   } else {
     float v = ws[i];
     int s = 1;

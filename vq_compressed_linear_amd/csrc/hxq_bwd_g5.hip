@@ -354,6 +354,7 @@ __global__ __launch_bounds__(256, 1) void bwdx_g5(BwdG5Args a) {
   {
     unsigned char* reg = cbs + wave * RS;
     float* out = a.out + (int64_t)(sg.slot0 + s) * a.slot_stride;
+    const bool split_out = a.slot_stride != 0;  // slots summed afterwards, else dx itself
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
@@ -373,7 +374,13 @@ __global__ __launch_bounds__(256, 1) void bwdx_g5(BwdG5Args a) {
         const int t = 2 * i + h;
         const int m = m0 + 128 * wm + 32 * g + t;
         const float4 v = *reinterpret_cast<const float4*>(reg + t * 512 + ((l32 ^ t) & 31) * 16);
-        if (m < M && k < K) *reinterpret_cast<float4*>(out + (int64_t)m * K + k) = v;
+        if (m < M && k < K) {
+          float* op = out + (int64_t)m * K + k;
+          if (split_out)  // a partial sum the reduction reads back soon: keep it in the cache
+            *reinterpret_cast<float4*>(op) = v;
+          else
+            __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(op));
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();

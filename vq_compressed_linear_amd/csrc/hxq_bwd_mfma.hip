@@ -152,6 +152,7 @@ struct BwdMArgs {
   const uint8_t* indices;
   const uint16_t* dy;   // [M][N] bf16
   float* out;           // dx, or the workspace splits when S > 1
+  int out_final;        // out is dx itself (stored past the cache), not slots summed afterwards
   int M, N, K;
   int ctw, mtiles, S, R;
   int CT;               // sidecar bins per step (K / 128); 0 = no sidecar
@@ -452,8 +453,15 @@ __global__ __launch_bounds__(bm::THREADS, 1) void bwdx_mfma(BwdMArgs a) {
     float* p = out + (int64_t)m * K + kc + 32 * g;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<float4*>(p + 8 * r) = make_float4(acc[t][0][r], acc[t][1][r], acc[t][2][r], acc[t][3][r]);
-      *reinterpret_cast<float4*>(p + 8 * r + 4) = make_float4(acc[t][4][r], acc[t][5][r], acc[t][6][r], acc[t][7][r]);
+      const f32x4 lo4 = {acc[t][0][r], acc[t][1][r], acc[t][2][r], acc[t][3][r]};
+      const f32x4 hi4 = {acc[t][4][r], acc[t][5][r], acc[t][6][r], acc[t][7][r]};
+      if (!a.out_final) {  // a partial sum the reduction reads back soon: keep it in the cache
+        *reinterpret_cast<f32x4*>(p + 8 * r) = lo4;
+        *reinterpret_cast<f32x4*>(p + 8 * r + 4) = hi4;
+      } else {
+        __builtin_nontemporal_store(lo4, reinterpret_cast<f32x4*>(p + 8 * r));
+        __builtin_nontemporal_store(hi4, reinterpret_cast<f32x4*>(p + 8 * r + 4));
+      }
     }
   }
 }
@@ -521,6 +529,7 @@ hipError_t launch_bwdx_mfma(const BwdArgs& a, bool pk12, hipStream_t stream) {
   m.indices = a.indices;
   m.dy = static_cast<const uint16_t*>(a.dy);
   m.out = grouped ? a.slots + (int64_t)a.slot0 * a.M * a.K : p.S > 1 ? reinterpret_cast<float*>(w) : a.dx;
+  m.out_final = !grouped && p.S <= 1;
   m.M = a.M;
   m.N = a.N;
   m.K = a.K;

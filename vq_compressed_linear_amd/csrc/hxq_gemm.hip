@@ -727,8 +727,9 @@ __global__ __launch_bounds__(gemm3::THREADS, 1) void gemm3_bf16(GemmArgs ga) {
       if (m >= M) continue;
       float* yp = a.y + (int64_t)m * N + n;
       if (vec_ok) {
-        *reinterpret_cast<float4*>(yp) =
-            make_float4(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1], acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
+        __builtin_nontemporal_store(
+            f32x4{acc[i][j][0] + bv[0], acc[i][j][1] + bv[1], acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]},
+            reinterpret_cast<f32x4*>(yp));
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r)

@@ -584,7 +584,10 @@ __global__ __launch_bounds__(256, 1) void gemm5_bf16(GemmArgs ga) {
         if (m >= M || n >= N) continue;
         float* yp = (ga.S > 1 ? ga.ws + (int64_t)split * ga.slot_stride : sg.y) + (int64_t)m * N + n;
         if (vec_ok) {
-          *reinterpret_cast<float4*>(yp) = v[i];
+          if (ga.S > 1)  // a run's partial sum, read back by the reduction right after: keep it in the cache
+            *reinterpret_cast<float4*>(yp) = v[i];
+          else  // y: written once, not read again by this launch
+            __builtin_nontemporal_store(f32x4{v[i].x, v[i].y, v[i].z, v[i].w}, reinterpret_cast<f32x4*>(yp));
         } else {
           yp[0] = v[i].x;
           if (n + 1 < N) yp[1] = v[i].y;
