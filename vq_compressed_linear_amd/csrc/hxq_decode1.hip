@@ -48,8 +48,10 @@ __device__ __forceinline__ int xoff(int k) {
 // CH: chunks of 16 weights per lane and row (K <= 1024 CH); XL: x read from
 // LDS per chunk (else held in registers, K == 1024 CH); ONE: no wave has more
 // than one row (the launch plan's rows per workgroup <= 8), so a wave requests
-// its row alone instead of a ring of three
-template <bool PK12, bool XBF, int CH, bool XL, bool ONE>
+// its row alone instead of a ring of three; NT: index bytes loaded
+// non-temporally (streamed past the caches: launches whose workgroups own
+// long runs of rows)
+template <bool PK12, bool XBF, int CH, bool XL, bool ONE, bool NT>
 __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
   using namespace dc1;
   __shared__ __align__(16) unsigned char cbs[PK12 ? 4096 * 8 : 256 * 256];
@@ -123,7 +125,8 @@ __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
         const u32x3 v = *reinterpret_cast<const u32x3*>(p + CB * cc);
         iq[c] = u32x4{v[0], v[1], v[2], 0u};
       } else {
-        iq[c] = *reinterpret_cast<const u32x4*>(p + CB * cc);
+        iq[c] = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + CB * cc))
+                   : *reinterpret_cast<const u32x4*>(p + CB * cc);
       }
     }
   };
@@ -330,43 +333,52 @@ static bool decode1_plan(GemvMArgs& g, int& grid) {
   return true;
 }
 
-template <bool PK12, bool XBF, int CH, bool XL, bool ONE>
+template <bool PK12, bool XBF, int CH, bool XL, bool ONE, bool NT>
 static hipError_t launch_decode1_o(const GemvMArgs& g, int grid, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&decode1_gemv<PK12, XBF, CH, XL, ONE>),
+      reinterpret_cast<const void*>(&decode1_gemv<PK12, XBF, CH, XL, ONE, NT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, dc1::LDS_DYN);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((decode1_gemv<PK12, XBF, CH, XL, ONE>), dim3((unsigned)grid), dim3(dc1::THREADS),
+  hipLaunchKernelGGL((decode1_gemv<PK12, XBF, CH, XL, ONE, NT>), dim3((unsigned)grid), dim3(dc1::THREADS),
                      dc1::LDS_DYN, stream, g);
   return hipGetLastError();
 }
 
+// one: at most one row per wave (no ring); long: the ring instance with
+// non-temporal index loads
 template <bool PK12, bool XBF, int CH, bool XL>
-static hipError_t launch_decode1_x(const GemvMArgs& g, int grid, bool one, hipStream_t stream) {
-  return one ? launch_decode1_o<PK12, XBF, CH, XL, true>(g, grid, stream)
-             : launch_decode1_o<PK12, XBF, CH, XL, false>(g, grid, stream);
+static hipError_t launch_decode1_x(const GemvMArgs& g, int grid, bool one, bool lng, hipStream_t stream) {
+  if (one) return launch_decode1_o<PK12, XBF, CH, XL, true, false>(g, grid, stream);
+  return lng ? launch_decode1_o<PK12, XBF, CH, XL, false, true>(g, grid, stream)
+             : launch_decode1_o<PK12, XBF, CH, XL, false, false>(g, grid, stream);
 }
 
 // K a multiple of 1024 up to 4096: x in registers; otherwise x from LDS with
 // the smallest instantiated chunk count that covers K
 template <bool PK12, bool XBF>
-static hipError_t launch_decode1_k(const GemvMArgs& g, int grid, bool one, hipStream_t stream) {
+static hipError_t launch_decode1_k(const GemvMArgs& g, int grid, bool one, bool lng, hipStream_t stream) {
   if (g.K % 1024 == 0 && g.K <= 4096) {
     switch (g.K / 1024) {
-      case 1: return launch_decode1_x<PK12, XBF, 1, false>(g, grid, one, stream);
-      case 2: return launch_decode1_x<PK12, XBF, 2, false>(g, grid, one, stream);
-      case 3: return launch_decode1_x<PK12, XBF, 3, false>(g, grid, one, stream);
-      default: return launch_decode1_x<PK12, XBF, 4, false>(g, grid, one, stream);
+      case 1: return launch_decode1_x<PK12, XBF, 1, false>(g, grid, one, lng, stream);
+      case 2: return launch_decode1_x<PK12, XBF, 2, false>(g, grid, one, lng, stream);
+      case 3: return launch_decode1_x<PK12, XBF, 3, false>(g, grid, one, lng, stream);
+      default: return launch_decode1_x<PK12, XBF, 4, false>(g, grid, one, lng, stream);
     }
   }
   const int ch = (g.K + 1023) / 1024;
-  if (ch <= 2) return launch_decode1_x<PK12, XBF, 2, true>(g, grid, one, stream);
-  if (ch <= 4) return launch_decode1_x<PK12, XBF, 4, true>(g, grid, one, stream);
-  if (ch <= 6) return launch_decode1_x<PK12, XBF, 6, true>(g, grid, one, stream);
-  if (ch <= 8) return launch_decode1_x<PK12, XBF, 8, true>(g, grid, one, stream);
-  if (ch <= 11) return launch_decode1_x<PK12, XBF, 11, true>(g, grid, one, stream);
-  return launch_decode1_x<PK12, XBF, 12, true>(g, grid, one, stream);
+  if (ch <= 2) return launch_decode1_x<PK12, XBF, 2, true>(g, grid, one, lng, stream);
+  if (ch <= 4) return launch_decode1_x<PK12, XBF, 4, true>(g, grid, one, lng, stream);
+  if (ch <= 6) return launch_decode1_x<PK12, XBF, 6, true>(g, grid, one, lng, stream);
+  if (ch <= 8) return launch_decode1_x<PK12, XBF, 8, true>(g, grid, one, lng, stream);
+  if (ch <= 11) return launch_decode1_x<PK12, XBF, 11, true>(g, grid, one, lng, stream);
+  return launch_decode1_x<PK12, XBF, 12, true>(g, grid, one, lng, stream);
 }
+
+// Rows per workgroup past which the index stream bypasses the caches: on the
+// Qwen decode step gate|up (86 rows per workgroup) 12.6 -> 11.8 us and the
+// step of four launches 35.4 -> 32.6-33.0 us, while launches of few rows per
+// workgroup (q|k|v: 10, o and down: 8) were 0.3-0.4 us slower that way.
+constexpr int kDecode1LongRun = 32;
 
 bool launch_decode1(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
                     hipStream_t stream, hipError_t& err) {
@@ -391,11 +403,12 @@ bool launch_decode1(const DecodeSeg* segs, int nseg, bool pk12, const void* x, b
     if (r > most) most = r;
   }
   const bool one = most <= dc1::WAVES;
+  const bool lng = most > kDecode1LongRun;
   if (pk12)
-    err = xbf ? launch_decode1_k<true, true>(g, grid, one, stream) : launch_decode1_k<true, false>(g, grid, one, stream);
+    err = xbf ? launch_decode1_k<true, true>(g, grid, one, lng, stream) : launch_decode1_k<true, false>(g, grid, one, lng, stream);
   else
-    err = xbf ? launch_decode1_k<false, true>(g, grid, one, stream)
-              : launch_decode1_k<false, false>(g, grid, one, stream);
+    err = xbf ? launch_decode1_k<false, true>(g, grid, one, lng, stream)
+              : launch_decode1_k<false, false>(g, grid, one, lng, stream);
   return true;
 }
 

@@ -75,8 +75,9 @@ __device__ __forceinline__ float reduce_blocks(f32x4 v) {
 
 // TG: groups of 4 tokens (1 up to 4 tokens, 2 up to 8); FG: fragments per
 // accumulator group (1 to 4, no more than a workgroup owns); X1: K <= 2048,
-// so a wave has at most one chunk and loads its x once
-template <bool PK12, bool XBF, int TG, int FG, bool X1>
+// so a wave has at most one chunk and loads its x once; NT: index bytes
+// loaded non-temporally (launches whose workgroups own long runs of rows)
+template <bool PK12, bool XBF, int TG, int FG, bool X1, bool NT>
 __global__ __launch_bounds__(gm4::THREADS, 1) void gemv_mfma4(GemvMArgs ga) {
   using namespace gm4;
   // u8: fp32 codebook, 64 copies per entry (copy j at byte e * 256 + 4 j);
@@ -145,7 +146,8 @@ __global__ __launch_bounds__(gm4::THREADS, 1) void gemv_mfma4(GemvMArgs ga) {
         const u32x3 v = *reinterpret_cast<const u32x3*>(p + k0 / 4 * 3);
         iq[f] = u32x4{v[0], v[1], v[2], 0u};
       } else {
-        iq[f] = *reinterpret_cast<const u32x4*>(p + k0);
+        iq[f] = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + k0))
+                   : *reinterpret_cast<const u32x4*>(p + k0);
       }
     }
   };
@@ -481,21 +483,29 @@ bool gemv_mfma4_group_fits(const GemvSeg* segs, int nseg) {
   return gemv_mfma4_args(segs, nseg, g) && gemv_mfma4_plan(g, grid, fmax);
 }
 
-template <bool PK12, bool XBF, int TG, int FG, bool X1>
+template <bool PK12, bool XBF, int TG, int FG, bool X1, bool NT>
 static hipError_t launch_gemv_mfma4_x(const GemvMArgs& g, int grid, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemv_mfma4<PK12, XBF, TG, FG, X1>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      gm4::LDS_DYN);
+      reinterpret_cast<const void*>(&gemv_mfma4<PK12, XBF, TG, FG, X1, NT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, gm4::LDS_DYN);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemv_mfma4<PK12, XBF, TG, FG, X1>), dim3((unsigned)grid), dim3(gm4::THREADS), gm4::LDS_DYN,
-                     stream, g);
+  hipLaunchKernelGGL((gemv_mfma4<PK12, XBF, TG, FG, X1, NT>), dim3((unsigned)grid), dim3(gm4::THREADS),
+                     gm4::LDS_DYN, stream, g);
   return hipGetLastError();
 }
 
+// Fragments per workgroup past which the index stream bypasses the caches
+// (gate|up at 8 tokens: 22), as in the one-token kernel.
+constexpr int kMfma4LongRun = 8;
+
 template <bool PK12, bool XBF, int TG, int FG>
-static hipError_t launch_gemv_mfma4_k(const GemvMArgs& g, int grid, hipStream_t stream) {
-  return g.K <= gm4::KC * gm4::WAVES ? launch_gemv_mfma4_x<PK12, XBF, TG, FG, true>(g, grid, stream)
-                                     : launch_gemv_mfma4_x<PK12, XBF, TG, FG, false>(g, grid, stream);
+static hipError_t launch_gemv_mfma4_k(const GemvMArgs& g, int fmax, int grid, hipStream_t stream) {
+  const bool x1 = g.K <= gm4::KC * gm4::WAVES;
+  if (fmax > kMfma4LongRun)
+    return x1 ? launch_gemv_mfma4_x<PK12, XBF, TG, FG, true, true>(g, grid, stream)
+              : launch_gemv_mfma4_x<PK12, XBF, TG, FG, false, true>(g, grid, stream);
+  return x1 ? launch_gemv_mfma4_x<PK12, XBF, TG, FG, true, false>(g, grid, stream)
+            : launch_gemv_mfma4_x<PK12, XBF, TG, FG, false, false>(g, grid, stream);
 }
 
 template <bool PK12, bool XBF, int TG>
@@ -505,10 +515,10 @@ static hipError_t launch_gemv_mfma4_f(const GemvMArgs& g, int fmax, int grid, hi
   int fg = 4;
   for (int c = 3; c >= 1; --c)
     if ((fmax + c - 1) / c * c < (fmax + fg - 1) / fg * fg) fg = c;
-  if (fg == 1) return launch_gemv_mfma4_k<PK12, XBF, TG, 1>(g, grid, stream);
-  if (fg == 2) return launch_gemv_mfma4_k<PK12, XBF, TG, 2>(g, grid, stream);
-  if (fg == 3) return launch_gemv_mfma4_k<PK12, XBF, TG, 3>(g, grid, stream);
-  return launch_gemv_mfma4_k<PK12, XBF, TG, 4>(g, grid, stream);
+  if (fg == 1) return launch_gemv_mfma4_k<PK12, XBF, TG, 1>(g, fmax, grid, stream);
+  if (fg == 2) return launch_gemv_mfma4_k<PK12, XBF, TG, 2>(g, fmax, grid, stream);
+  if (fg == 3) return launch_gemv_mfma4_k<PK12, XBF, TG, 3>(g, fmax, grid, stream);
+  return launch_gemv_mfma4_k<PK12, XBF, TG, 4>(g, fmax, grid, stream);
 }
 
 template <bool PK12>
