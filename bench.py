@@ -350,34 +350,38 @@ class LayerSet:
 
 def stream_ceiling(torch, L, nbytes, steps):
     """Attainable read bandwidth at the dominant launch's size: hxq_stream_read
-    over contiguous buffers of `nbytes` (as many rotating copies as exceed
-    twice the Infinity Cache), for a sweep of grid sizes; the best is the
-    ceiling the decode kernels are compared against."""
+    (ordinary loads) and hxq_stream_read_nt (non-temporal loads) over
+    contiguous buffers of `nbytes` (as many rotating copies as exceed twice the
+    Infinity Cache), for a sweep of grid sizes; the best is the ceiling the
+    decode kernels are compared against."""
     nb = nbytes // 16 * 16
     copies = max(2, -(-ROTATE_BYTES // nb))
     bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(i & 255) for i in range(copies)]
     stream = torch.cuda.current_stream().cuda_stream
     sweep = []
-    for wgs in (256, 512, 1024, 2048, 4096, 8192):
-        words = 8 * wgs  # a word per wave
-        sink = torch.zeros(words, dtype=torch.int32, device="cuda")
+    for loads, fn in (("ordinary", L.hxq_stream_read), ("non-temporal", L.hxq_stream_read_nt)):
+        for wgs in (256, 512, 1024, 2048, 4096, 8192):
+            words = 8 * wgs  # a word per wave
+            sink = torch.zeros(words, dtype=torch.int32, device="cuda")
 
-        def reader(b, sink=sink, words=words):
-            def f():
-                st = L.hxq_stream_read(b.data_ptr(), nb, sink.data_ptr(), words, stream)
-                if st != 0:
-                    raise RuntimeError("hxq_stream_read failed with status %d" % st)
-            return f
+            def reader(b, sink=sink, words=words, fn=fn):
+                def f():
+                    st = fn(b.data_ptr(), nb, sink.data_ptr(), words, stream)
+                    if st != 0:
+                        raise RuntimeError("stream read failed with status %d" % st)
+                return f
 
-        calls = [[reader(b)] for b in bufs]
-        n = max(steps, len(bufs))
-        avg = time_steps(torch, calls, n, 2) / n
-        sweep.append(dict(workgroups=wgs, avg_us=round(avg * 1e3, 3), gbs=round(nb / (avg * 1e-3) / 1e9, 1)))
+            calls = [[reader(b)] for b in bufs]
+            n = max(steps, len(bufs))
+            avg = time_steps(torch, calls, n, 2) / n
+            sweep.append(dict(loads=loads, workgroups=wgs, avg_us=round(avg * 1e3, 3),
+                              gbs=round(nb / (avg * 1e-3) / 1e9, 1)))
     best = max(sweep, key=lambda r: r["gbs"])
     del bufs
     torch.cuda.empty_cache()
-    return dict(kernel="stream_read_kernel (hxq_stream_read)", bytes_per_launch=nb, rotating_copies=copies,
-                best_workgroups=best["workgroups"], avg_us=best["avg_us"], gbs=best["gbs"], sweep=sweep)
+    return dict(kernel="stream_read_kernel (hxq_stream_read, hxq_stream_read_nt)", bytes_per_launch=nb,
+                rotating_copies=copies, best_loads=best["loads"], best_workgroups=best["workgroups"],
+                avg_us=best["avg_us"], gbs=best["gbs"], sweep=sweep)
 
 
 def percentiles(torch, calls, n):

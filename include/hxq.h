@@ -211,6 +211,13 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count,
 int hxq_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words,
                     hipStream_t stream);
 
+/* The same read with non-temporal loads (the form the decode and
+ * input-gradient kernels use for launches that stream more index bytes than
+ * the L2 caches hold); same arguments, digest and errors.  The attainable
+ * read bandwidth is the better of the two over the grid sweep. */
+int hxq_stream_read_nt(const void* src, int64_t bytes, uint32_t* sink, int sink_words,
+                       hipStream_t stream);
+
 /* Measurement helper, not part of the forward pass: the dense bf16 weight of
  * one layer, for timing the buffered design the HXQ whitepaper's inference
  * paragraph describes (gather the weight into a shared bf16 buffer, then a

@@ -186,8 +186,9 @@ def test_grouped_rejects_call_arguments(L):
     assert f(B.HXQ_FMT_U8, _layers(2, N=0), 1, FAKE, B.HXQ_F32, 0, 16, None) == B.HXQ_OK
 
 
-def test_stream_read_rejects(L):
-    f = L.hxq_stream_read
+@pytest.mark.parametrize("fn", ["hxq_stream_read", "hxq_stream_read_nt"])
+def test_stream_read_rejects(L, fn):
+    f = getattr(L, fn)
     assert f(FAKE, 15, FAKE, 8, None) == B.HXQ_ERR_SHAPE
     assert f(FAKE, -16, FAKE, 8, None) == B.HXQ_ERR_SHAPE
     assert f(FAKE, 16, FAKE, 0, None) == B.HXQ_ERR_SHAPE

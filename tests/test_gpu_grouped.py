@@ -195,7 +195,8 @@ def test_grouped_is_deterministic():
 
 @pytest.mark.parametrize("nbytes", [16, 1024 * 1024 + 48, 23 * 1000 * 1000 // 16 * 16])
 @pytest.mark.parametrize("words", [8, 256, 1024, 4096 * 8])
-def test_stream_read_digest(nbytes, words):
+@pytest.mark.parametrize("fn", ["hxq_stream_read", "hxq_stream_read_nt"])
+def test_stream_read_digest(nbytes, words, fn):
     # the measurement helper reads every byte once whatever its grid (a word
     # per wave, words / 8 workgroups): XOR of the digests is the XOR of all
     # 32-bit words
@@ -204,8 +205,8 @@ def test_stream_read_digest(nbytes, words):
     host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
     src = t.from_numpy(host.view(np.int32)).cuda()
     sink = t.zeros(words, dtype=t.int32, device="cuda")
-    st = hx.lib().hxq_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), words,
-                                  t.cuda.current_stream().cuda_stream)
+    st = getattr(hx.lib(), fn)(src.data_ptr(), nbytes, sink.data_ptr(), words,
+                               t.cuda.current_stream().cuda_stream)
     assert st == 0
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(host)

@@ -95,6 +95,7 @@ SIGNATURES = {
     "hxq_linear_fwd_workspace": (_I64, [_INT, _INT, _I64, _I64, _I64]),
     "hxq_linear_fwd_grouped": (_INT, [_INT, ctypes.POINTER(HxqLayer), _INT, _P, _INT, _I64, _I64, _P]),
     "hxq_stream_read": (_INT, [_P, _I64, _P, _INT, _P]),
+    "hxq_stream_read_nt": (_INT, [_P, _I64, _P, _INT, _P]),
     "hxq_dequant_bf16": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _I64, _I64, _P]),
     "hxq_linear_bwd_x": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "hxq_linear_bwd_x_ex": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _P, _INT, _P, _I64, _I64, _I64, _P, _I64, _P,

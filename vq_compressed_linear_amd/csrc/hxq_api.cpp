@@ -738,13 +738,22 @@ int hxq_linear_fwd_grouped(int fmt, const hxq_layer* layers, int count, const vo
   return HXQ_OK;
 }
 
-int hxq_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream) {
+static int stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, bool nt,
+                       hipStream_t stream) {
   if (bytes < 0 || bytes % 16 != 0 || sink_words < 8) return HXQ_ERR_SHAPE;
   if (bytes == 0) return HXQ_OK;
   if (!src || !sink) return HXQ_ERR_NULL;
   if (misaligned(src, 16) || misaligned(sink, 4)) return HXQ_ERR_ALIGN;
   (void)hipGetLastError();
-  return status_of(hxq::launch_stream_read(src, bytes, sink, sink_words, stream));
+  return status_of(hxq::launch_stream_read(src, bytes, sink, sink_words, nt, stream));
+}
+
+int hxq_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream) {
+  return stream_read(src, bytes, sink, sink_words, false, stream);
+}
+
+int hxq_stream_read_nt(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream) {
+  return stream_read(src, bytes, sink, sink_words, true, stream);
 }
 
 int hxq_dequant_bf16(int fmt, const float* codebook, const uint8_t* indices, const int32_t* sc_rows,

@@ -49,8 +49,9 @@ __device__ __forceinline__ float load_dy(const void* dy, int64_t off) {
 // VEC: one 8-byte load (u8: K % 8 == 0; pk12: K % 16 == 0, so the row pitch
 // is a multiple of 12 bytes and the lane's 6 bytes sit inside an aligned
 // 8-byte window: bytes 0-5 for even lanes, 2-7 for odd ones).  Otherwise byte
-// loads with the columns clamped to the row.
-template <bool PK12, bool VEC>
+// loads with the columns clamped to the row.  NT: the 8-byte loads are
+// non-temporal (a launch that streams more than the L2s hold, once).
+template <bool PK12, bool VEC, bool NT>
 struct IdxLoad {
   const uint8_t* base;  // the lane's first byte in row 0 (VEC) or the row 0 start
   int64_t pitch;        // bytes per row
@@ -59,7 +60,14 @@ struct IdxLoad {
 
   __device__ __forceinline__ uint2 load(int n) const {
     const uint8_t* p = base + (int64_t)n * pitch;
-    if (VEC) return *reinterpret_cast<const uint2*>(p);
+    if (VEC) {
+      if (NT) {
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        return make_uint2(v.x, v.y);
+      }
+      return *reinterpret_cast<const uint2*>(p);
+    }
     if (PK12) {
       // groups t0 = cl / 4 and t0 + 1 (three bytes each), clamped to the row's last group
       const int tl = (K + 3) / 4 - 1;
@@ -119,7 +127,7 @@ __device__ __forceinline__ void gather8(uint2 q, bool odd, const unsigned char* 
 
 // LPR: lanes per row, 16 (a 128-column tile, four rows per wave instruction)
 // or 64 (a 512-column tile, one row per instruction, for long rows)
-template <bool PK12, bool DYBF, int MT, bool VEC, int LPR>
+template <bool PK12, bool DYBF, int MT, bool VEC, int LPR, bool NT>
 __global__ __launch_bounds__(bx::THREADS) void bwdx_valu(BwdArgs ba) {
   using namespace bx;
   constexpr int UNR = MT >= 8 ? 4 : 8;        // rows per row position and group
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(bx::THREADS) void bwdx_valu(BwdArgs ba) {
   const int cl = c0 + 8 * (lane % LPR);            // the lane's first column
   const uint32_t lane4 = (uint32_t)lane << 2;
 
-  IdxLoad<PK12, VEC> il;
+  IdxLoad<PK12, VEC, NT> il;
   il.pitch = PK12 ? (int64_t)((K + 3) / 4) * 3 : (int64_t)K;
   il.cl = cl;
   il.K = K;
@@ -424,22 +432,28 @@ static bool vec_ok(const uint8_t* indices, int K, bool pk12) {
 
 bool bwdx_vec_ok(const BwdArgs& a, bool pk12) { return vec_ok(a.indices, a.K, pk12); }
 
-template <bool PK12, bool DYBF, bool VEC, int LPR>
+template <bool PK12, bool DYBF, bool VEC, int LPR, bool NT>
 static hipError_t launch_bx(const BwdArgs& a, int mt, dim3 grid, hipStream_t stream) {
   switch (mt) {
-    case 1: hipLaunchKernelGGL((bwdx_valu<PK12, DYBF, 1, VEC, LPR>), grid, dim3(bx::THREADS), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((bwdx_valu<PK12, DYBF, 2, VEC, LPR>), grid, dim3(bx::THREADS), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((bwdx_valu<PK12, DYBF, 4, VEC, LPR>), grid, dim3(bx::THREADS), 0, stream, a); break;
-    default: hipLaunchKernelGGL((bwdx_valu<PK12, DYBF, 8, VEC, LPR>), grid, dim3(bx::THREADS), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((bwdx_valu<PK12, DYBF, 1, VEC, LPR, NT>), grid, dim3(bx::THREADS), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((bwdx_valu<PK12, DYBF, 2, VEC, LPR, NT>), grid, dim3(bx::THREADS), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((bwdx_valu<PK12, DYBF, 4, VEC, LPR, NT>), grid, dim3(bx::THREADS), 0, stream, a); break;
+    default: hipLaunchKernelGGL((bwdx_valu<PK12, DYBF, 8, VEC, LPR, NT>), grid, dim3(bx::THREADS), 0, stream, a); break;
   }
   return hipGetLastError();
 }
 
+// nt: non-temporal index loads (8-byte loads only)
 template <bool PK12, bool DYBF>
-static hipError_t launch_bx_v(const BwdArgs& a, int mt, bool vec, int lpr, dim3 grid, hipStream_t stream) {
+static hipError_t launch_bx_v(const BwdArgs& a, int mt, bool vec, bool nt, int lpr, dim3 grid, hipStream_t stream) {
+  if (!vec)
+    return lpr == 64 ? launch_bx<PK12, DYBF, false, 64, false>(a, mt, grid, stream)
+                     : launch_bx<PK12, DYBF, false, 16, false>(a, mt, grid, stream);
   if (lpr == 64)
-    return vec ? launch_bx<PK12, DYBF, true, 64>(a, mt, grid, stream) : launch_bx<PK12, DYBF, false, 64>(a, mt, grid, stream);
-  return vec ? launch_bx<PK12, DYBF, true, 16>(a, mt, grid, stream) : launch_bx<PK12, DYBF, false, 16>(a, mt, grid, stream);
+    return nt ? launch_bx<PK12, DYBF, true, 64, true>(a, mt, grid, stream)
+              : launch_bx<PK12, DYBF, true, 64, false>(a, mt, grid, stream);
+  return nt ? launch_bx<PK12, DYBF, true, 16, true>(a, mt, grid, stream)
+            : launch_bx<PK12, DYBF, true, 16, false>(a, mt, grid, stream);
 }
 
 // The launch shape: tokens per workgroup, column tile width, and the number
@@ -484,11 +498,17 @@ static hipError_t launch_bx_any(const BwdArgs& a, const BwdPlan& p, bool pk12, b
   const int64_t blocks = (int64_t)p.ct * p.mtiles * S;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
+  // index bytes read once (one token tile) and more of them than the L2s
+  // hold: non-temporal loads (Qwen input-gradient step at one token 55.5 ->
+  // 52.2 us with every launch so, gate|up the one that gains)
+  int64_t ib = 0;
+  for (int i = 0; i < a.nseg; ++i) ib += index_bytes(a.seg[i].N, a.K, pk12);
+  const bool nt = p.mtiles == 1 && ib > kStreamPastCacheBytes;
   if (pk12)
-    return a.dy_bf16 ? launch_bx_v<true, true>(a, p.mt, vec, p.lpr, grid, stream)
-                     : launch_bx_v<true, false>(a, p.mt, vec, p.lpr, grid, stream);
-  return a.dy_bf16 ? launch_bx_v<false, true>(a, p.mt, vec, p.lpr, grid, stream)
-                   : launch_bx_v<false, false>(a, p.mt, vec, p.lpr, grid, stream);
+    return a.dy_bf16 ? launch_bx_v<true, true>(a, p.mt, vec, nt, p.lpr, grid, stream)
+                     : launch_bx_v<true, false>(a, p.mt, vec, nt, p.lpr, grid, stream);
+  return a.dy_bf16 ? launch_bx_v<false, true>(a, p.mt, vec, nt, p.lpr, grid, stream)
+                   : launch_bx_v<false, false>(a, p.mt, vec, nt, p.lpr, grid, stream);
 }
 
 hipError_t launch_bwdx_valu(const BwdArgs& a0, bool pk12, hipStream_t stream) {

@@ -49,8 +49,7 @@ __device__ __forceinline__ int xoff(int k) {
 // LDS per chunk (else held in registers, K == 1024 CH); ONE: no wave has more
 // than one row (the launch plan's rows per workgroup <= 8), so a wave requests
 // its row alone instead of a ring of three; NT: index bytes loaded
-// non-temporally (streamed past the caches: launches whose workgroups own
-// long runs of rows)
+// non-temporally (launches that stream more than the L2s hold)
 template <bool PK12, bool XBF, int CH, bool XL, bool ONE, bool NT>
 __global__ __launch_bounds__(dc1::THREADS, 1) void decode1_gemv(GemvMArgs ga) {
   using namespace dc1;
@@ -344,8 +343,8 @@ static hipError_t launch_decode1_o(const GemvMArgs& g, int grid, hipStream_t str
   return hipGetLastError();
 }
 
-// one: at most one row per wave (no ring); long: the ring instance with
-// non-temporal index loads
+// one: at most one row per wave (no ring); lng: non-temporal index loads
+// (ring instance only: no ring-less launch streams that much)
 template <bool PK12, bool XBF, int CH, bool XL>
 static hipError_t launch_decode1_x(const GemvMArgs& g, int grid, bool one, bool lng, hipStream_t stream) {
   if (one) return launch_decode1_o<PK12, XBF, CH, XL, true, false>(g, grid, stream);
@@ -374,12 +373,6 @@ static hipError_t launch_decode1_k(const GemvMArgs& g, int grid, bool one, bool 
   return launch_decode1_x<PK12, XBF, 12, true>(g, grid, one, lng, stream);
 }
 
-// Rows per workgroup past which the index stream bypasses the caches: on the
-// Qwen decode step gate|up (86 rows per workgroup) 12.6 -> 11.8 us and the
-// step of four launches 35.4 -> 32.6-33.0 us, while launches of few rows per
-// workgroup (q|k|v: 10, o and down: 8) were 0.3-0.4 us slower that way.
-constexpr int kDecode1LongRun = 32;
-
 bool launch_decode1(const DecodeSeg* segs, int nseg, bool pk12, const void* x, bool xbf, int M, int K,
                     hipStream_t stream, hipError_t& err) {
   if (nseg < 1 || nseg > kMaxSegments) return false;
@@ -403,7 +396,11 @@ bool launch_decode1(const DecodeSeg* segs, int nseg, bool pk12, const void* x, b
     if (r > most) most = r;
   }
   const bool one = most <= dc1::WAVES;
-  const bool lng = most > kDecode1LongRun;
+  // non-temporal index loads past the L2s' capacity (Qwen decode step: gate|up
+  // 12.6 -> 11.8-12.1 us, the four launches 35.3 -> 31.7 us)
+  int64_t ib = 0;
+  for (int i = 0; i < nseg; ++i) ib += index_bytes(segs[i].N, K, pk12);
+  const bool lng = ib > kStreamPastCacheBytes;
   if (pk12)
     err = xbf ? launch_decode1_k<true, true>(g, grid, one, lng, stream) : launch_decode1_k<true, false>(g, grid, one, lng, stream);
   else

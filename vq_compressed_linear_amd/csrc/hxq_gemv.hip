@@ -576,10 +576,13 @@ hipError_t launch_sidecar_add(const LayerArgs& a, hipStream_t stream) {
 // 16 bytes per lane per request, each wave a contiguous stretch with eight
 // requests in flight, and folds what it read into one word per workgroup
 // (so no load can be dropped): the XOR of all sink words is the XOR of all
-// 32-bit words of the buffer.  Same grid shape as the decode kernel.
+// 32-bit words of the buffer.  Same grid shape as the decode kernel.  NT:
+// non-temporal loads (the form the streaming kernels use past the L2s'
+// capacity).
 
 namespace hxq {
 
+template <bool NT>
 __global__ __launch_bounds__(512) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                            uint32_t* __restrict__ sink) {
   // the grid sweeps the buffer in order: each round every thread requests P
@@ -598,7 +601,8 @@ __global__ __launch_bounds__(512) void stream_read_kernel(const u32x4* __restric
     for (int p = 0; p < P; ++p) {
       const int64_t i = i0 + p * nthr + t;
       keep[p] = i < n16 ? 0xffffffffu : 0u;  // a thread past the end re-reads a valid piece and drops it
-      v[p] = src[i < n16 ? i : n16 - 1];
+      const u32x4* q = src + (i < n16 ? i : n16 - 1);
+      v[p] = NT ? __builtin_nontemporal_load(q) : *q;
     }
   };
   auto fold = [&](const u32x4 (&v)[P], const uint32_t (&keep)[P]) {
@@ -627,7 +631,8 @@ __global__ __launch_bounds__(512) void stream_read_kernel(const u32x4* __restric
   if (lane == 0) sink[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = acc;
 }
 
-hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream) {
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, bool nt,
+                              hipStream_t stream) {
   // one workgroup per 8 sink words (a word per wave; the caller picks the
   // grid), no more than the buffer's pieces need
   int64_t grid = sink_words / 8;
@@ -635,8 +640,12 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, in
   if (grid > need) grid = need;
   if (grid > 65535) grid = 65535;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(512), 0, stream,
-                     static_cast<const u32x4*>(src), bytes / 16, sink);
+  if (nt)
+    hipLaunchKernelGGL(stream_read_kernel<true>, dim3((unsigned)grid), dim3(512), 0, stream,
+                       static_cast<const u32x4*>(src), bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<false>, dim3((unsigned)grid), dim3(512), 0, stream,
+                       static_cast<const u32x4*>(src), bytes / 16, sink);
   return hipGetLastError();
 }
 

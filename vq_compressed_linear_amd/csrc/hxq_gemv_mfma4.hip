@@ -76,7 +76,7 @@ __device__ __forceinline__ float reduce_blocks(f32x4 v) {
 // TG: groups of 4 tokens (1 up to 4 tokens, 2 up to 8); FG: fragments per
 // accumulator group (1 to 4, no more than a workgroup owns); X1: K <= 2048,
 // so a wave has at most one chunk and loads its x once; NT: index bytes
-// loaded non-temporally (launches whose workgroups own long runs of rows)
+// loaded non-temporally (launches that stream more than the L2s hold)
 template <bool PK12, bool XBF, int TG, int FG, bool X1, bool NT>
 __global__ __launch_bounds__(gm4::THREADS, 1) void gemv_mfma4(GemvMArgs ga) {
   using namespace gm4;
@@ -494,14 +494,14 @@ static hipError_t launch_gemv_mfma4_x(const GemvMArgs& g, int grid, hipStream_t 
   return hipGetLastError();
 }
 
-// Fragments per workgroup past which the index stream bypasses the caches
-// (gate|up at 8 tokens: 22), as in the one-token kernel.
-constexpr int kMfma4LongRun = 8;
-
+// Non-temporal index loads for launches that stream more than the L2s hold
+// (Qwen decode step at 8 tokens 62.5 -> 59.5 us, at 4 tokens 50.1 -> 47.9 us).
 template <bool PK12, bool XBF, int TG, int FG>
-static hipError_t launch_gemv_mfma4_k(const GemvMArgs& g, int fmax, int grid, hipStream_t stream) {
+static hipError_t launch_gemv_mfma4_k(const GemvMArgs& g, int grid, hipStream_t stream) {
   const bool x1 = g.K <= gm4::KC * gm4::WAVES;
-  if (fmax > kMfma4LongRun)
+  int64_t ib = 0;
+  for (int i = 0; i < g.nseg; ++i) ib += index_bytes(g.seg[i].N, g.K, PK12);
+  if (ib > kStreamPastCacheBytes)
     return x1 ? launch_gemv_mfma4_x<PK12, XBF, TG, FG, true, true>(g, grid, stream)
               : launch_gemv_mfma4_x<PK12, XBF, TG, FG, false, true>(g, grid, stream);
   return x1 ? launch_gemv_mfma4_x<PK12, XBF, TG, FG, true, false>(g, grid, stream)
@@ -515,10 +515,10 @@ static hipError_t launch_gemv_mfma4_f(const GemvMArgs& g, int fmax, int grid, hi
   int fg = 4;
   for (int c = 3; c >= 1; --c)
     if ((fmax + c - 1) / c * c < (fmax + fg - 1) / fg * fg) fg = c;
-  if (fg == 1) return launch_gemv_mfma4_k<PK12, XBF, TG, 1>(g, fmax, grid, stream);
-  if (fg == 2) return launch_gemv_mfma4_k<PK12, XBF, TG, 2>(g, fmax, grid, stream);
-  if (fg == 3) return launch_gemv_mfma4_k<PK12, XBF, TG, 3>(g, fmax, grid, stream);
-  return launch_gemv_mfma4_k<PK12, XBF, TG, 4>(g, fmax, grid, stream);
+  if (fg == 1) return launch_gemv_mfma4_k<PK12, XBF, TG, 1>(g, grid, stream);
+  if (fg == 2) return launch_gemv_mfma4_k<PK12, XBF, TG, 2>(g, grid, stream);
+  if (fg == 3) return launch_gemv_mfma4_k<PK12, XBF, TG, 3>(g, grid, stream);
+  return launch_gemv_mfma4_k<PK12, XBF, TG, 4>(g, grid, stream);
 }
 
 template <bool PK12>

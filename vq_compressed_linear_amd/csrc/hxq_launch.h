@@ -33,6 +33,16 @@ bool gemv_fast_path_ok(const LayerArgs& a, bool pk12);
 // One layer of a decode launch.  The launcher fills in the row split and the
 // sidecar density.
 constexpr int kMaxSegments = 8;
+
+// Index bytes of one launch past which the streaming kernels (one-token and
+// few-token decode, the vector input gradient) load them non-temporally: a
+// launch that reads more than the eight XCDs' L2 caches hold (8 x 4 MB) and
+// never reads a byte twice gains from not allocating it (Qwen gate|up, 45.8
+// MB, and the decode step around it), while smaller launches (down, 22.9 MB;
+// q|k|v, o) were slower that way on their own.
+constexpr int64_t kStreamPastCacheBytes = (int64_t)32 << 20;
+// Bytes of one layer's index matrix.
+inline int64_t index_bytes(int64_t N, int64_t K, bool pk12) { return N * (pk12 ? K / 4 * 3 : K); }
 struct DecodeSeg {
   const void* codebook;
   const uint8_t* indices;
@@ -186,9 +196,10 @@ hipError_t launch_gemm5_split(const GemmSeg& sg, bool pk12, const void* x, int M
 // y += S x.
 hipError_t launch_sidecar_add(const LayerArgs& a, hipStream_t stream);
 
-// Reads `bytes` (a multiple of 16) of src once; one word per workgroup into
-// sink (at most sink_words workgroups).
-hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, hipStream_t stream);
+// Reads `bytes` (a multiple of 16) of src once; one word per wave into sink
+// (sink_words / 8 workgroups at most); nt: non-temporal loads.
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int sink_words, bool nt,
+                              hipStream_t stream);
 
 // ---- input gradient dx = dy W (hxq_bwd.hip, hxq_bwd_mfma.hip)
 // One layer of a vector-kernel launch: its rows split into runs of R rows,
