@@ -231,3 +231,21 @@ def test_large_layers_m5_to_8(x_dtype, M, Ns, K, nnz_den):
         G.check(y, Y, B, G.TOL_FP32, "large layer N=%d" % lay.N)
     if len(lays) == 1:
         assert G.torch().equal(ys[0], G.run(lays[0], ds[0], xd)), "grouped and single-layer results differ bitwise"
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_grouped_streaming_launch(M):
+    # a launch of more index bytes than the L2 caches hold (gate|up of the
+    # Qwen set: 2 x 11008 x 2048 u8, 45 MB) takes the instances with
+    # non-temporal index loads; each layer alone (22.5 MB) takes the ordinary
+    # ones: the same arithmetic, so equal bit for bit, and equal to the oracle
+    G.say("grouped streaming launch M=%d" % M)
+    K = 2048
+    lays, ds = _group("u8", [11008, 11008], K, seed=40 + M)
+    x_np = _x(M + 77, M, K, "f32")
+    xd = G.dev_x(x_np, "f32")
+    ys = _grouped("u8", lays, ds, xd)
+    for lay, d, y in zip(lays, ds, ys):
+        Y, B = G.oracle_fwd(lay, x_np, "f32")
+        G.check(y, Y, B, G.TOL_FP32, "streaming launch N=%d M=%d" % (lay.N, M))
+        assert G.torch().equal(y, G.run(lay, d, xd)), "grouped and single-layer results differ bitwise"
